@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for the NVFP4 W4A16 MTP hot path.
+
+This module only draws random numbers and lays them out; it performs none of
+the method's arithmetic (no quantization, no dot products, no argmax).  The
+tests feed the same arrays to the CPU oracle and to the HIP library.
+
+Recipe (stated once here, used everywhere):
+* ``numpy.random.default_rng(seed)``; draws happen in the order W, x, router
+  logits, plant positions.
+* Normal draws are fp32 ``standard_normal`` times the stated deviation, then
+  rounded to bf16 (nearest-even) -- bf16 weights ~N(0, 0.02), activations
+  ~N(0, 1), router logits fp32 ~N(0, 1).
+* Weights "in the quantized domain" (used where a test needs hundreds of
+  expert matrices without running a quantizer on the CPU) draw E2M1 codes
+  from a fixed histogram close to that of quantized normal blocks, E4M3
+  scales from a narrow band of bytes and a power-of-two-free global scale.
+* The exact-arithmetic family draws x from {-3..3}, power-of-two block scales
+  in [2^-2, 2^2] and a power-of-two global scale, so that every partial sum
+  of every dot product is exactly representable in fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounding = ((u >> 16) & 1) + 0x7FFF
+    return ((u + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+def weight_bf16(seed: int, n: int, k: int, std: float = 0.02) -> np.ndarray:
+    """bf16 weight [n, k] ~ N(0, std)."""
+    return normal_bf16(np.random.default_rng(seed), (n, k), std)
+
+
+def acts_bf16(seed: int, m: int, k: int, std: float = 1.0) -> np.ndarray:
+    """bf16 activations [m, k] ~ N(0, std); the stream is offset from the
+    weight stream of the same seed."""
+    return normal_bf16(np.random.default_rng([seed, 1]), (m, k), std)
+
+
+def router_logits(seed: int, m: int, e: int) -> np.ndarray:
+    return np.random.default_rng([seed, 2]).standard_normal((m, e), dtype=np.float32)
+
+
+# Probability of each E2M1 magnitude code 0..7 (close to what quantizing a
+# normal block with its max mapped to 6 gives).
+_CODE_P = np.array([0.11, 0.19, 0.17, 0.15, 0.15, 0.11, 0.08, 0.04])
+_CODE_P = _CODE_P / _CODE_P.sum()
+
+
+def quantized_domain_weight(rng: np.random.Generator, n: int, k: int):
+    """Synthetic NVFP4 weight drawn directly as codes/scales/global.
+    Returns (codes u8[n, k/2], scales u8[n, k/16], g_dec f32)."""
+    mag = rng.choice(8, size=(n, k), p=_CODE_P).astype(np.uint8)
+    sign = (rng.integers(0, 2, size=(n, k), dtype=np.uint8) << 3)
+    code = mag | sign
+    codes = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    # E4M3 bytes 0x50..0x7E: scales roughly 4 .. 448, the band quantized
+    # normal weights land in with a global scale of amax/2688.
+    scales = rng.integers(0x50, 0x7F, size=(n, k // 16), dtype=np.uint8)
+    g_dec = np.float32(rng.uniform(1e-5, 3e-5))
+    return codes, scales, g_dec
+
+
+def moe_quantized_experts(seed: int, num_experts: int, hidden: int, inter: int):
+    """Stacked synthetic NVFP4 experts: gate/up [E, inter, hidden], down
+    [E, hidden, inter].  Each returned as (codes, scales, g_dec[E])."""
+    rng = np.random.default_rng([seed, 3])
+    out = []
+    for rows, cols in ((inter, hidden), (inter, hidden), (hidden, inter)):
+        c = np.empty((num_experts, rows, cols // 2), np.uint8)
+        s = np.empty((num_experts, rows, cols // 16), np.uint8)
+        g = np.empty(num_experts, np.float32)
+        for e in range(num_experts):
+            c[e], s[e], g[e] = quantized_domain_weight(rng, rows, cols)
+        out.append((c, s, g))
+    return out
+
+
+def exact_family(seed: int, m: int, n: int, k: int):
+    """Inputs whose dot products are exact in fp32 in any summation order:
+    x in {-3..3}, codes uniform over all 16, block scales 2^-2..2^2 (E4M3
+    bytes 0x28, 0x30, 0x38, 0x40, 0x48), g_dec a power of two.
+    Returns (x bf16 bits [m, k], codes, scales, g_dec)."""
+    rng = np.random.default_rng([seed, 4])
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = (rng.integers(5, 10, size=(n, k // 16)) << 3).astype(np.uint8)
+    g_dec = np.float32(2.0 ** int(rng.integers(-6, 1)))
+    x = f32_to_bf16_bits(rng.integers(-3, 4, size=(m, k)).astype(np.float32))
+    return x, codes, scales, g_dec
+
+
+
+
+def plant_lmhead_rows(codes: np.ndarray, scales: np.ndarray, h_bf16: np.ndarray, seed: int,
+                      n_near: int = 4, dup: bool = False, scale_byte: int = 0x7E,
+                      vrows: int | None = None) -> dict:
+    """Overwrite LM-head rows in place so that every token has a known winner.
+
+    For token i a row ``star`` gets E2M1 code 7 (magnitude 6) with the sign of
+    h[i, k] at every k and the E4M3 byte ``scale_byte`` in every block.
+    ``n_near`` copies of it have one code stepped down to 6 (magnitude 4) at
+    the k's with the largest |h[i, k]|.  With ``dup`` two exact copies go one
+    below and one above ``star``.  Rows are only placed inside [0, vrows).
+    """
+    n, half = codes.shape
+    k = half * 2
+    v = n if vrows is None else min(vrows, n)
+    m = h_bf16.shape[0]
+    rng = np.random.default_rng([seed, 6])
+    hf = bf16_bits_to_f32(h_bf16)
+    used: set[int] = set()
+
+    def fresh(lo: int, hi: int) -> int:
+        while True:
+            r = int(rng.integers(lo, hi))
+            if r not in used:
+                used.add(r)
+                return r
+
+    info = {"star": [], "near": [], "near_k": [], "dups": [], "scale_byte": scale_byte}
+    for i in range(m):
+        sign = (np.signbit(hf[i]).astype(np.uint8) << 3)
+        code = (7 | sign).astype(np.uint8)
+        row_codes = (code[0::2] | (code[1::2] << 4)).astype(np.uint8)
+        star = fresh(v // 4, (3 * v) // 4)
+        codes[star] = row_codes
+        scales[star] = scale_byte
+        order = np.argsort(-np.abs(hf[i]), kind="stable")[:n_near]
+        near, near_k = [], []
+        for kk in order:
+            r = fresh(0, v)
+            c2 = code.copy()
+            c2[kk] = 6 | sign[kk]
+            codes[r] = (c2[0::2] | (c2[1::2] << 4)).astype(np.uint8)
+            scales[r] = scale_byte
+            near.append(r)
+            near_k.append(int(kk))
+        dups = []
+        if dup:
+            for lo, hi in ((0, star), (star + 1, v)):
+                r = fresh(lo, hi)
+                codes[r] = row_codes
+                scales[r] = scale_byte
+                dups.append(r)
+        info["star"].append(star)
+        info["near"].append(near)
+        info["near_k"].append(near_k)
+        info["dups"].append(dups)
+    assert k == h_bf16.shape[1]
+    return info
