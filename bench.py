@@ -1,0 +1,292 @@
+"""Benchmark of the NVFP4 W4A16 MTP draft-head hot path on one MI355X.
+
+A step is one draft step of a Qwen-shaped MTP head at M decode rows: the
+fc / q / k / v / o W4A16 GEMVs, the routed MoE FFN (256 NVFP4 experts,
+top-8) and the full-vocabulary (151936 x 2048) NVFP4 LM head fused with
+argmax.  The step is captured once per weight copy in a HIP graph and the
+graphs are replayed in rotation over three independent copies of every
+weight (~1.5 GB in total, several times the 256 MB Infinity Cache), so the
+weights stream from HBM as they would in serving.  All inputs are seeded
+synthetic data resident in HBM before the timed region.
+
+Printed: one JSON line.  `value` = algorithmic HBM bytes of the step (NVFP4
+codes + scales + globals actually read, activations in, results out) per
+second.  Extra fields: drafts/s of the LM head, a roofline object for the
+dominant kernel (the LM-head GEMV+argmax, timed with HIP events on the
+stream it runs on), per-row measurements (quantizer, each GEMV, MoE, LM
+head, the prefill GEMM) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+H, I, E, TOPK, VOCAB = 2048, 1024, 256, 8, 151936
+PROJ = [("fc", 2048, 4096), ("q", 8192, 2048), ("k", 512, 2048), ("v", 512, 2048), ("o", 2048, 4096)]
+NCOPIES = 3
+
+
+def nvfp4_bytes(n, k):
+    return n * k // 2 + n * k // 16 + 16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--m", type=int, default=1, help="decode rows per step (1..8)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this build runs on a single "
+              "MI355X; the multi-GPU sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    if a.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 5}))
+        return
+    import nvfp4_w4a16_mtp_amd as nv
+    nv.lib()
+    M = a.m
+    assert 1 <= M <= 8
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def randn_bf16(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    # ---------------- weights: NCOPIES copies, quantized on the GPU ----------------
+    qev0, qev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    quant_bytes = 0
+    quant_ms = 0.0
+    copies = []
+    for c in range(NCOPIES):
+        ws = {}
+        for name, n, k in PROJ + [("lm", VOCAB, H)]:
+            w = randn_bf16((n, k), 0.02)
+            qev0.record()
+            ws[name] = nv.nvfp4_quantize(w)
+            qev1.record()
+            torch.cuda.synchronize()
+            quant_ms += qev0.elapsed_time(qev1)
+            quant_bytes += 2 * (n * k * 2) + nvfp4_bytes(n, k)
+            del w
+        # experts: stacked [E, rows, cols]; each matrix quantized with its own global scale
+        ex = {}
+        for proj, rows, cols in (("gate", I, H), ("up", I, H), ("down", H, I)):
+            codes = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((E, rows, cols // 16), dtype=torch.uint8, device=dev)
+            glob = torch.empty((E, 4), dtype=torch.float32, device=dev)
+            for e in range(E):
+                w = randn_bf16((rows, cols), 0.02)
+                nv.nvfp4_quantize(w, out=nv.NVFP4Weight(codes[e], scales[e], glob[e], rows, cols))
+            ex[proj] = (codes, scales, glob)
+        ws["moe"] = nv.NVFP4Experts(*ex["gate"], *ex["up"], *ex["down"])
+        copies.append(ws)
+    torch.cuda.synchronize()
+
+    # ---------------- activations and outputs (resident) ----------------
+    xs = {name: randn_bf16((M, k), 1.0) for name, n, k in PROJ}
+    xm = randn_bf16((M, H), 1.0)
+    router = torch.randn((M, E), generator=gen, device=dev, dtype=torch.float32)
+    hl = randn_bf16((M, H), 1.0)
+    ys = {name: torch.empty((M, n), dtype=torch.float32, device=dev) for name, n, k in PROJ}
+    ymoe = torch.empty((M, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    wts = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    moe_ws = nv.moe_workspace(M, TOPK, copies[0]["moe"], dev)
+    lm_ws = nv.lmhead_workspace(M, VOCAB, dev)
+    out_idx = torch.empty(M, dtype=torch.int32, device=dev)
+    out_max = torch.empty(M, dtype=torch.float32, device=dev)
+
+    def step(ws, ev=None):
+        for name, n, k in PROJ:
+            nv.w4a16_gemv(xs[name], ws[name], out=ys[name])
+        nv.moe_w4a16_gemv(xm, router, TOPK, ws["moe"], workspace=moe_ws, out=ymoe, topk_ids=ids, topk_w=wts)
+        if ev is not None:
+            ev[0].record()
+        nv.lmhead_gemv_argmax(hl, ws["lm"], vocab_rows=VOCAB, workspace=lm_ws, out_idx=out_idx, out_max=out_max)
+        if ev is not None:
+            ev[1].record()
+
+    # distinct experts hit by the routing (same router logits every step)
+    step(copies[0])
+    torch.cuda.synchronize()
+    n_distinct = len(set(ids.cpu().numpy().ravel().tolist()))
+    moe_bytes = n_distinct * 3 * nvfp4_bytes(I, H) + M * H * 2 + M * E * 4 + M * H * 4 + 2 * M * TOPK * 4
+    gemv_bytes = sum(nvfp4_bytes(n, k) + M * k * 2 + M * n * 4 for name, n, k in PROJ)
+    lm_bytes = nvfp4_bytes(VOCAB, H) + M * H * 2 + M * 8
+    step_bytes = gemv_bytes + moe_bytes + lm_bytes
+
+    # ---------------- capture one graph per copy; LM head bracketed by events ----------------
+    s = torch.cuda.Stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    graphs = []
+    with torch.cuda.stream(s):
+        for c in range(NCOPIES):      # warm the kernels before capture
+            step(copies[c])
+        torch.cuda.synchronize()
+        for c in range(NCOPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(copies[c])
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    # The LM-head launch is timed with HIP events in eager replays of the same
+    # step, interleaved with the graph replays of the timed region.
+    with torch.cuda.stream(s):
+        for i in range(a.warmup):
+            graphs[i % NCOPIES].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            graphs[i % NCOPIES].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # eager pass over the same steps for the per-launch LM-head duration
+        for i in range(a.steps):
+            step(copies[i % NCOPIES], evs[i])
+        torch.cuda.synchronize()
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    lm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "W4A16 GEMV achieved HBM GB/s (% peak) + MTP drafts/sec (LM-head GEMV+argmax)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded normal bf16 weights quantized on the GPU, normal activations)",
+        "config": {"workload": "qwen_mtp_draft_step", "m_rows": M, "hidden": H, "proj": {n: [r, c] for n, r, c in PROJ},
+                   "moe": {"experts": E, "top_k": TOPK, "inter": I, "distinct_experts": n_distinct},
+                   "lm_head": [VOCAB, H], "weight_copies_rotated": NCOPIES, "graph": True},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "step_bytes": step_bytes,
+        "drafts_per_s": round(M / (lm_ms * 1e-3), 1),
+        "step_drafts_per_s": round(M / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "lmhead_gemv_argmax (151936 x 2048 NVFP4)", "bound": "hbm", "achieved": round(lm_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": lm_bytes, "avg_launch_ms": round(lm_ms, 5)},
+        "load_time_quantizer": {"bytes": quant_bytes, "ms": round(quant_ms, 3),
+                                "gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1)},
+    }
+    if not a.no_rows:
+        result["rows"] = rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s)
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(M, step_bytes, n_distinct)
+    print(json.dumps(result), flush=True)
+
+
+def _time(torch, fn, reps, stream):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
+    """Per-row timings (eager, rotating copies), each with its roofline fraction."""
+    out = {}
+    reps = 30
+    for name, n, k in PROJ:
+        ms = _time(torch, lambda i: nv.w4a16_gemv(xs[name], copies[i % NCOPIES][name], out=ys[name]), reps, s)
+        b = nvfp4_bytes(n, k) + M * k * 2 + M * n * 4
+        out[f"gemv_{name}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    # LM head at both vocabulary sizes of the workload
+    for v in (32768, VOCAB):
+        ws = nv.lmhead_workspace(M, v, hl.device)
+        ms = _time(torch, lambda i: nv.lmhead_gemv_argmax(hl, copies[i % NCOPIES]["lm"], vocab_rows=v, workspace=ws), reps, s)
+        b = nvfp4_bytes(v, H) + M * H * 2 + M * 8
+        out[f"lmhead_v{v}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+                               "drafts_per_s": round(M / (ms * 1e-3), 1)}
+    ws = nv.moe_workspace(M, TOPK, copies[0]["moe"], hl.device)
+    ms = _time(torch, lambda i: nv.moe_w4a16_gemv(xm, router, TOPK, copies[i % NCOPIES]["moe"], workspace=ws), reps, s)
+    out["moe"] = {"ms": round(ms, 5)}
+    # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120) at M = 1024
+    gen = torch.Generator(device=hl.device)
+    gen.manual_seed(1)
+    for name, n, k, m in (("fc", 2048, 4096, 1024), ("gate_up", 17408, 5120, 1024), ("gate_up", 17408, 5120, 8192)):
+        w = nv.nvfp4_quantize((torch.randn((n, k), generator=gen, device=hl.device) * 0.02).to(torch.bfloat16))
+        x = torch.randn((m, k), generator=gen, device=hl.device).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=hl.device)
+        ms = _time(torch, lambda i: nv.w4a16_gemm_m128(x, w, out=y), 10, s)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out[f"gemm_{name}_m{m}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del w, x, y
+    return out
+
+
+def cpu_baseline(M, step_bytes, n_distinct):
+    """The CPU oracle (single-threaded C, fp64 accumulation) timed on a bounded
+    sample: whole draft steps of the same shapes on synthetic NVFP4 weights,
+    repeated for about 10 s."""
+    import oracle
+    from nvfp4_w4a16_mtp_amd import synth
+    rng = np.random.default_rng(0)
+    W = {name: synth.quantized_domain_weight(rng, n, k) for name, n, k in PROJ}
+    lm = synth.quantized_domain_weight(rng, VOCAB, H)
+    ex = synth.moe_quantized_experts(0, 16, H, I)          # the routed subset is what the oracle reads
+    x = {name: synth.acts_bf16(1, M, k) for name, n, k in PROJ}
+    xm = synth.acts_bf16(2, M, H)
+    r = synth.router_logits(3, M, 16)
+    topk = min(TOPK, 16)
+    t0 = time.perf_counter()
+    nsteps = 0
+    while True:
+        for name, n, k in PROJ:
+            oracle.gemv(x[name], *W[name])
+        oracle.moe(xm, r, topk, *ex)
+        oracle.lmhead_argmax(x["q"], *lm)
+        nsteps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = (time.perf_counter() - t0) / nsteps
+    return {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nsteps} whole draft step(s) at M={M} (5 GEMVs, MoE over {min(16, M * topk)} of 16 experts "
+                      f"standing in for the {n_distinct} routed of 256, LM head 151936x2048) on synthetic NVFP4 "
+                      f"weights; {dt:.2f} s per step",
+            "ms_per_step": round(dt * 1e3, 1)}
+
+
+if __name__ == "__main__":
+    main()

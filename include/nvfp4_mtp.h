@@ -1,0 +1,202 @@
+/*
+ * nvfp4_mtp.h -- C ABI of the NVFP4 W4A16 MTP draft-head library (AMD gfx950).
+ *
+ * The library runs the hot path of a multi-token-prediction draft head whose
+ * projection, expert and LM-head weights are NVFP4: a quantizer, a W4A16
+ * decode GEMV, a W4A16 GEMM for prompt-sized row counts, an LM-head GEMV fused
+ * with argmax, and a top-k MoE expert FFN.  The operations are the ones the
+ * following pages describe (cited by page and item):
+ *   [new.rs]      spark_model/layers/mtp_head/new.rs -- `MtpHead::new`
+ *   [mtp_head.rs] metrale_model_layers/layers/mtp_head.rs -- module doc,
+ *                 `MtpHead` fields, `MtpHead::gemv`, `quantize_proj`
+ *   [v4_mtp.rs]   spark_model/layers/deepseek_v4_mtp.rs -- `forward_one`,
+ *                 `argmax_grammar_masked`
+ *   [prefill.rs]  spark_model/layers/qwen3_attention/prefill_weights.rs --
+ *                 `w4a16_gemm_m128_dispatch`
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers unless a comment says "host".
+ *    The caller owns every buffer; the library allocates nothing, keeps no
+ *    state between calls and is safe to call from several host threads.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; it never synchronizes or reads back.
+ *  - Return value: NVFP4_OK (0) or a negative status.  Arguments are checked
+ *    on the host before anything is enqueued; on failure nothing is enqueued
+ *    and nvfp4_mtp_last_error() describes the problem.
+ *  - bf16 data are passed as uint16_t bit patterns.
+ *
+ * NVFP4 weight layout (the pages show only the packed [N, K/2] code array;
+ * the rest is the public NVFP4 format): a weight W[N][K] (out = in @ W^T, the
+ * convention of [mtp_head.rs] `MtpHead::gemv` and [prefill.rs]) is stored as
+ *   codes [N][K/2]  u8, two E2M1 codes per byte, even k in the low nibble;
+ *   scales[N][K/16] u8, one E4M3FN scale per 16 consecutive k of a row,
+ *                   row-major, no swizzle (bytes 0x7F/0xFF are invalid);
+ *   global          one nvfp4_global, dequantized value
+ *                   W^[n][k] = e2m1(code) * e4m3(scale) * global.dec.
+ */
+#ifndef NVFP4_MTP_H
+#define NVFP4_MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Per-matrix global scale, 16 bytes, device resident.  Written by
+ * nvfp4_quantize: amax = max |W|, enc = 2688 / amax (0 if amax == 0, at most
+ * FLT_MAX), dec = amax / 2688 (2688 = 6 * 448, the largest E2M1 value times
+ * the largest E4M3 value).  flags is reserved (written 0). */
+typedef struct nvfp4_global {
+    float dec;
+    float enc;
+    float amax;
+    uint32_t flags;
+} nvfp4_global;
+
+/* Host-side descriptor of one NVFP4 matrix W[n][k] (device pointers inside).
+ * codes must be 16-byte aligned, scales 2-byte aligned, global 4-byte
+ * aligned; k % 32 == 0; n >= 0. */
+typedef struct nvfp4_weight {
+    const uint8_t *codes;         /* [n][k/2]  */
+    const uint8_t *scales;        /* [n][k/16] */
+    const nvfp4_global *global;   /* one struct */
+    int32_t n;
+    int32_t k;
+} nvfp4_weight;
+
+/* Host-side descriptor of a stack of NVFP4 routed experts (the NVFP4 MoE of
+ * [new.rs] `MtpHead::new`: per expert a gate and an up projection
+ * [inter][hidden] and a down projection [hidden][inter]).  Expert e's gate
+ * codes start at gate_codes + e * inter * hidden / 2, its scales at
+ * gate_scales + e * inter * hidden / 16, its global at gate_global[e]; the
+ * same for up; down uses [hidden][inter] per expert. */
+typedef struct nvfp4_moe_weights {
+    int32_t num_experts;   /* E, 1..1024            */
+    int32_t hidden;        /* H, % 32 == 0          */
+    int32_t inter;         /* I, % 32 == 0          */
+    const uint8_t *gate_codes, *gate_scales;
+    const nvfp4_global *gate_global;
+    const uint8_t *up_codes, *up_scales;
+    const nvfp4_global *up_global;
+    const uint8_t *down_codes, *down_scales;
+    const nvfp4_global *down_global;
+} nvfp4_moe_weights;
+
+enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_ARG = -1,         /* null pointer or out-of-range scalar    */
+    NVFP4_ERR_SHAPE = -2,       /* k % 32 != 0, m out of range, ...       */
+    NVFP4_ERR_ALIGN = -3,       /* a pointer misses its alignment         */
+    NVFP4_ERR_WORKSPACE = -4,   /* workspace missing or too small         */
+    NVFP4_ERR_UNSUPPORTED = -5, /* shape the kernels do not handle        */
+    NVFP4_ERR_HIP = -6          /* kernel launch failed (message has why) */
+};
+
+enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
+
+/* Bit 0 of lmhead_gemv_argmax's flags: compare bf16-rounded logits. */
+#define NVFP4_ARGMAX_BF16_KEYS 1u
+
+/*
+ * nvfp4_quantize -- the two quantizer passes [new.rs] resolves in
+ * `MtpHead::new` as `nvfp4_global_absmax` and `quantize_bf16_to_nvfp4` and
+ * applies to every projection, router and expert matrix (`quantize_proj` in
+ * [mtp_head.rs]).
+ *   w_bf16  [n][k] bf16, row-major, 16-byte aligned; finite values (with a
+ *           NaN or Inf the outputs are unspecified, nothing faults).
+ *   codes   out [n][k/2] (16-byte aligned); scales out [n][k/16] (2-byte
+ *           aligned); global out (one struct, 16-byte aligned).
+ * Pass 1: amax = max |w|.  Pass 2, per 16-element block of a row:
+ *   scale = E4M3_rne_sat(fl(fl(bmax * enc) / 6)), sf = its value;
+ *   inv = sf > 0 ? min(fl(enc / sf), FLT_MAX) : 0;
+ *   code = E2M1 nearest to fl(w * inv), ties to the even code, saturating
+ *   at 6, sign = sign of the product.
+ * Requires n >= 1, k >= 32, k % 32 == 0, n * k < 2^40.  Three launches
+ * (clear, absmax, encode); no workspace.
+ */
+int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint8_t *codes,
+                   uint8_t *scales, nvfp4_global *global, void *stream);
+
+/*
+ * w4a16_gemv -- decode-row W4A16 GEMV, y[m][n] = sum_k x[m][k] * W^[n][k]
+ * ([mtp_head.rs] `MtpHead::gemv` -> `w4a16_decode_gemv`; its doc of the
+ * batched-M tiers: one pass over the weight serves all M rows).
+ *   x_bf16  [m][w->k] bf16, 16-byte aligned; m in 1..8.
+ *   y       [m][w->n], fp32 (y_dtype NVFP4_OUT_F32) or bf16 rounded to
+ *           nearest-even from the fp32 sum (NVFP4_OUT_BF16); 4-byte aligned.
+ * fp32 accumulation; one pass over codes and scales.
+ */
+int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
+               int32_t y_dtype, void *stream);
+
+/*
+ * w4a16_gemm_m128 -- W4A16 GEMM for prompt-sized row counts, the
+ * `w4a16_gemm_m128_dispatch` of [prefill.rs] in its lossless form (NVFP4 ->
+ * bf16 dequantization, bf16 matrix products, fp32 accumulation; activations
+ * are never quantized).  y[m][n] = sum_k x[m][k] * W^[n][k].
+ *   x_bf16  [m][w->k] bf16, 16-byte aligned; m >= 1 (any m; work is tiled in
+ *           128-row blocks, a ragged last block is masked).
+ *   y       [m][w->n] fp32 or bf16 (y_dtype), 4-byte aligned.
+ * Requires w->n % 16 == 0.
+ */
+int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
+                    int32_t y_dtype, void *stream);
+
+/*
+ * lmhead_gemv_argmax -- LM-head GEMV over the first V vocabulary rows fused
+ * with argmax: the draft-token selection of [v4_mtp.rs] `forward_one` (LM
+ * head, then argmax) and of the NVFP4 LM head of [new.rs], with the reduced
+ * vocabulary of [new.rs] / [v4_mtp.rs] (V = min(vocab_rows, w->n), 0 = all).
+ * No logits tensor is written.
+ *   h_bf16   [m][w->k] bf16, 16-byte aligned; m in 1..8.
+ *   out_idx  [m] int32: the lowest index i < V whose key is the maximum,
+ *            where key = logit (fp32), or the logit rounded to bf16 when
+ *            flags & NVFP4_ARGMAX_BF16_KEYS.  The selection follows the
+ *            ascending strict-greater scan of [v4_mtp.rs]
+ *            `argmax_grammar_masked`: NaN never wins, -0 == +0, and if no
+ *            key exceeds -inf the index is 0.
+ *   out_max  [m] fp32: the fp32 logit of the selected row.
+ *   workspace device scratch of at least
+ *            lmhead_gemv_argmax_workspace_bytes(m, V) bytes, 256-byte
+ *            aligned; contents on entry are ignored.
+ * Rows with equal codes and scales produce bit-identical logits.
+ */
+size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows);
+int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                       int32_t vocab_rows, int32_t *out_idx, float *out_max, void *workspace,
+                       size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * moe_w4a16_gemv -- routed-expert MoE FFN for decode rows: the
+ * `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain named in
+ * [new.rs] `MtpHead::new`, on NVFP4 experts.
+ *   x_bf16         [m][H] bf16, 16-byte aligned; m in 1..8.
+ *   router_logits  [m][E] fp32 (the router projection's output).
+ *   top_k          1..min(E, 16).
+ *   y              out [m][H] fp32: sum_j w[j] * down_e(j)(a_j), j in
+ *                  descending-logit order.
+ *   topk_ids       out [m][top_k] int32: experts by descending logit, the
+ *                  lower id first among equal logits.
+ *   topk_w         out [m][top_k] fp32: softmax over the selected logits.
+ *   workspace      at least moe_w4a16_gemv_workspace_bytes(m, top_k, e),
+ *                  256-byte aligned; contents on entry are ignored.
+ * Per selected expert: g = gate x, u = up x (fp32),
+ * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
+ * read once per call however many rows select it.  Requires H, I % 32 == 0.
+ */
+size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
+int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,
+                   int32_t top_k, const nvfp4_moe_weights *e, float *y, int32_t *topk_ids,
+                   float *topk_w, void *workspace, size_t ws_bytes, void *stream);
+
+/* Message of the last failing call on this host thread ("" if none); the
+ * pointer stays valid until the next call on the same thread. */
+const char *nvfp4_mtp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MTP_H */

@@ -1,0 +1,255 @@
+"""NVFP4 W4A16 MTP draft-head hot path on AMD gfx950 (MI355X).
+
+Thin ctypes binding over ``libnvfp4_mtp.so`` (C ABI in include/nvfp4_mtp.h).
+It only marshals arguments: every step of every operation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+library is not built the calls raise -- there is no fallback.
+
+Operations (same names as the C ABI):
+  nvfp4_quantize       bf16 W[n, k] -> NVFP4Weight (codes, scales, global)
+  w4a16_gemv           x[m<=8, k] @ W^T
+  w4a16_gemm_m128      x[m, k] @ W^T for prompt-sized m (bf16 MFMA)
+  lmhead_gemv_argmax   argmax over the first V rows of h @ W^T
+  moe_w4a16_gemv       top-k routed NVFP4 expert FFN
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4_mtp.so")
+_lib = None
+
+NVFP4_OUT_F32 = 0
+NVFP4_OUT_BF16 = 1
+NVFP4_ARGMAX_BF16_KEYS = 1
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_", ctypes.c_void_p),
+                ("n", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class _MoeWeights(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("gate_codes", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p), ("gate_global", ctypes.c_void_p),
+                ("up_codes", ctypes.c_void_p), ("up_scales", ctypes.c_void_p), ("up_global", ctypes.c_void_p),
+                ("down_codes", ctypes.c_void_p), ("down_scales", ctypes.c_void_p), ("down_global", ctypes.c_void_p)]
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NVFP4Error(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                             "or python nvfp4_w4a16_mtp_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        WP = ctypes.POINTER(_Weight)
+        EP = ctypes.POINTER(_MoeWeights)
+        L.nvfp4_quantize.argtypes = [P, i32, i32, P, P, P, P]
+        L.w4a16_gemv.argtypes = [P, i32, WP, P, i32, P]
+        L.w4a16_gemm_m128.argtypes = [P, i32, WP, P, i32, P]
+        L.lmhead_gemv_argmax_workspace_bytes.argtypes = [i32, i32]
+        L.lmhead_gemv_argmax_workspace_bytes.restype = sz
+        L.lmhead_gemv_argmax.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P]
+        L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
+        L.moe_w4a16_gemv_workspace_bytes.restype = sz
+        L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
+        L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
+        for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemm_m128", "lmhead_gemv_argmax", "moe_w4a16_gemv"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = lib().nvfp4_mtp_last_error().decode(errors="replace")
+        raise NVFP4Error(f"{what} failed ({rc}): {msg}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _as_bf16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t.view(torch.bfloat16)
+    raise TypeError(f"expected bf16 (or 16-bit bit patterns), got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class NVFP4Weight:
+    """One NVFP4 matrix W[n, k] on the device: codes [n, k/2] u8, scales
+    [n, k/16] u8 (E4M3FN), glob 4 x fp32 = the 16-byte nvfp4_global struct
+    {dec, enc, amax, flags}."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    glob: torch.Tensor
+    n: int
+    k: int
+
+    def desc(self) -> _Weight:
+        return _Weight(self.codes.data_ptr(), self.scales.data_ptr(), self.glob.data_ptr(), self.n, self.k)
+
+    @staticmethod
+    def from_parts(codes: torch.Tensor, scales: torch.Tensor, g_dec: float) -> "NVFP4Weight":
+        n, half = codes.shape
+        glob = torch.tensor([float(g_dec), 0.0, 0.0, 0.0], dtype=torch.float32, device=codes.device)
+        return NVFP4Weight(codes.contiguous(), scales.contiguous(), glob, n, half * 2)
+
+
+@dataclass
+class NVFP4Experts:
+    """Stacked routed experts: gate/up codes [E, I, H/2], scales [E, I, H/16];
+    down codes [E, H, I/2], scales [E, H, I/16]; globals [E, 4] fp32."""
+    gate_codes: torch.Tensor
+    gate_scales: torch.Tensor
+    gate_glob: torch.Tensor
+    up_codes: torch.Tensor
+    up_scales: torch.Tensor
+    up_glob: torch.Tensor
+    down_codes: torch.Tensor
+    down_scales: torch.Tensor
+    down_glob: torch.Tensor
+
+    @property
+    def num_experts(self):
+        return self.gate_codes.shape[0]
+
+    @property
+    def inter(self):
+        return self.gate_codes.shape[1]
+
+    @property
+    def hidden(self):
+        return self.gate_codes.shape[2] * 2
+
+    def desc(self) -> _MoeWeights:
+        return _MoeWeights(self.num_experts, self.hidden, self.inter,
+                           self.gate_codes.data_ptr(), self.gate_scales.data_ptr(), self.gate_glob.data_ptr(),
+                           self.up_codes.data_ptr(), self.up_scales.data_ptr(), self.up_glob.data_ptr(),
+                           self.down_codes.data_ptr(), self.down_scales.data_ptr(), self.down_glob.data_ptr())
+
+
+def nvfp4_quantize(w: torch.Tensor, out: NVFP4Weight | None = None) -> NVFP4Weight:
+    w = _as_bf16(w)
+    _dev(w, "w")
+    n, k = w.shape
+    if out is None:
+        dev = w.device
+        out = NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(4, dtype=torch.float32, device=dev), n, k)
+    _check(lib().nvfp4_quantize(_ptr(w), n, k, _ptr(out.codes), _ptr(out.scales), _ptr(out.glob), _stream(w)),
+           "nvfp4_quantize")
+    return out
+
+
+def _out_code(dtype):
+    if dtype == torch.float32:
+        return NVFP4_OUT_F32
+    if dtype == torch.bfloat16:
+        return NVFP4_OUT_BF16
+    raise TypeError("output dtype must be float32 or bfloat16")
+
+
+def w4a16_gemv(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: torch.Tensor | None = None):
+    x = _as_bf16(x)
+    _dev(x, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    d = w.desc()
+    _check(lib().w4a16_gemv(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype), _stream(x)), "w4a16_gemv")
+    return out
+
+
+def w4a16_gemm_m128(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: torch.Tensor | None = None):
+    x = _as_bf16(x)
+    _dev(x, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    d = w.desc()
+    _check(lib().w4a16_gemm_m128(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype), _stream(x)),
+           "w4a16_gemm_m128")
+    return out
+
+
+def lmhead_workspace(m: int, vocab_rows: int, device) -> torch.Tensor:
+    nbytes = lib().lmhead_gemv_argmax_workspace_bytes(m, vocab_rows)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,
+                       workspace: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                       out_max: torch.Tensor | None = None):
+    h = _as_bf16(h)
+    _dev(h, "h")
+    m = h.shape[0]
+    if workspace is None:
+        workspace = lmhead_workspace(m, vocab_rows, h.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    d = w.desc()
+    _check(lib().lmhead_gemv_argmax(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(out_idx), _ptr(out_max),
+                                    _ptr(workspace), workspace.numel(),
+                                    NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
+           "lmhead_gemv_argmax")
+    return out_idx, out_max
+
+
+def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:
+    d = experts.desc()
+    nbytes = lib().moe_w4a16_gemv_workspace_bytes(m, top_k, ctypes.byref(d))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, experts: NVFP4Experts,
+                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+    x = _as_bf16(x)
+    _dev(x, "x")
+    _dev(router_logits, "router_logits")
+    if router_logits.dtype != torch.float32:
+        raise TypeError("router_logits must be float32")
+    m = x.shape[0]
+    if workspace is None:
+        workspace = moe_workspace(m, top_k, experts, x.device)
+    if out is None:
+        out = torch.empty((m, experts.hidden), dtype=torch.float32, device=x.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((m, top_k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((m, top_k), dtype=torch.float32, device=x.device)
+    d = experts.desc()
+    _check(lib().moe_w4a16_gemv(_ptr(x), m, _ptr(router_logits), top_k, ctypes.byref(d), _ptr(out), _ptr(topk_ids),
+                                _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x)),
+           "moe_w4a16_gemv")
+    return out, topk_ids, topk_w

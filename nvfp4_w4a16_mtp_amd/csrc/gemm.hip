@@ -1,0 +1,161 @@
+// W4A16 GEMM for prompt-sized row counts (drafter prefill): the
+// `w4a16_gemm_m128_dispatch` of prefill_weights.rs in its lossless variant --
+// NVFP4 weights dequantized exactly to bf16, bf16 matrix products, fp32
+// accumulation, activations never quantized.  y[m][n] = sum_k x[m][k] W^[n][k].
+//
+// gfx950 design: a 128 x 128 output tile per workgroup (4 wavefronts, each
+// 64 x 64 = 4 x 4 blocks of v_mfma_f32_16x16x32_bf16), K in steps of 64.
+// Per step the workgroup stages the 128 x 64 activation tile and the
+// 128 x 64 weight tile in LDS; the weight tile is dequantized on the way in
+// (hardware E2M1 -> fp32 convert, times the E4M3 block scale, packed to
+// bf16 -- exact, since e2m1 * e4m3 has at most 6 significant bits).  The
+// next step's global loads are issued before the current step's MFMAs.
+// LDS rows are padded to 144 bytes so the 16 rows read by one MFMA operand
+// load fall in distinct banks.  The global scale is applied in the epilogue.
+#include "common.hpp"
+
+namespace nvfp4 {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsRow = kBK * 2 + 16;   // bytes per padded LDS row
+
+// Two E2M1 codes (byte SEL of word) times sf, packed as two bf16 (exact).
+template <int SEL>
+__device__ __forceinline__ uint32_t dq2(uint32_t word, float sf) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+    const uint32_t lo = __float_as_uint(f.x * sf), hi = __float_as_uint(f.y * sf);
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // upper halves: exact bf16
+}
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+                                             const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
+                                             int M, int N, int K, void *__restrict__ y) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBN * kLdsRow];
+
+    const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+
+    // staging role: row th/2 of both tiles, half th%2 (32 k) of the K step
+    const int srow = th >> 1, shalf = th & 1;
+    const int xm = m0 + srow, wnr = n0 + srow;
+    const bool xval = xm < M, wval = wnr < N;
+    const uint16_t *xrow = x + (size_t)(xval ? xm : 0) * K;
+    const uint8_t *crow = codes + (size_t)(wval ? wnr : 0) * (K >> 1);
+    const uint8_t *srow_p = scales + (size_t)(wval ? wnr : 0) * (K >> 4);
+
+    uint4 xr[4];
+    uint4 cr;
+    uint32_t sr;
+    auto load_step = [&](int k0) {
+        const int kk = k0 + 32 * shalf;
+        const bool kin = kk < K;
+        if (xval && kin) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(xrow + kk);
+            xr[0] = p[0];
+            xr[1] = p[1];
+            xr[2] = p[2];
+            xr[3] = p[3];
+        } else {
+            xr[0] = xr[1] = xr[2] = xr[3] = make_uint4(0, 0, 0, 0);
+        }
+        if (wval && kin) {
+            cr = *reinterpret_cast<const uint4 *>(crow + (kk >> 1));
+            sr = *reinterpret_cast<const uint16_t *>(srow_p + (kk >> 4));
+        } else {
+            cr = make_uint4(0, 0, 0, 0);
+            sr = 0;
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    load_step(0);
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+        // stage: activations as they are, weights dequantized
+        {
+            uint4 *pa = reinterpret_cast<uint4 *>(lds_a + srow * kLdsRow + 64 * shalf);
+            pa[0] = xr[0];
+            pa[1] = xr[1];
+            pa[2] = xr[2];
+            pa[3] = xr[3];
+            const float sf0 = e4m3_to_f32(sr & 0xFFu), sf1 = e4m3_to_f32(sr >> 8);
+            const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
+            uint4 *pb = reinterpret_cast<uint4 *>(lds_b + srow * kLdsRow + 64 * shalf);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const float sf = d < 2 ? sf0 : sf1;
+                pb[d] = make_uint4(dq2<0>(cw[d], sf), dq2<1>(cw[d], sf), dq2<2>(cw[d], sf), dq2<3>(cw[d], sf));
+            }
+        }
+        __syncthreads();
+        if (k0 + kBK < K) load_step(k0 + kBK);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 af[4], bfr[4];
+            const int koff = 64 * ks + 16 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8 *>(lds_a + (64 * wm + 16 * i + (lane & 15)) * kLdsRow + koff);
+                bfr[i] = *reinterpret_cast<const bf16x8 *>(lds_b + (64 * wn + 16 * i + (lane & 15)) * kLdsRow + koff);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    const float dec = g->dec;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + 64 * wn + 16 * j + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
+                if (m < M && n < N) {
+                    const float o = acc[i][j][r] * dec;
+                    if constexpr (BF16OUT)
+                        reinterpret_cast<uint16_t *>(y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(o);
+                    else
+                        reinterpret_cast<float *>(y)[(size_t)m * N + n] = o;
+                }
+            }
+        }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,
+                               void *stream) {
+    int rc = validate_weight(w, "w4a16_gemm_m128");
+    if (rc) return rc;
+    if (w->n == 0 && m >= 1) return ok();   // empty output: nothing to read or write
+    if (!x_bf16 || !y) return fail(NVFP4_ERR_ARG, "w4a16_gemm_m128: NULL x or y");
+    if (m < 1) return fail(NVFP4_ERR_SHAPE, "w4a16_gemm_m128: m=%d < 1", m);
+    if (y_dtype != NVFP4_OUT_F32 && y_dtype != NVFP4_OUT_BF16)
+        return fail(NVFP4_ERR_ARG, "w4a16_gemm_m128: unknown y_dtype %d", y_dtype);
+    if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: x not 16-byte aligned");
+    if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: y not 4-byte aligned");
+    if ((w->n + kBN - 1) / kBN > 2147483647 || (m + kBM - 1) / kBM > 65535)
+        return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemm_m128: grid too large");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    dim3 grid((w->n + kBN - 1) / kBN, (m + kBM - 1) / kBM);
+    if (y_dtype == NVFP4_OUT_BF16)
+        hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, s, x_bf16, w->codes, w->scales, w->global, m, w->n, w->k, y);
+    else
+        hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, s, x_bf16, w->codes, w->scales, w->global, m, w->n, w->k, y);
+    return check_launch("w4a16_gemm_m128");
+}

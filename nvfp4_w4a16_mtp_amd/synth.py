@@ -26,9 +26,13 @@ import numpy as np
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounding = ((u >> 16) & 1) + 0x7FFF
-    return ((u + rounding) >> 16).astype(np.uint16)
+    u = a.view(np.uint32).ravel()
+    out = np.empty(u.shape, np.uint16)
+    step = 1 << 24
+    for lo in range(0, u.size, step):
+        v = u[lo:lo + step]
+        out[lo:lo + step] = ((v + (((v >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+    return out.reshape(a.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -55,20 +59,23 @@ def router_logits(seed: int, m: int, e: int) -> np.ndarray:
     return np.random.default_rng([seed, 2]).standard_normal((m, e), dtype=np.float32)
 
 
-# Probability of each E2M1 magnitude code 0..7 (close to what quantizing a
-# normal block with its max mapped to 6 gives).
-_CODE_P = np.array([0.11, 0.19, 0.17, 0.15, 0.15, 0.11, 0.08, 0.04])
-_CODE_P = _CODE_P / _CODE_P.sum()
+# E2M1 magnitude codes 0..7 drawn with probabilities close to what
+# quantizing a normal block with its max mapped to 6 gives, as counts out of
+# 128 (one random byte per element: low 7 bits pick the magnitude through
+# this table, the top bit is the sign).
+_CODE_COUNTS = [14, 24, 22, 19, 19, 14, 11, 5]
+_MAG_LUT = np.repeat(np.arange(8, dtype=np.uint8), _CODE_COUNTS)
+assert _MAG_LUT.size == 128
+_CODE_LUT = (_MAG_LUT[np.arange(256) & 0x7F] | ((np.arange(256) >> 7) << 3)).astype(np.uint8)
+# one random uint16 -> one packed byte (two codes, low byte -> even k)
+_PAIR_LUT = (_CODE_LUT[np.arange(65536) & 0xFF] | (_CODE_LUT[np.arange(65536) >> 8] << 4)).astype(np.uint8)
 
 
 def quantized_domain_weight(rng: np.random.Generator, n: int, k: int):
     """Synthetic NVFP4 weight drawn directly as codes/scales/global.
     Returns (codes u8[n, k/2], scales u8[n, k/16], g_dec f32)."""
-    mag = rng.choice(8, size=(n, k), p=_CODE_P).astype(np.uint8)
-    sign = (rng.integers(0, 2, size=(n, k), dtype=np.uint8) << 3)
-    code = mag | sign
-    codes = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    # E4M3 bytes 0x50..0x7E: scales roughly 4 .. 448, the band quantized
+    codes = _PAIR_LUT[rng.integers(0, 65536, size=(n, k // 2), dtype=np.uint16)]
+    # E4M3 bytes 0x50..0x7E: scales roughly 8 .. 448, the band quantized
     # normal weights land in with a global scale of amax/2688.
     scales = rng.integers(0x50, 0x7F, size=(n, k // 16), dtype=np.uint8)
     g_dec = np.float32(rng.uniform(1e-5, 3e-5))
@@ -81,11 +88,9 @@ def moe_quantized_experts(seed: int, num_experts: int, hidden: int, inter: int):
     rng = np.random.default_rng([seed, 3])
     out = []
     for rows, cols in ((inter, hidden), (inter, hidden), (hidden, inter)):
-        c = np.empty((num_experts, rows, cols // 2), np.uint8)
-        s = np.empty((num_experts, rows, cols // 16), np.uint8)
-        g = np.empty(num_experts, np.float32)
-        for e in range(num_experts):
-            c[e], s[e], g[e] = quantized_domain_weight(rng, rows, cols)
+        c = _PAIR_LUT[rng.integers(0, 65536, size=(num_experts, rows, cols // 2), dtype=np.uint16)]
+        s = rng.integers(0x50, 0x7F, size=(num_experts, rows, cols // 16), dtype=np.uint8)
+        g = rng.uniform(1e-5, 3e-5, size=num_experts).astype(np.float32)
         out.append((c, s, g))
     return out
 

@@ -90,9 +90,15 @@ ORC_API int orc_e2m1_encode(float v) {
     if (a >= 6.0) {
         best = 7;
     } else {
+        static double grid[8];
+        static int grid_ready = 0;
+        if (!grid_ready) {
+            for (int c = 0; c < 8; ++c) grid[c] = orc_e2m1_decode(c);
+            grid_ready = 1;
+        }
         double bd = INFINITY;
         for (int c = 0; c < 8; ++c) {
-            double d = fabs(a - orc_e2m1_decode(c));
+            double d = fabs(a - grid[c]);
             if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
         }
     }
@@ -211,28 +217,36 @@ ORC_API void orc_dequantize(const uint8_t *codes, const uint8_t *scales, float g
  * convention of [mtp_head.rs] `MtpHead::gemv` and of the prefill GEMM in
  * [prefill.rs].  fp64 sum of exact terms, one fp32 rounding at the end.   */
 /* ------------------------------------------------------------------ */
-static double dot_row(const uint16_t *xrow, const uint8_t *crow, const uint8_t *srow, int64_t k) {
-    double acc = 0.0;
+/* Decode tables filled from the closed forms above (exact values; a lookup
+ * instead of recomputing ldexp per element keeps the full-size cases fast). */
+static double E2M1_TAB[16], E4M3_TAB[256];
+static int tabs_ready = 0;
+static void init_tabs(void) {
+    if (tabs_ready) return;
+    for (int c = 0; c < 16; ++c) E2M1_TAB[c] = orc_e2m1_decode(c);
+    for (int b = 0; b < 256; ++b) E4M3_TAB[b] = orc_e4m3_decode(b);
+    tabs_ready = 1;
+}
+
+/* sum_k x[k] * e2m1(code[k]) * e4m3(scale[k/16]) in fp64 (every term exact);
+ * optionally also sum_k |term| for rounding-error bounds. */
+static double dot_row2(const uint16_t *xrow, const uint8_t *crow, const uint8_t *srow, int64_t k,
+                       double *abs_sum) {
+    init_tabs();
+    double acc = 0.0, aacc = 0.0;
     for (int64_t c = 0; c < k; ++c) {
         uint8_t byte = crow[c / 2];
         int code = (c & 1) ? (byte >> 4) : (byte & 15);
-        double term = (double)bf16_to_f32(xrow[c]) * orc_e2m1_decode(code) *
-                      orc_e4m3_decode(srow[c / 16]);
+        double term = (double)bf16_to_f32(xrow[c]) * E2M1_TAB[code] * E4M3_TAB[srow[c / 16]];
         acc += term;
+        aacc += fabs(term);
     }
+    if (abs_sum) *abs_sum = aacc;
     return acc;
 }
 
-/* Sum of |terms| of the same dot product (for rounding-error bounds). */
-static double absdot_row(const uint16_t *xrow, const uint8_t *crow, const uint8_t *srow, int64_t k) {
-    double acc = 0.0;
-    for (int64_t c = 0; c < k; ++c) {
-        uint8_t byte = crow[c / 2];
-        int code = (c & 1) ? (byte >> 4) : (byte & 15);
-        acc += fabs((double)bf16_to_f32(xrow[c]) * orc_e2m1_decode(code) *
-                    orc_e4m3_decode(srow[c / 16]));
-    }
-    return acc;
+static double dot_row(const uint16_t *xrow, const uint8_t *crow, const uint8_t *srow, int64_t k) {
+    return dot_row2(xrow, crow, srow, k, NULL);
 }
 
 ORC_API void orc_gemv(const uint16_t *x, int64_t m, const uint8_t *codes, const uint8_t *scales,
@@ -274,9 +288,10 @@ ORC_API void orc_lmhead_argmax(const uint16_t *h, int64_t m, const uint8_t *code
         for (int64_t r = 0; r < vrows; ++r) {
             const uint8_t *crow = codes + r * (k / 2);
             const uint8_t *srow = scales + r * (k / 16);
-            float logit = (float)((double)g_dec * dot_row(h + i * k, crow, srow, k));
+            double asum = 0.0;
+            float logit = (float)((double)g_dec * dot_row2(h + i * k, crow, srow, k, &asum));
             if (logits) logits[i * vrows + r] = logit;
-            if (abs_bound) abs_bound[i * vrows + r] = (double)g_dec * absdot_row(h + i * k, crow, srow, k);
+            if (abs_bound) abs_bound[i * vrows + r] = (double)g_dec * asum;
             float key = (flags & 1u) ? orc_bf16_round(logit) : logit;
             if (key > best) { best = key; bi = (int32_t)r; bestlogit = logit; have = 1; }
         }

@@ -1,0 +1,45 @@
+"""The HIP library loads on a machine without a GPU and exports every
+function include/nvfp4_mtp.h declares (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_mtp.h")
+LIB = os.path.join(ROOT, "nvfp4_w4a16_mtp_amd", "libnvfp4_mtp.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemm_m128", "lmhead_gemv_argmax", "moe_w4a16_gemv",
+              "lmhead_gemv_argmax_workspace_bytes", "moe_w4a16_gemv_workspace_bytes", "nvfp4_mtp_last_error"):
+        assert f in names, f
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run __graft_entry__.build())")
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(LIB)
+    for f in declared_functions():
+        assert hasattr(L, f), f"{f} declared in nvfp4_mtp.h but not exported"
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run __graft_entry__.build())")
+def test_argument_errors_need_no_gpu():
+    """Host-side validation rejects bad arguments before touching the GPU."""
+    import nvfp4_w4a16_mtp_amd as nv
+    L = nv.lib()
+    w = nv._Weight(0, 0, 0, 16, 32)
+    assert L.w4a16_gemv(None, 1, ctypes.byref(w), None, 0, None) == -1
+    assert b"NULL" in L.nvfp4_mtp_last_error()
+    assert L.nvfp4_quantize(ctypes.c_void_p(16), 4, 48, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                            ctypes.c_void_p(16), None) == -2
+    assert L.lmhead_gemv_argmax_workspace_bytes(8, 151936) >= 8 * 16

@@ -1,0 +1,79 @@
+"""GPU parity: w4a16_gemm_m128 (C ABI) vs the oracle: bit-exact on the exact-
+arithmetic family (bf16 MFMA products are exact), within tolerance on normal
+inputs, sampled at the prefill configurations."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_w4a16_mtp_amd import synth
+from tests.gpu_util import assert_close, bf16_round_f64, dev_bf16, dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(codes, scales, g_dec):
+    import nvfp4_w4a16_mtp_amd as nv
+    return nv.NVFP4Weight.from_parts(dev_u8(codes), dev_u8(scales), float(g_dec))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (128, 128, 64), (200, 384, 512), (77, 130, 96), (300, 512, 2048)])
+def test_exact_family_bit_exact(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(200 + m, m, n, k)
+    y = nv.w4a16_gemm_m128(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 2048, 4096), (257, 512, 2048)])
+def test_random_full(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    w = synth.weight_bf16(300 + n, n, k)
+    x = synth.acts_bf16(301, m, k)
+    codes, scales, glob = orc.quantize(w)
+    y = nv.w4a16_gemm_m128(dev_bf16(x), _w(codes, scales, glob[0])).cpu().numpy()
+    assert_close(y, orc.gemv(x, codes, scales, glob[0]), f"gemm {m}x{n}x{k}")
+
+
+def test_gemm_m1_equals_gemv(orc):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(9, 8, 512, 1024)
+    wd = _w(codes, scales, g)
+    a = nv.w4a16_gemm_m128(dev_bf16(x), wd).cpu().numpy()
+    b = nv.w4a16_gemv(dev_bf16(x), wd).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+_WEIGHTS = {}
+
+
+@pytest.mark.parametrize("m", [128, 1024, 8192])
+@pytest.mark.parametrize("name,n,k", [("fc", 2048, 4096), ("kv", 512, 2048), ("gate_up", 17408, 5120),
+                                      ("down", 5120, 17408)])
+def test_prefill_configs_sampled(orc, m, name, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    if name not in _WEIGHTS:
+        codes, scales, g = synth.quantized_domain_weight(np.random.default_rng([400, n, k]), n, k)
+        _WEIGHTS[name] = (codes, scales, g, _w(codes, scales, g))
+    codes, scales, g, wd = _WEIGHTS[name]
+    rng = np.random.default_rng(400 + m)
+    x = synth.acts_bf16(401 + m, m, k)
+    y = nv.w4a16_gemm_m128(dev_bf16(x), wd)
+    mi = rng.integers(0, m, 3000)
+    ni = rng.integers(0, n, 3000)
+    mi[:4] = [0, m - 1, 0, m - 1]
+    ni[:4] = [0, n - 1, n - 1, 0]
+    got = y[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    ref = orc.gemm_sample(x, codes, scales, g, mi, ni)
+    assert_close(got, ref, f"{name} m={m}")
+
+
+def test_bf16_output(orc):
+    import nvfp4_w4a16_mtp_amd as nv
+    w = synth.weight_bf16(500, 256, 512)
+    x = synth.acts_bf16(501, 130, 512)
+    codes, scales, glob = orc.quantize(w)
+    wd = _w(codes, scales, glob[0])
+    y32 = nv.w4a16_gemm_m128(dev_bf16(x), wd).cpu().numpy()
+    yb = nv.w4a16_gemm_m128(dev_bf16(x), wd, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(yb, bf16_round_f64(y32).astype(np.float32))

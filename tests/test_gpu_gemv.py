@@ -1,0 +1,93 @@
+"""GPU parity: w4a16_gemv (C ABI) vs the oracle.  Bit-exact on the exact-
+arithmetic family, within |d| <= 1e-3 + 2e-3 |ref| on normal inputs, at the
+tiny and the Qwen-shaped projection sizes for M = 1..8."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_w4a16_mtp_amd import synth
+from tests.gpu_util import assert_close, bf16_round_f64, dev_bf16, dev_u8
+
+pytestmark = pytest.mark.gpu
+
+PROJ = {"fc": (2048, 4096), "q": (8192, 2048), "k": (512, 2048), "v": (512, 2048), "o": (2048, 4096)}
+
+
+def _w(codes, scales, g_dec):
+    import nvfp4_w4a16_mtp_amd as nv
+    return nv.NVFP4Weight.from_parts(dev_u8(codes), dev_u8(scales), float(g_dec))
+
+
+@pytest.mark.parametrize("m", range(1, 9))
+@pytest.mark.parametrize("n,k", [(64, 32), (333, 512), (96, 4096), (2050, 2048)])
+def test_exact_family_bit_exact(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(100 + m, m, n, k)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+def test_tiny_config(orc):
+    import nvfp4_w4a16_mtp_amd as nv
+    w = synth.weight_bf16(0, 512, 256)
+    x = synth.acts_bf16(0, 1, 256)
+    q = nv.nvfp4_quantize(dev_bf16(w))
+    codes, scales, glob = orc.quantize(w)
+    assert np.array_equal(q.codes.cpu().numpy(), codes)
+    y = nv.w4a16_gemv(dev_bf16(x), q).cpu().numpy()
+    assert_close(y, orc.gemv(x, codes, scales, glob[0]), "tiny")
+
+
+@pytest.mark.parametrize("name", list(PROJ))
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_projection_configs(orc, name, m):
+    import nvfp4_w4a16_mtp_amd as nv
+    n, k = PROJ[name]
+    w = synth.weight_bf16(20 + len(name), n, k)
+    x = synth.acts_bf16(30 + m, m, k)
+    codes, scales, glob = orc.quantize(w)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, glob[0])).cpu().numpy()
+    assert_close(y, orc.gemv(x, codes, scales, glob[0]), f"{name} m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_bf16_output(orc, m):
+    import nvfp4_w4a16_mtp_amd as nv
+    w = synth.weight_bf16(40, 700, 1024)
+    x = synth.acts_bf16(41, m, 1024)
+    codes, scales, glob = orc.quantize(w)
+    wd = _w(codes, scales, glob[0])
+    y32 = nv.w4a16_gemv(dev_bf16(x), wd).cpu().numpy()
+    yb = nv.w4a16_gemv(dev_bf16(x), wd, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(yb, bf16_round_f64(y32).astype(np.float32))      # RNE of the fp32 result
+    ref = orc.gemv(x, codes, scales, glob[0])
+    ulp = np.abs(bf16_round_f64(ref)) * 2.0 ** -7
+    assert (np.abs(yb - bf16_round_f64(ref)) <= ulp + 1e-30).all()           # within 1 bf16 ulp
+
+
+def test_empty_and_errors():
+    import nvfp4_w4a16_mtp_amd as nv
+    x = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda")
+    w0 = nv.NVFP4Weight.from_parts(torch.zeros((0, 32), dtype=torch.uint8, device="cuda"),
+                                   torch.zeros((0, 4), dtype=torch.uint8, device="cuda"), 1.0)
+    assert nv.w4a16_gemv(x, w0).shape == (1, 0)
+    w = nv.NVFP4Weight.from_parts(torch.zeros((4, 32), dtype=torch.uint8, device="cuda"),
+                                  torch.zeros((4, 4), dtype=torch.uint8, device="cuda"), 1.0)
+    with pytest.raises(nv.NVFP4Error):
+        nv.w4a16_gemv(torch.zeros((9, 64), dtype=torch.bfloat16, device="cuda"), w)
+    bad = nv.NVFP4Weight(w.codes, w.scales, w.glob, 4, 48)
+    with pytest.raises(nv.NVFP4Error):
+        nv.w4a16_gemv(torch.zeros((1, 48), dtype=torch.bfloat16, device="cuda"), bad)
+
+
+def test_no_write_outside_output(orc):
+    """Canary words around y stay untouched."""
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(7, 3, 100, 256)
+    buf = torch.full((3 * 100 + 128,), 12345.0, dtype=torch.float32, device="cuda")
+    y = buf[64:64 + 300].view(3, 100)
+    nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g), out=y)
+    b = buf.cpu().numpy()
+    assert (b[:64] == 12345.0).all() and (b[364:] == 12345.0).all()
+    assert np.array_equal(y.cpu().numpy(), orc.gemv(x, codes, scales, g))
