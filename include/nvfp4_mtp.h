@@ -126,7 +126,8 @@ int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint8_t *codes,
  *   x_bf16  [m][w->k] bf16, 16-byte aligned; m in 1..8.
  *   y       [m][w->n], fp32 (y_dtype NVFP4_OUT_F32) or bf16 rounded to
  *           nearest-even from the fp32 sum (NVFP4_OUT_BF16); 4-byte aligned.
- * fp32 accumulation; one pass over codes and scales.
+ * fp32 accumulation; one pass over codes and scales; one launch.  The
+ * activations are staged in LDS: round_up_pow2(m) * k * 2 <= 65536.
  */
 int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
                int32_t y_dtype, void *stream);
@@ -139,7 +140,7 @@ int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y
  *   x_bf16  [m][w->k] bf16, 16-byte aligned; m >= 1 (any m; work is tiled in
  *           128-row blocks, a ragged last block is masked).
  *   y       [m][w->n] fp32 or bf16 (y_dtype), 4-byte aligned.
- * Requires w->n % 16 == 0.
+ * Any n >= 0; rows and columns outside the 128 x 128 tiles are masked.
  */
 int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
                     int32_t y_dtype, void *stream);
@@ -159,9 +160,12 @@ int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, vo
  *            key exceeds -inf the index is 0.
  *   out_max  [m] fp32: the fp32 logit of the selected row.
  *   workspace device scratch of at least
- *            lmhead_gemv_argmax_workspace_bytes(m, V) bytes, 256-byte
- *            aligned; contents on entry are ignored.
- * Rows with equal codes and scales produce bit-identical logits.
+ *            lmhead_gemv_argmax_workspace_bytes(m, V) bytes (V = the number
+ *            of rows scored), 256-byte aligned.  It holds a ticket counter
+ *            that must be zero before the first call (zero-fill the buffer
+ *            once); each call returns it to zero.  A workspace serves one
+ *            call at a time: calls that overlap on one workspace race.
+ * Rows with equal codes and scales produce bit-identical logits.  One launch.
  */
 size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows);
 int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
@@ -181,10 +185,13 @@ int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
  *                  lower id first among equal logits.
  *   topk_w         out [m][top_k] fp32: softmax over the selected logits.
  *   workspace      at least moe_w4a16_gemv_workspace_bytes(m, top_k, e),
- *                  256-byte aligned; contents on entry are ignored.
+ *                  256-byte aligned, zero-filled before its first use (it
+ *                  holds per-tile ticket counters that every call returns to
+ *                  zero).  One call at a time per workspace.
  * Per selected expert: g = gate x, u = up x (fp32),
  * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
- * read once per call however many rows select it.  Requires H, I % 32 == 0.
+ * read once per call however many rows select it.  Requires H, I % 32 == 0
+ * and H, I <= 3968.  Three launches (route, gate/up, down + combine).
  */
 size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
 int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,

@@ -201,8 +201,10 @@ def w4a16_gemm_m128(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, ou
 
 
 def lmhead_workspace(m: int, vocab_rows: int, device) -> torch.Tensor:
+    """Zero-filled workspace for lmhead_gemv_argmax scoring `vocab_rows` rows
+    (the effective V).  It must start zeroed; every call leaves it reusable."""
     nbytes = lib().lmhead_gemv_argmax_workspace_bytes(m, vocab_rows)
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,
@@ -212,7 +214,8 @@ def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf1
     _dev(h, "h")
     m = h.shape[0]
     if workspace is None:
-        workspace = lmhead_workspace(m, vocab_rows, h.device)
+        v = w.n if vocab_rows <= 0 else min(vocab_rows, w.n)
+        workspace = lmhead_workspace(m, v, h.device)
     if out_idx is None:
         out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
     if out_max is None:
@@ -226,9 +229,11 @@ def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf1
 
 
 def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:
+    """Zero-filled workspace for moe_w4a16_gemv (must start zeroed; every call
+    leaves it reusable)."""
     d = experts.desc()
     nbytes = lib().moe_w4a16_gemv_workspace_bytes(m, top_k, ctypes.byref(d))
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, experts: NVFP4Experts,

@@ -3,7 +3,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "common.hpp"
 
@@ -55,6 +57,21 @@ int num_cus() {
         cache[dev] = v;
     }
     return cache[dev];
+}
+
+int blocks_per_cu(const void *kernel, int block, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_tuple(dev, kernel, block, lds);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, block, lds) != hipSuccess || v < 1) v = 1;
+    cache[key] = v;
+    return v;
 }
 
 }  // namespace nvfp4

@@ -24,6 +24,9 @@ int validate_weight(const nvfp4_weight *w, const char *what);
 
 // Number of compute units of the current device (cached per device).
 int num_cus();
+// Resident workgroups per CU for a kernel at a block size and dynamic LDS
+// (hipOccupancyMaxActiveBlocksPerMultiprocessor, cached; at least 1).
+int blocks_per_cu(const void *kernel, int block, size_t lds);
 
 // ----------------------------------------------------------- bf16 / fp32 --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -66,6 +69,24 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)); // mirror
     return v;
 }
+
+// Cross-workgroup hand-off without cache-wide fences.  Values one workgroup
+// publishes for another are written with device-scope stores (they write
+// through the XCD-local L2), the writer waits for its memory operations to
+// complete before taking a ticket with a device-scope atomic, and the
+// workgroup that draws the last ticket reads with device-scope loads (they
+// do not hit stale L2 lines).  A release/acquire fence would also work but
+// writes back or invalidates the whole L2 of the XCD, once per workgroup.
+template <class T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory operation this thread issued has completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Argmax combine: (v, i) beats (bv, bi) when v > bv, or v == bv with a lower
 // index.  NaN never wins (both comparisons are false).

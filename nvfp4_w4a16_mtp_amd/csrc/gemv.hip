@@ -1,46 +1,53 @@
 // W4A16 decode GEMV and the LM-head GEMV fused with argmax.
 //
 // w4a16_gemv: the projection GEMV of mtp_head.rs (`MtpHead::gemv` ->
-// `w4a16_decode_gemv`) for M = 1..8 rows, used for the head's fc, q/k/v/o
+// `w4a16_decode_gemv`) for M = 1..8 rows, used for the head's fc and q/k/v/o
 // projections (new.rs, `MtpHead::new` quantizes exactly these).
 //
 // lmhead_gemv_argmax: the NVFP4 LM head over the first V vocabulary rows and
 // the argmax that turns it into the draft token (new.rs resolves the NVFP4
 // LM head and `argmax_bf16`; deepseek_v4_mtp.rs `forward_one` runs LM head
-// then argmax, with the reduced vocabulary).  Pass 1 computes logits tile by
-// tile and keeps, per workgroup and row m, the best (key, index); no logits
-// tensor is written.  Pass 2 (one workgroup) combines the partials.  The
-// combine keeps the larger key and, on equal keys, the lower index, which is
-// exactly the ascending strict-greater scan of `argmax_grammar_masked`.
+// then argmax, with the reduced vocabulary).  One launch: each workgroup
+// scores one tile of rows and writes, per activation row, the best (key,
+// index) of its tile; the last workgroup to finish (a ticket counter in the
+// workspace, returned to zero afterwards) combines the partials.  No logits
+// tensor is written.  The combine keeps the larger key and, on equal keys,
+// the lower index -- exactly the ascending strict-greater scan of
+// `argmax_grammar_masked`, independent of the order workgroups finish in.
 #include <float.h>
 
 #include "gemv_core.hpp"
 
 namespace nvfp4 {
 
-constexpr int kMaxPartials = 4096;        // LM-head pass-1 workgroups at most
-constexpr int kLmStaticLds = 16 * 8 * 16; // per-slot argmax candidates of pass 1
-
-template <int M, int R, int KS, bool BF16OUT>
-__global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+template <int MT, int R, int KS, int CPL>
+__global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                              const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                             int n, int k, void *__restrict__ y) {
+                                             int n, int k, void *__restrict__ y, int bf16out) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
-    float *red = reinterpret_cast<float *>(smem + (M * k) / 8);
-    stage_x(xs, reinterpret_cast<const uint4 *>(x), M, k);
-    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
+    constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
+    const int row0 = blockIdx.x * rows;
     const float dec = g->dec;
-    constexpr int rows = GemvTile<M, R, KS>::kRowsPerTile;
-    const int ntiles = (n + rows - 1) / rows;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        gemv_tile<M, R, KS>(xs, codes, scales, n, k, tile * rows, red, [&](int row, int mm, float v) {
-            const float o = v * dec;
-            if constexpr (BF16OUT)
-                reinterpret_cast<uint16_t *>(y)[(size_t)mm * n + row] = (uint16_t)f32_to_bf16_bits(o);
-            else
-                reinterpret_cast<float *>(y)[(size_t)mm * n + row] = o;
-        });
+    auto epi = [&](int row, int mm, float v) {
+        if (mm >= m_rt) return;
+        const float o = v * dec;
+        if (bf16out)
+            reinterpret_cast<uint16_t *>(y)[(size_t)mm * n + row] = (uint16_t)f32_to_bf16_bits(o);
+        else
+            reinterpret_cast<float *>(y)[(size_t)mm * n + row] = o;
+    };
+    if constexpr (CPL > 0) {
+        TileRegs<MT, R, KS, CPL> t;
+        gemv_tile_load(t, codes, scales, n, k, row0);   // weight loads in flight while x is staged
+        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __syncthreads();
+        gemv_tile_compute(t, xs, n, k, row0, red, epi);
+    } else {
+        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __syncthreads();
+        gemv_tile_loop<MT, R, KS>(xs, codes, scales, n, k, row0, red, epi);
     }
 }
 
@@ -51,147 +58,222 @@ struct ArgPart {
     int pad;
 };
 
-template <int M, int R, int KS, bool BF16KEY>
-__global__ __launch_bounds__(256) void k_lmhead_pass1(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
-                                                     const uint8_t *__restrict__ scales,
-                                                     const nvfp4_global *__restrict__ g, int v, int k,
-                                                     ArgPart *__restrict__ parts, float *__restrict__ row0) {
-    extern __shared__ uint4 smem[];
-    uint4 *xs = smem;
-    float *red = reinterpret_cast<float *>(smem + (M * k) / 8);
-    stage_x(xs, reinterpret_cast<const uint4 *>(x), M, k);
-    __syncthreads();
-    const float dec = g->dec;
-    constexpr int rows = GemvTile<M, R, KS>::kRowsPerTile;
-    const int ntiles = (v + rows - 1) / rows;
-    // lane m of every slot keeps the best of the rows it was handed for m
-    float bkey = -INFINITY, bval = -INFINITY;
-    int bidx = INT_MAX;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        gemv_tile<M, R, KS>(xs, codes, scales, v, k, tile * rows, red, [&](int row, int mm, float s) {
-            const float logit = s * dec;
-            const float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
-            if (row == 0) row0[mm] = logit;
-            if (beats(key, row, bkey, bidx)) {
-                bkey = key;
-                bval = logit;
-                bidx = row;
-            }
-        });
-    }
-    // workgroup combine: 16 slots x M candidates -> M partials
-    __shared__ ArgPart cand[16][8];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane >> 4, t = lane & 15;
-    const int gslot = wave * 4 + slot;
-    if (t < M) cand[gslot][t] = ArgPart{bkey, bval, bidx, 0};
-    __syncthreads();
-    if (threadIdx.x < M) {
-        const int mm = threadIdx.x;
-        ArgPart best{-INFINITY, -INFINITY, INT_MAX, 0};
-        for (int s = 0; s < 16; ++s) {
-            // wavefronts of K segments other than 0 never produced candidates
-            ArgPart c = cand[s][mm];
-            if (KS > 1 && ((s >> 2) % KS) != 0) continue;
-            if (beats(c.key, c.idx, best.key, best.idx)) best = c;
-        }
-        parts[(size_t)blockIdx.x * M + mm] = best;
-    }
+__device__ __forceinline__ void argpart_shfl_combine(ArgPart &b, int off) {
+    ArgPart o;
+    o.key = __shfl_xor(b.key, off, 64);
+    o.val = __shfl_xor(b.val, off, 64);
+    o.idx = __shfl_xor(b.idx, off, 64);
+    o.pad = 0;
+    if (beats(o.key, o.idx, b.key, b.idx)) b = o;
 }
 
-__global__ __launch_bounds__(256) void k_lmhead_pass2(const ArgPart *__restrict__ parts, int nparts, int m,
-                                                     const float *__restrict__ row0, int32_t *__restrict__ out_idx,
-                                                     float *__restrict__ out_max) {
-    __shared__ ArgPart red[256];
-    for (int mm = 0; mm < m; ++mm) {
-        ArgPart best{-INFINITY, -INFINITY, INT_MAX, 0};
-        for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
-            ArgPart c = parts[(size_t)p * m + mm];
-            if (beats(c.key, c.idx, best.key, best.idx)) best = c;
-        }
-        red[threadIdx.x] = best;
+// Workspace layout of lmhead_gemv_argmax.
+constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
+constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
+constexpr int kLmParts = 256;     // ArgPart[ntiles][MT]
+
+// Persistent LM-head pass: workgroup g scores tiles [g * tpw, (g + 1) * tpw)
+// of the global tiling (16 * R rows per tile).  With a fixed chunk count the
+// next tile's loads are issued before the current tile is computed, so the
+// workgroup streams without gaps; the activations are staged once.
+template <int MT, int R, int KS, int CPL, bool BF16KEY>
+__global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
+                                               const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
+                                               int v, int k, int tpw, char *__restrict__ ws, int32_t *__restrict__ out_idx,
+                                               float *__restrict__ out_max) {
+    extern __shared__ uint4 smem[];
+    uint4 *xs = smem;
+    float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
+    __shared__ ArgPart cand[16][MT];
+    __shared__ ArgPart wbest[4][MT];
+    __shared__ int s_last;
+    unsigned int *ticket = reinterpret_cast<unsigned int *>(ws + kLmTicket);
+    float *row0 = reinterpret_cast<float *>(ws + kLmRow0);
+    ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
+
+    constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
+    const int ntiles = (v + rows - 1) / rows;
+    const int t_begin = blockIdx.x * tpw;
+    const int t_end = min(ntiles, t_begin + tpw);
+    const float dec = g->dec;
+    // lane m of every slot keeps the best of its rows for activation row m
+    ArgPart best{-INFINITY, -INFINITY, INT_MAX, 0};
+    auto epi = [&](int row, int mm, float s) {
+        const float logit = s * dec;
+        const float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
+        if (row == 0) st_dev(&row0[mm], logit);
+        if (beats(key, row, best.key, best.idx)) best = ArgPart{key, logit, row, 0};
+    };
+    if constexpr (CPL > 0) {
+        TileRegs<MT, R, KS, CPL> cur;
+        gemv_tile_load(cur, codes, scales, v, k, t_begin * rows);
+        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        for (int s = 128; s > 0; s >>= 1) {
-            if (threadIdx.x < s) {
-                ArgPart c = red[threadIdx.x + s];
-                if (beats(c.key, c.idx, red[threadIdx.x].key, red[threadIdx.x].idx)) red[threadIdx.x] = c;
-            }
-            __syncthreads();
+        for (int t = t_begin; t < t_end; ++t) {
+            TileRegs<MT, R, KS, CPL> nxt;
+            if (t + 1 < t_end)
+                gemv_tile_load(nxt, codes, scales, v, k, (t + 1) * rows);
+            else
+                nxt = cur;
+            gemv_tile_compute(cur, xs, v, k, t * rows, red, epi);
+            cur = nxt;
         }
-        if (threadIdx.x == 0) {
-            ArgPart b = red[0];
-            // nothing above -inf: the scan keeps its initial index 0
-            if (!(b.key > -INFINITY)) {
-                out_idx[mm] = 0;
-                out_max[mm] = row0[mm];
-            } else {
-                out_idx[mm] = b.idx;
-                out_max[mm] = b.val;
-            }
-        }
+    } else {
+        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
+        for (int t = t_begin; t < t_end; ++t) gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
     }
+
+    // workgroup combine: 16 slots x MT candidates -> MT partials
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane >> 4, t = lane & 15;
+    if (t < MT) cand[wave * 4 + slot][t] = best;
+    __syncthreads();
+    if (threadIdx.x < MT) {
+        const int mm = threadIdx.x;
+        ArgPart b{-INFINITY, -INFINITY, INT_MAX, 0};
+        for (int s = 0; s < 16; ++s) {
+            const ArgPart c = cand[s][mm];
+            if (beats(c.key, c.idx, b.key, b.idx)) b = c;
+        }
+        ArgPart *dst = parts + (size_t)blockIdx.x * MT + mm;
+        st_dev(&dst->key, b.key);
+        st_dev(&dst->val, b.val);
+        st_dev(&dst->idx, b.idx);
+    }
+    wait_mem();   // partials and row-0 logits have reached device scope
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+
+    // last workgroup: combine every tile's partials
+    const int nparts = gridDim.x;
+    ArgPart b[MT];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, 0};
+    for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+            const ArgPart *src = parts + (size_t)p * MT + mm;
+            const ArgPart c{ld_dev(&src->key), ld_dev(&src->val), ld_dev(&src->idx), 0};
+            if (beats(c.key, c.idx, b[mm].key, b[mm].idx)) b[mm] = c;
+        }
+    }
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) argpart_shfl_combine(b[mm], off);
+    if (lane == 0) {
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) wbest[wave][mm] = b[mm];
+    }
+    __syncthreads();
+    if (threadIdx.x < m_rt) {
+        const int mm = threadIdx.x;
+        ArgPart f = wbest[0][mm];
+        for (int w = 1; w < 4; ++w) {
+            const ArgPart c = wbest[w][mm];
+            if (beats(c.key, c.idx, f.key, f.idx)) f = c;
+        }
+        // nothing above -inf: the scan keeps its initial index 0
+        if (!(f.key > -INFINITY)) {
+            out_idx[mm] = 0;
+            out_max[mm] = ld_dev(&row0[mm]);
+        } else {
+            out_idx[mm] = f.idx;
+            out_max[mm] = f.val;
+        }
+    }
+    if (threadIdx.x == 0) st_dev(ticket, 0u);   // ready for the next call
 }
 
 // ------------------------------------------------------------ dispatch ----
-template <int M>
-static int launch_gemv_m(const uint16_t *x, const nvfp4_weight *w, void *y, bool bf16, hipStream_t s) {
-    const TileChoice tc = choose_tile(w->n, num_cus(), ksplit_fits(M, w->k));
-    const int rows = 16 * tc.R / tc.KS;
-    const int ntiles = (w->n + rows - 1) / rows;
-    const int grid = ntiles;
-    const size_t lds = gemv_lds_bytes(M, w->k, tc);
-#define NVFP4_GEMV_CASE(RR, KK)                                                                           \
-    if (tc.R == RR && tc.KS == KK) {                                                                      \
-        if (bf16)                                                                                         \
-            hipLaunchKernelGGL((k_gemv<M, RR, KK, true>), dim3(grid), dim3(256), lds, s, x, w->codes,     \
-                               w->scales, w->global, w->n, w->k, y);                                      \
-        else                                                                                              \
-            hipLaunchKernelGGL((k_gemv<M, RR, KK, false>), dim3(grid), dim3(256), lds, s, x, w->codes,    \
-                               w->scales, w->global, w->n, w->k, y);                                      \
-        return check_launch("w4a16_gemv");                                                                \
-    }
-    NVFP4_GEMV_CASE(4, 1)
-    NVFP4_GEMV_CASE(2, 1)
-    NVFP4_GEMV_CASE(1, 1)
-    NVFP4_GEMV_CASE(1, 2)
-    NVFP4_GEMV_CASE(1, 4)
-#undef NVFP4_GEMV_CASE
-    return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemv: no tile shape");
+// Instantiated tile shapes (R rows per slot, KS K-segments, CPL fixed chunks
+// per lane or 0 for the generic loop).
+#define NVFP4_TILE_SWITCH(FN, MT, tc, ...)                                               \
+    do {                                                                                 \
+        if (tc.R == 4 && tc.KS == 1 && tc.CPL == 4) FN<MT, 4, 1, 4>(__VA_ARGS__);        \
+        else if (tc.R == 4 && tc.KS == 1 && tc.CPL == 2) FN<MT, 4, 1, 2>(__VA_ARGS__);   \
+        else if (tc.R == 4 && tc.KS == 1) FN<MT, 4, 1, 0>(__VA_ARGS__);                  \
+        else if (tc.R == 2 && tc.KS == 1 && tc.CPL == 4) FN<MT, 2, 1, 4>(__VA_ARGS__);   \
+        else if (tc.R == 2 && tc.KS == 1) FN<MT, 2, 1, 0>(__VA_ARGS__);                  \
+        else if (tc.R == 1 && tc.KS == 1 && tc.CPL == 4) FN<MT, 1, 1, 4>(__VA_ARGS__);   \
+        else if (tc.R == 1 && tc.KS == 1 && tc.CPL == 2) FN<MT, 1, 1, 2>(__VA_ARGS__);   \
+        else if (tc.R == 1 && tc.KS == 1) FN<MT, 1, 1, 0>(__VA_ARGS__);                  \
+        else if (tc.KS == 2 && tc.CPL == 2) FN<MT, 1, 2, 2>(__VA_ARGS__);                \
+        else if (tc.KS == 2 && tc.CPL == 4) FN<MT, 1, 2, 4>(__VA_ARGS__);                \
+        else if (tc.KS == 2) FN<MT, 1, 2, 0>(__VA_ARGS__);                               \
+        else if (tc.KS == 4 && tc.CPL == 1) FN<MT, 1, 4, 1>(__VA_ARGS__);                \
+        else if (tc.KS == 4 && tc.CPL == 2) FN<MT, 1, 4, 2>(__VA_ARGS__);                \
+        else FN<MT, 1, 4, 0>(__VA_ARGS__);                                               \
+    } while (0)
+
+// Reduces a tile choice to the instantiated set above.
+static TileChoice canonical(TileChoice tc) {
+    if (tc.KS == 1 && tc.R == 4 && tc.CPL != 4 && tc.CPL != 2) tc.CPL = 0;
+    if (tc.KS == 1 && tc.R == 2 && tc.CPL != 4) tc.CPL = 0;
+    if (tc.KS == 1 && tc.R == 1 && tc.CPL != 4 && tc.CPL != 2) tc.CPL = 0;
+    if (tc.KS == 2 && tc.CPL != 2 && tc.CPL != 4) tc.CPL = 0;
+    if (tc.KS == 4 && tc.CPL != 1 && tc.CPL != 2) tc.CPL = 0;
+    return tc;
 }
 
-template <int M>
-static int launch_lmhead_m(const uint16_t *h, const nvfp4_weight *w, int v, ArgPart *parts, float *row0,
-                           int32_t *out_idx, float *out_max, bool bf16key, hipStream_t s) {
-    const bool ks_ok = gemv_lds_bytes(M, w->k, TileChoice{1, 2}) + kLmStaticLds <= (size_t)kLdsBytes;
-    const TileChoice tc = choose_tile(v, num_cus(), ks_ok);
+template <int MT, int R, int KS, int CPL>
+static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w,
+                            void *y, int bf16) {
+    hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, w->codes, w->scales, w->global, w->n,
+                       w->k, y, bf16);
+}
+
+template <int MT>
+static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16, hipStream_t s) {
+    const TileChoice tc = canonical(choose_tile(w->n, w->k, MT, 2 * num_cus(), 0));
     const int rows = 16 * tc.R / tc.KS;
-    const int ntiles = (v + rows - 1) / rows;
-    int grid = num_cus() * 4;
-    if (grid > ntiles) grid = ntiles;
-    if (grid > kMaxPartials) grid = kMaxPartials;
-    const size_t lds = gemv_lds_bytes(M, w->k, tc);
-#define NVFP4_LM_CASE(RR, KK)                                                                             \
-    if (tc.R == RR && tc.KS == KK) {                                                                      \
-        if (bf16key)                                                                                      \
-            hipLaunchKernelGGL((k_lmhead_pass1<M, RR, KK, true>), dim3(grid), dim3(256), lds, s, h,       \
-                               w->codes, w->scales, w->global, v, w->k, parts, row0);                     \
-        else                                                                                              \
-            hipLaunchKernelGGL((k_lmhead_pass1<M, RR, KK, false>), dim3(grid), dim3(256), lds, s, h,      \
-                               w->codes, w->scales, w->global, v, w->k, parts, row0);                     \
-        int rc = check_launch("lmhead_gemv_argmax(pass 1)");                                              \
-        if (rc) return rc;                                                                                \
-        hipLaunchKernelGGL(k_lmhead_pass2, dim3(1), dim3(256), 0, s, parts, grid, M, row0, out_idx,       \
-                           out_max);                                                                      \
-        return check_launch("lmhead_gemv_argmax(pass 2)");                                                \
+    const dim3 grid((w->n + rows - 1) / rows);
+    NVFP4_TILE_SWITCH(launch_gemv_cfg, MT, tc, grid, gemv_lds_bytes(MT, w->k, tc), s, x, m, w, y, bf16);
+    return check_launch("w4a16_gemv");
+}
+
+// Grid of the persistent LM-head kernel: as many workgroups as fit on the
+// device at once, each with the same number of tiles (the last fewer).
+template <class K>
+static int lm_grid(K kernel, size_t lds, int ntiles, int &tpw) {
+    const int cap = num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
+    tpw = (ntiles + cap - 1) / cap;
+    return (ntiles + tpw - 1) / tpw;
+}
+
+template <int MT, int R, int KS, int CPL>
+static void launch_lm_cfg(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws,
+                          int32_t *oi, float *om, bool bk) {
+    if constexpr (KS == 1) {
+        const int ntiles = (v + 16 * R - 1) / (16 * R);
+        int tpw = 1;
+        if (bk) {
+            auto kern = k_lmhead<MT, R, KS, CPL, true>;
+            const int grid = lm_grid(kern, lds, ntiles, tpw);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, tpw,
+                               ws, oi, om);
+        } else {
+            auto kern = k_lmhead<MT, R, KS, CPL, false>;
+            const int grid = lm_grid(kern, lds, ntiles, tpw);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, tpw,
+                               ws, oi, om);
+        }
     }
-    NVFP4_LM_CASE(4, 1)
-    NVFP4_LM_CASE(2, 1)
-    NVFP4_LM_CASE(1, 1)
-    NVFP4_LM_CASE(1, 2)
-    NVFP4_LM_CASE(1, 4)
-#undef NVFP4_LM_CASE
-    return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: no tile shape");
+}
+
+// The LM head keeps KS = 1 and R = 2 (two tiles of loads in flight per
+// wavefront fit in registers); there are at most ceil(V / 16) partials.
+template <int MT>
+static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
+                           bool bk, hipStream_t s) {
+    TileChoice tc{2, 1, 0};
+    if (w->k % 512 == 0 && (w->k / 512 == 4)) tc.CPL = 4;
+    tc = canonical(tc);
+    NVFP4_TILE_SWITCH(launch_lm_cfg, MT, tc, gemv_lds_bytes(MT, w->k, tc), s, h, m, w, v, ws, oi, om, bk);
+    return check_launch("lmhead_gemv_argmax");
 }
 
 }  // namespace nvfp4
@@ -202,35 +284,30 @@ extern "C" int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight 
                           void *stream) {
     int rc = validate_weight(w, "w4a16_gemv");
     if (rc) return rc;
-    if (w->n == 0 && m >= 1) return ok();   // empty output: nothing to read or write
-    if (!x_bf16 || !y) return fail(NVFP4_ERR_ARG, "w4a16_gemv: NULL x or y");
     if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "w4a16_gemv: m=%d outside 1..8", m);
+    if (w->n == 0) return ok();   // empty output: nothing to read or write
+    if (!x_bf16 || !y) return fail(NVFP4_ERR_ARG, "w4a16_gemv: NULL x or y");
     if (y_dtype != NVFP4_OUT_F32 && y_dtype != NVFP4_OUT_BF16)
         return fail(NVFP4_ERR_ARG, "w4a16_gemv: unknown y_dtype %d", y_dtype);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemv: x not 16-byte aligned");
     if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemv: y not 4-byte aligned");
-    if ((size_t)m * w->k * 2 > (size_t)kLdsBytes)
-        return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemv: m * k = %lld exceeds %d activations", (long long)m * w->k,
-                    kLdsBytes / 2);
+    const int mt = round_up_mt(m);
+    if ((size_t)mt * w->k * 2 > (size_t)kLdsBytes)
+        return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemv: %d (rounded-up) rows x k=%d activations exceed LDS", mt, w->k);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const bool bf16 = y_dtype == NVFP4_OUT_BF16;
-    switch (m) {
-        case 1: return launch_gemv_m<1>(x_bf16, w, y, bf16, s);
-        case 2: return launch_gemv_m<2>(x_bf16, w, y, bf16, s);
-        case 3: return launch_gemv_m<3>(x_bf16, w, y, bf16, s);
-        case 4: return launch_gemv_m<4>(x_bf16, w, y, bf16, s);
-        case 5: return launch_gemv_m<5>(x_bf16, w, y, bf16, s);
-        case 6: return launch_gemv_m<6>(x_bf16, w, y, bf16, s);
-        case 7: return launch_gemv_m<7>(x_bf16, w, y, bf16, s);
-        default: return launch_gemv_m<8>(x_bf16, w, y, bf16, s);
+    const int bf16 = y_dtype == NVFP4_OUT_BF16;
+    switch (mt) {
+        case 1: return launch_gemv_m<1>(x_bf16, m, w, y, bf16, s);
+        case 2: return launch_gemv_m<2>(x_bf16, m, w, y, bf16, s);
+        case 4: return launch_gemv_m<4>(x_bf16, m, w, y, bf16, s);
+        default: return launch_gemv_m<8>(x_bf16, m, w, y, bf16, s);
     }
 }
 
 extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows) {
-    (void)vocab_rows;
-    if (m < 1) m = 1;
-    if (m > 8) m = 8;
-    return (size_t)kMaxPartials * m * sizeof(ArgPart) + 256;
+    if (vocab_rows < 1) return 0;
+    const int mt = round_up_mt(m < 1 ? 1 : (m > 8 ? 8 : m));
+    return (size_t)kLmParts + (size_t)sizeof(ArgPart) * mt * (size_t)((vocab_rows + 15) / 16);
 }
 
 extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
@@ -246,25 +323,21 @@ extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4
     if (v < 1) return fail(NVFP4_ERR_SHAPE, "lmhead_gemv_argmax: empty vocabulary");
     if (!aligned(h_bf16, 16) || !aligned(out_idx, 4) || !aligned(out_max, 4))
         return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax: h needs 16-byte, outputs 4-byte alignment");
-    if ((size_t)m * w->k * 2 + kLmStaticLds > (size_t)kLdsBytes)
-        return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: m * k exceeds %d activations",
-                    (kLdsBytes - kLmStaticLds) / 2);
-    if (!workspace || ws_bytes < lmhead_gemv_argmax_workspace_bytes(m, vocab_rows))
-        return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax: workspace needs %zu bytes",
-                    lmhead_gemv_argmax_workspace_bytes(m, vocab_rows));
+    const int mt = round_up_mt(m);
+    if ((size_t)mt * w->k * 2 > (size_t)kLdsBytes - 4096)
+        return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: %d (rounded-up) rows x k=%d activations exceed LDS", mt,
+                    w->k);
+    const size_t need = lmhead_gemv_argmax_workspace_bytes(m, v);
+    if (!workspace || ws_bytes < need)
+        return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax: workspace needs %zu bytes for %d rows", need, v);
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax: workspace not 256-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float *row0 = reinterpret_cast<float *>(workspace);
-    ArgPart *parts = reinterpret_cast<ArgPart *>(reinterpret_cast<char *>(workspace) + 256);
+    char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
-    switch (m) {
-        case 1: return launch_lmhead_m<1>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 2: return launch_lmhead_m<2>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 3: return launch_lmhead_m<3>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 4: return launch_lmhead_m<4>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 5: return launch_lmhead_m<5>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 6: return launch_lmhead_m<6>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        case 7: return launch_lmhead_m<7>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
-        default: return launch_lmhead_m<8>(h_bf16, w, v, parts, row0, out_idx, out_max, bk, s);
+    switch (mt) {
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
+        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
+        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
+        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
     }
 }

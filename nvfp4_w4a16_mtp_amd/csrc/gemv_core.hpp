@@ -3,8 +3,10 @@
 //
 // The operation is the `w4a16_decode_gemv` of mtp_head.rs (`MtpHead::gemv`)
 // and its batched-M tiers (one pass over the weight serves all rows).  On
-// gfx950 it is bound by HBM: every weight byte is read exactly once with
-// 16-byte loads, the activations are staged once per workgroup in LDS.
+// gfx950 it is bound by HBM: every weight byte is read exactly once, with
+// 16-byte non-temporal loads (the weights stream; keeping them out of the
+// caches leaves room for the activations), and the activations are staged
+// once per workgroup in LDS.
 //
 // Work mapping (workgroup = 256 threads = 4 wavefronts):
 //  * a "slot" is 16 lanes (one DPP row); a slot owns R weight rows and the
@@ -12,12 +14,17 @@
 //    = 32 weights per chunk) round-robin;
 //  * with KS > 1 the 4 wavefronts split K into KS segments over the same
 //    rows (for short-and-wide matrices that would otherwise leave CUs idle);
-//  * a workgroup tile is 16 * R / KS rows; workgroups stride over tiles.
+//  * a workgroup tile is 16 * R / KS rows.
+// When every lane owns exactly CPL chunks of each row (K = 512 * KS * CPL),
+// all R * CPL chunk loads of a tile are issued before any arithmetic, so a
+// wavefront keeps R * CPL * 1 KiB in flight; other shapes take a loop.
 // Per chunk a lane converts 32 E2M1 codes to bf16 with the hardware FP4
-// converter (exact), takes bf16 dot products with the activation chunk read
-// from LDS (fp32 accumulation), and applies the two E4M3 block scales with
-// one FMA each.  The 16 lanes of a slot are summed with a fixed DPP
-// butterfly, so every row is reduced in the same order wherever it runs.
+// converter and its two E4M3 scales with the hardware FP8 converter (both
+// exact), takes bf16 dot products with the activation chunk read from LDS
+// (fp32 accumulation), and applies the block scales with one FMA each.  The
+// 16 lanes of a slot are summed with a fixed DPP butterfly, so every row is
+// reduced in the same order wherever it runs (identical rows give identical
+// results).
 #pragma once
 
 #include <climits>
@@ -27,131 +34,148 @@
 
 namespace nvfp4 {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t *p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream2(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+}
+
+// Both E4M3FN scale bytes of a chunk (low byte first) -> fp32, exactly.
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t two, float &s0, float &s1) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
+    s0 = f.x;
+    s1 = f.y;
+}
+
 // LDS image of x: 16-byte units, unit (m, q, c) = x[m][32c + 8q .. 32c + 8q + 8)
 // at index (m * 4 + q) * C + c, so that the 16 lanes of a slot reading
-// consecutive chunks hit consecutive LDS addresses.
-__device__ __forceinline__ void stage_x(uint4 *xs, const uint4 *__restrict__ x, int m, int k) {
-    const int C = k >> 5;
-    const int units = m * (k >> 3);
+// consecutive chunks hit consecutive LDS addresses.  Rows m_rt .. MT-1 are
+// zero-filled (the kernel is instantiated for MT >= m_rt rows).
+__device__ __forceinline__ void stage_x(uint4 *xs, const uint4 *__restrict__ x, int m_rt, int mt, int k) {
+    const int C = k >> 5, upr = k >> 3;
+    const int units = mt * upr;
     for (int p = threadIdx.x; p < units; p += blockDim.x) {
-        int mm = p / (k >> 3), w = p - mm * (k >> 3);
+        int mm = p / upr, w = p - mm * upr;
         int c = w >> 2, q = w & 3;
-        xs[(mm * 4 + q) * C + c] = x[p];
+        xs[(mm * 4 + q) * C + c] = mm < m_rt ? x[p] : make_uint4(0, 0, 0, 0);
     }
 }
 
-template <int M, int R, int KS>
+template <int R, int KS>
 struct GemvTile {
     static constexpr int kRowsPerTile = 16 * R / KS;
 };
 
+// One chunk of one row: dot products with the MT activation rows, scaled.
+template <int MT>
+__device__ __forceinline__ void chunk_fma(const uint4 cw, uint32_t sw, const uint4 *xs, int C, int c, float (&acc)[MT]) {
+    float sf0, sf1;
+    e4m3x2_to_f32(sw, sf0, sf1);
+    const uint32_t cwd[4] = {cw.x, cw.y, cw.z, cw.w};
+    bf16x2 wv[16];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        wv[4 * d + 0] = e2m1x2_to_bf16<0>(cwd[d]);
+        wv[4 * d + 1] = e2m1x2_to_bf16<1>(cwd[d]);
+        wv[4 * d + 2] = e2m1x2_to_bf16<2>(cwd[d]);
+        wv[4 * d + 3] = e2m1x2_to_bf16<3>(cwd[d]);
+    }
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+        const uint4 x0 = xs[(mm * 4 + 0) * C + c], x1 = xs[(mm * 4 + 1) * C + c];
+        const uint4 x2 = xs[(mm * 4 + 2) * C + c], x3 = xs[(mm * 4 + 3) * C + c];
+        const uint32_t xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const uint32_t xb[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b0 = dot2(wv[i], as_bf16x2(xa[i]), b0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b1 = dot2(wv[8 + i], as_bf16x2(xb[i]), b1);
+        acc[mm] = __builtin_fmaf(b0, sf0, acc[mm]);
+        acc[mm] = __builtin_fmaf(b1, sf1, acc[mm]);
+    }
+}
+
 // Computes the tile's dot products; calls epi(row, m, value) once per
-// (row < n, m < M) with the fp32 sum (before the global scale), from lane
+// (row < n, m < MT) with the fp32 sum (before the global scale), from lane
 // m of the slot in the K-segment-0 wavefront.  red: LDS scratch of
-// 16 * R * M floats (used when KS > 1).
-template <int M, int R, int KS, class Epi>
-__device__ __forceinline__ void gemv_tile(const uint4 *xs, const uint8_t *__restrict__ codes,
-                                          const uint8_t *__restrict__ scales, int n, int k, int row0,
-                                          float *red, Epi &&epi) {
+// 16 * R * MT floats (used when KS > 1).  If PRELOADED, the first tile's
+// loads were issued by gemv_tile_load into `pre` before x was staged.
+template <int MT, int R, int KS, int CPL>
+struct TileRegs {
+    uint4 c[R][CPL > 0 ? CPL : 1];
+    uint32_t s[R][CPL > 0 ? CPL : 1];
+};
+
+template <int MT, int R, int KS, int CPL>
+__device__ __forceinline__ void gemv_tile_load(TileRegs<MT, R, KS, CPL> &t, const uint8_t *__restrict__ codes,
+                                               const uint8_t *__restrict__ scales, int n, int k, int row0) {
+    static_assert(CPL > 0, "preloading needs a fixed chunk count");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane >> 4, tl = lane & 15;
+    const int ks = (KS == 1) ? 0 : (wave % KS);
+    const int rg = wave / KS;
+    const int rbase = row0 + (rg * 4 + slot) * R;
+    const int c_lo = ks * 16 * CPL;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = rbase + r;
+        const bool ok = row < n;
+        const uint8_t *cp = codes + (size_t)(ok ? row : 0) * (size_t)(k >> 1);
+        const uint8_t *sp = scales + (size_t)(ok ? row : 0) * (size_t)(k >> 4);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = c_lo + tl + 16 * j;
+            t.c[r][j] = ok ? ld_stream16(cp + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
+            t.s[r][j] = ok ? ld_stream2(sp + 2 * (size_t)c) : 0u;
+        }
+    }
+}
+
+template <int MT, int R, int KS, int CPL, class Epi>
+__device__ __forceinline__ void gemv_tile_finish(float (&acc)[R][MT], int n, int row0, float *red, Epi &&epi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane >> 4, t = lane & 15;
     const int ks = (KS == 1) ? 0 : (wave % KS);
     const int rg = wave / KS;
-    const int C = k >> 5;
-    const int cs = (C + KS - 1) / KS;
-    const int c_lo = ks * cs;
-    const int c_hi = min(C, c_lo + cs);
     const int rbase = row0 + (rg * 4 + slot) * R;
-
-    float acc[R][M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int mm = 0; mm < M; ++mm) acc[r][mm] = 0.0f;
-
-    const size_t row_code_bytes = (size_t)(k >> 1), row_scale_bytes = (size_t)(k >> 4);
-
-    for (int c = c_lo + t; c < c_hi; c += 16) {
-        uint4 cw[R];
-        uint32_t sw[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = rbase + r;
-            if (row < n) {
-                cw[r] = *reinterpret_cast<const uint4 *>(codes + (size_t)row * row_code_bytes + 16 * (size_t)c);
-                sw[r] = *reinterpret_cast<const uint16_t *>(scales + (size_t)row * row_scale_bytes + 2 * (size_t)c);
-            } else {
-                cw[r] = make_uint4(0, 0, 0, 0);
-                sw[r] = 0;
-            }
-        }
-        uint4 xv[M][4];
-#pragma unroll
-        for (int mm = 0; mm < M; ++mm)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) xv[mm][q] = xs[(mm * 4 + q) * C + c];
-
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float sf0 = e4m3_to_f32(sw[r] & 0xFFu), sf1 = e4m3_to_f32(sw[r] >> 8);
-            const uint32_t cwd[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-            bf16x2 wv[16];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                wv[4 * d + 0] = e2m1x2_to_bf16<0>(cwd[d]);
-                wv[4 * d + 1] = e2m1x2_to_bf16<1>(cwd[d]);
-                wv[4 * d + 2] = e2m1x2_to_bf16<2>(cwd[d]);
-                wv[4 * d + 3] = e2m1x2_to_bf16<3>(cwd[d]);
-            }
-#pragma unroll
-            for (int mm = 0; mm < M; ++mm) {
-                const uint32_t x0[8] = {xv[mm][0].x, xv[mm][0].y, xv[mm][0].z, xv[mm][0].w,
-                                        xv[mm][1].x, xv[mm][1].y, xv[mm][1].z, xv[mm][1].w};
-                const uint32_t x1[8] = {xv[mm][2].x, xv[mm][2].y, xv[mm][2].z, xv[mm][2].w,
-                                        xv[mm][3].x, xv[mm][3].y, xv[mm][3].z, xv[mm][3].w};
-                float b0 = 0.0f, b1 = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) b0 = dot2(wv[i], as_bf16x2(x0[i]), b0);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) b1 = dot2(wv[8 + i], as_bf16x2(x1[i]), b1);
-                acc[r][mm] = __builtin_fmaf(b0, sf0, acc[r][mm]);
-                acc[r][mm] = __builtin_fmaf(b1, sf1, acc[r][mm]);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int mm = 0; mm < M; ++mm) acc[r][mm] = row16_sum(acc[r][mm]);
+        for (int mm = 0; mm < MT; ++mm) acc[r][mm] = row16_sum(acc[r][mm]);
 
     if constexpr (KS == 1) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = rbase + r;
 #pragma unroll
-            for (int mm = 0; mm < M; ++mm)
+            for (int mm = 0; mm < MT; ++mm)
                 if (t == mm && row < n) epi(row, mm, acc[r][mm]);
         }
     } else {
-        // red[((rg * 4 + slot) * R + r) * KS + ks][M]
+        // red[((rg * 4 + slot) * R + r) * KS + ks][MT]
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int mm = 0; mm < M; ++mm)
-                if (t == mm) red[((((rg * 4 + slot) * R + r) * KS + ks) * M) + mm] = acc[r][mm];
+            for (int mm = 0; mm < MT; ++mm)
+                if (t == mm) red[((((rg * 4 + slot) * R + r) * KS + ks) * MT) + mm] = acc[r][mm];
         __syncthreads();
         if (ks == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int row = rbase + r;
 #pragma unroll
-                for (int mm = 0; mm < M; ++mm) {
+                for (int mm = 0; mm < MT; ++mm) {
                     if (t == mm && row < n) {
-                        const float *p = red + (((rg * 4 + slot) * R + r) * KS) * M + mm;
+                        const float *p = red + (((rg * 4 + slot) * R + r) * KS) * MT + mm;
                         float v = p[0];
 #pragma unroll
-                        for (int s = 1; s < KS; ++s) v += p[s * M];
+                        for (int s = 1; s < KS; ++s) v += p[s * MT];
                         epi(row, mm, v);
                     }
                 }
@@ -161,31 +185,107 @@ __device__ __forceinline__ void gemv_tile(const uint4 *xs, const uint8_t *__rest
     }
 }
 
-// Host-side choice of the tile shape for an n-row weight: the largest R
-// (fewest, fattest tiles) that still gives at least two workgroups per CU,
-// else split K across the wavefronts.
-struct TileChoice {
-    int R, KS;
-};
-// allow_ksplit is false when the K-split reduction scratch would not fit
-// next to the activation image in LDS.
-inline TileChoice choose_tile(int n, int cus, bool allow_ksplit) {
-    static const TileChoice order[] = {{4, 1}, {2, 1}, {1, 1}, {1, 2}, {1, 4}};
-    for (const TileChoice &c : order) {
-        if (c.KS > 1 && !allow_ksplit) break;
-        int rows = 16 * c.R / c.KS;
-        if ((n + rows - 1) / rows >= 2 * cus) return c;
-    }
-    return allow_ksplit ? TileChoice{1, 4} : TileChoice{1, 1};
+// Full tile with fixed chunk count: loads already issued into `t`.
+template <int MT, int R, int KS, int CPL, class Epi>
+__device__ __forceinline__ void gemv_tile_compute(const TileRegs<MT, R, KS, CPL> &t, const uint4 *xs, int n, int k,
+                                                  int row0, float *red, Epi &&epi) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tl = lane & 15;
+    const int ks = (KS == 1) ? 0 : (wave % KS);
+    const int C = k >> 5;
+    const int c_lo = ks * 16 * CPL;
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int r = 0; r < R; ++r) chunk_fma<MT>(t.c[r][j], t.s[r][j], xs, C, c_lo + tl + 16 * j, acc[r]);
+    gemv_tile_finish<MT, R, KS, CPL>(acc, n, row0, red, epi);
 }
+
+// Generic shape (any K % 32 == 0): loop over the lane's chunks.
+template <int MT, int R, int KS, class Epi>
+__device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *__restrict__ codes,
+                                               const uint8_t *__restrict__ scales, int n, int k, int row0, float *red,
+                                               Epi &&epi) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane >> 4, tl = lane & 15;
+    const int ks = (KS == 1) ? 0 : (wave % KS);
+    const int rg = wave / KS;
+    const int C = k >> 5;
+    const int cs = (C + KS - 1) / KS;
+    const int c_lo = ks * cs;
+    const int c_hi = min(C, c_lo + cs);
+    const int rbase = row0 + (rg * 4 + slot) * R;
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
+    for (int c = c_lo + tl; c < c_hi; c += 16) {
+        uint4 cw[R];
+        uint32_t sw[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = rbase + r;
+            if (row < n) {
+                cw[r] = ld_stream16(codes + (size_t)row * (size_t)(k >> 1) + 16 * (size_t)c);
+                sw[r] = ld_stream2(scales + (size_t)row * (size_t)(k >> 4) + 2 * (size_t)c);
+            } else {
+                cw[r] = make_uint4(0, 0, 0, 0);
+                sw[r] = 0;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[r], sw[r], xs, C, c, acc[r]);
+    }
+    gemv_tile_finish<MT, R, KS, 0>(acc, n, row0, red, epi);
+}
+
+// ---------------------------------------------------------------- host ----
+struct TileChoice {
+    int R, KS, CPL;   // CPL 0: generic loop
+};
 
 constexpr int kLdsBytes = 64 * 1024;   // LDS budget of one workgroup
 
 // LDS bytes of a GEMV workgroup: the activation image plus, with a K split,
-// 16 * R * M fp32 partial sums.
-inline size_t gemv_lds_bytes(int m, int k, TileChoice tc) {
-    return (size_t)m * k * 2 + (tc.KS > 1 ? (size_t)16 * tc.R * m * 4 : 0);
+// 16 * R * MT fp32 partial sums.
+inline size_t gemv_lds_bytes(int mt, int k, TileChoice tc) {
+    return (size_t)mt * k * 2 + (tc.KS > 1 ? (size_t)16 * tc.R * mt * 4 : 0);
 }
-inline bool ksplit_fits(int m, int k) { return gemv_lds_bytes(m, k, TileChoice{1, 2}) <= (size_t)kLdsBytes; }
+
+// Tile shape for an n x k weight and MT activation rows: the largest R
+// (fewest, fattest tiles) that still gives at least `min_tiles` workgroups,
+// else a K split across the wavefronts (if its scratch fits in LDS next to
+// the activations, `extra_lds` bytes of static LDS included).  CPL is the
+// fixed per-lane chunk count when K splits evenly into 16-lane rows.
+inline TileChoice choose_tile(int n, int k, int mt, int min_tiles, size_t extra_lds) {
+    static const int order[][2] = {{4, 1}, {2, 1}, {1, 1}, {1, 2}, {1, 4}};
+    TileChoice pick{1, 1, 0};
+    bool found = false;
+    for (const auto &o : order) {
+        TileChoice c{o[0], o[1], 0};
+        if (c.KS > 1 && gemv_lds_bytes(mt, k, c) + extra_lds > (size_t)kLdsBytes) break;
+        pick = c;
+        const int rows = 16 * c.R / c.KS;
+        if ((n + rows - 1) / rows >= min_tiles) {
+            found = true;
+            break;
+        }
+    }
+    (void)found;
+    const int per = 512 * pick.KS;
+    if (k % per == 0) {
+        const int cpl = k / per;
+        if (cpl == 1 || cpl == 2 || cpl == 4) pick.CPL = cpl;
+    }
+    return pick;
+}
+
+__host__ __device__ inline int round_up_mt(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
 
 }  // namespace nvfp4
