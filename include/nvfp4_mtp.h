@@ -191,7 +191,7 @@ int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
  * Per selected expert: g = gate x, u = up x (fp32),
  * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
  * read once per call however many rows select it.  Requires H, I % 32 == 0
- * and H, I <= 3968.  Three launches (route, gate/up, down + combine).
+ * and H, I <= 3968.  Two launches (routing + gate/up, down + combine).
  */
 size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
 int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,

@@ -38,7 +38,13 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, in
         else
             reinterpret_cast<float *>(y)[(size_t)mm * n + row] = o;
     };
-    if constexpr (CPL > 0) {
+    if constexpr (MT == 1 && CPL > 0) {
+        TileRegs<MT, R, KS, CPL> t;
+        gemv_tile_load(t, codes, scales, n, k, row0);
+        XRegs<CPL> xr;
+        load_xregs<KS, CPL>(xr, x);
+        gemv_tile_compute_x1(t, xr, n, row0, red, epi);
+    } else if constexpr (CPL > 0) {
         TileRegs<MT, R, KS, CPL> t;
         gemv_tile_load(t, codes, scales, n, k, row0);   // weight loads in flight while x is staged
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
@@ -104,7 +110,18 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         if (row == 0) st_dev(&row0[mm], logit);
         if (beats(key, row, best.key, best.idx)) best = ArgPart{key, logit, row, 0};
     };
-    if constexpr (CPL > 0) {
+    if constexpr (MT == 1 && CPL > 0) {
+        // one activation row: it lives in registers; each tile's loads are
+        // issued at the top of its iteration and other resident wavefronts
+        // cover the latency
+        XRegs<CPL> xr;
+        load_xregs<KS, CPL>(xr, x);
+        for (int t = t_begin; t < t_end; ++t) {
+            TileRegs<MT, R, KS, CPL> cur;
+            gemv_tile_load(cur, codes, scales, v, k, t * rows);
+            gemv_tile_compute_x1(cur, xr, v, t * rows, red, epi);
+        }
+    } else if constexpr (CPL > 0) {
         TileRegs<MT, R, KS, CPL> cur;
         gemv_tile_load(cur, codes, scales, v, k, t_begin * rows);
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
@@ -152,13 +169,29 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     ArgPart b[MT];
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, 0};
-    for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
+    // U partials per thread per round: all their loads are issued before any
+    // is compared, so a round costs one memory latency, not U of them
+    constexpr int U = 16 / MT;
+    for (int p0 = threadIdx.x; p0 < nparts; p0 += blockDim.x * U) {
+        ArgPart c[U][MT];
 #pragma unroll
-        for (int mm = 0; mm < MT; ++mm) {
-            const ArgPart *src = parts + (size_t)p * MT + mm;
-            const ArgPart c{ld_dev(&src->key), ld_dev(&src->val), ld_dev(&src->idx), 0};
-            if (beats(c.key, c.idx, b[mm].key, b[mm].idx)) b[mm] = c;
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * (int)blockDim.x;
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm) {
+                if (p < nparts) {
+                    const ArgPart *src = parts + (size_t)p * MT + mm;
+                    c[u][mm] = ArgPart{ld_dev(&src->key), ld_dev(&src->val), ld_dev(&src->idx), 0};
+                } else {
+                    c[u][mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, 0};
+                }
+            }
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                if (beats(c[u][mm].key, c[u][mm].idx, b[mm].key, b[mm].idx)) b[mm] = c[u][mm];
     }
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm)
@@ -235,11 +268,13 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *w, void *
     return check_launch("w4a16_gemv");
 }
 
-// Grid of the persistent LM-head kernel: as many workgroups as fit on the
-// device at once, each with the same number of tiles (the last fewer).
+// Grid of the persistent LM-head kernel: each workgroup gets the same
+// number of tiles (the last fewer).
 template <class K>
 static int lm_grid(K kernel, size_t lds, int ntiles, int &tpw) {
-    const int cap = num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
+    // twice the resident capacity: a second wave of workgroups fills the
+    // slots of the first as they finish, which evens out the tail
+    const int cap = 2 * num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
     tpw = (ntiles + cap - 1) / cap;
     return (ntiles + tpw - 1) / tpw;
 }

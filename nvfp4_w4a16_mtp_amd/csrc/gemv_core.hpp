@@ -206,6 +206,71 @@ __device__ __forceinline__ void gemv_tile_compute(const TileRegs<MT, R, KS, CPL>
     gemv_tile_finish<MT, R, KS, CPL>(acc, n, row0, red, epi);
 }
 
+// Single activation row with a fixed chunk count: a lane always works on the
+// same CPL chunks of K, so its 32 * CPL activations live in registers for
+// the whole kernel (no LDS image, no LDS reads in the inner loop).
+template <int CPL>
+struct XRegs {
+    uint32_t w[CPL][16];
+};
+
+template <int KS, int CPL>
+__device__ __forceinline__ void load_xregs(XRegs<CPL> &xr, const uint16_t *__restrict__ x) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tl = lane & 15;
+    const int ks = (KS == 1) ? 0 : (wave % KS);
+    const int c_lo = ks * 16 * CPL;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x + 32 * (c_lo + tl + 16 * j));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 u = p[q];
+            xr.w[j][4 * q + 0] = u.x;
+            xr.w[j][4 * q + 1] = u.y;
+            xr.w[j][4 * q + 2] = u.z;
+            xr.w[j][4 * q + 3] = u.w;
+        }
+    }
+}
+
+// One chunk of one row against register-held activations.
+__device__ __forceinline__ float chunk_dot_xreg(const uint4 cw, uint32_t sw, const uint32_t (&xr)[16], float acc) {
+    float sf0, sf1;
+    e4m3x2_to_f32(sw, sf0, sf1);
+    const uint32_t cwd[4] = {cw.x, cw.y, cw.z, cw.w};
+    float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        b0 = dot2(e2m1x2_to_bf16<0>(cwd[d]), as_bf16x2(xr[4 * d + 0]), b0);
+        b0 = dot2(e2m1x2_to_bf16<1>(cwd[d]), as_bf16x2(xr[4 * d + 1]), b0);
+        b0 = dot2(e2m1x2_to_bf16<2>(cwd[d]), as_bf16x2(xr[4 * d + 2]), b0);
+        b0 = dot2(e2m1x2_to_bf16<3>(cwd[d]), as_bf16x2(xr[4 * d + 3]), b0);
+    }
+#pragma unroll
+    for (int d = 2; d < 4; ++d) {
+        b1 = dot2(e2m1x2_to_bf16<0>(cwd[d]), as_bf16x2(xr[4 * d + 0]), b1);
+        b1 = dot2(e2m1x2_to_bf16<1>(cwd[d]), as_bf16x2(xr[4 * d + 1]), b1);
+        b1 = dot2(e2m1x2_to_bf16<2>(cwd[d]), as_bf16x2(xr[4 * d + 2]), b1);
+        b1 = dot2(e2m1x2_to_bf16<3>(cwd[d]), as_bf16x2(xr[4 * d + 3]), b1);
+    }
+    acc = __builtin_fmaf(b0, sf0, acc);
+    return __builtin_fmaf(b1, sf1, acc);
+}
+
+template <int R, int KS, int CPL, class Epi>
+__device__ __forceinline__ void gemv_tile_compute_x1(const TileRegs<1, R, KS, CPL> &t, const XRegs<CPL> &xr, int n,
+                                                     int row0, float *red, Epi &&epi) {
+    float acc[R][1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][0] = chunk_dot_xreg(t.c[r][j], t.s[r][j], xr.w[j], acc[r][0]);
+    gemv_tile_finish<1, R, KS, CPL>(acc, n, row0, red, epi);
+}
+
 // Generic shape (any K % 32 == 0): loop over the lane's chunks.
 template <int MT, int R, int KS, class Epi>
 __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *__restrict__ codes,

@@ -3,22 +3,24 @@
 // (`MtpHead::new`) names for the head's MoE, with the NVFP4 expert
 // gate/up [inter][hidden] and down [hidden][inter] matrices it quantizes.
 //
-// Three launches, sized for the worst case and reading the routing from
-// device memory (no host round trip):
-//  1. route   (one workgroup, one wavefront per token): top-k by logit with
-//             the lower id first on ties (shuffle argmax over register-held
-//             logits), softmax over the selected logits, and for each
-//             distinct expert (ascending id) the tokens that chose it and
-//             their (token, slot) pair indices;
-//  2. gate_up (row tiles x distinct experts): the gate and up GEMVs over
+// Two launches, sized for the worst case, with the routing decided on the
+// device (no host round trip):
+//  1. gate_up (row tiles x distinct experts): every workgroup first computes
+//             the routing in LDS -- top-k by logit with the lower id first on
+//             ties (one wavefront per token, DPP argmax over register-held
+//             logits), softmax over the selected logits, the distinct experts
+//             in ascending id with their tokens and (token, slot) pairs --
+//             then runs the gate and up GEMVs over
 //             exactly the tokens that chose the expert -- its weights are
 //             streamed once however many tokens use it -- then
 //             a = bf16(silu(g) * u) for each (token, slot) pair;
-//  3. down    (row tiles x distinct experts): d = down(a) for the same
+//  2. down    (row tiles x distinct experts): d = down(a) for the same
 //             pairs; the last expert to finish a 16-row tile (a ticket per
 //             tile, returned to zero afterwards) writes y[t] = sum_j w[t][j] *
 //             d[t][j] in slot order for those rows -- deterministic, no
 //             floating-point atomics.
+#include <algorithm>
+
 #include "gemv_core.hpp"
 
 namespace nvfp4 {
@@ -44,64 +46,116 @@ struct MoeRoute {
 };
 static_assert(sizeof(MoeRoute) <= kMoeHeader, "route header");
 
-__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int m, int E, int topk,
-                                                  int32_t *__restrict__ ids, float *__restrict__ wts,
-                                                  MoeRoute *__restrict__ route) {
-    __shared__ int tokmask[kMoeMaxExperts];
-    __shared__ unsigned char jof[kMoeMaxExperts][8];   // slot at which token t chose expert e
-    __shared__ int wsum[4];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) tokmask[e] = 0;
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &i) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+    if (beats(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Argmax of (v, i) over the wavefront (larger v, then lower i); every lane
+// gets the result.  DPP within each 16-lane row, then the four row winners
+// are compared in a fixed order.
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+    argmax_dpp<0xB1>(v, i);    // xor 1
+    argmax_dpp<0x4E>(v, i);    // xor 2
+    argmax_dpp<0x141>(v, i);   // half mirror
+    argmax_dpp<0x140>(v, i);   // mirror
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (beats(rv, ri, bv, bi)) {
+            bv = rv;
+            bi = ri;
+        }
+    }
+    v = bv;
+    i = bi;
+}
+
+// Sum over the wavefront in a fixed order; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Routing of all m tokens, computed by one workgroup in LDS.
+struct RouteLds {
+    int tokmask[kMoeMaxExperts];                 // bit t: token t chose expert e
+    unsigned char jof[kMoeMaxExperts][8];        // slot at which token t chose e
+    int sel_i[8][kMoeMaxTopK];
+    float sel_w[8][kMoeMaxTopK];
+    int wsum[4];
+    int n_distinct;
+    MoeExpert ex[128];
+};
+
+// Top-k by logit (lower id first on ties), softmax over the selected logits,
+// then the distinct experts in ascending id with their tokens and pairs.
+// One wavefront per token; each lane holds up to 16 logits and its own best
+// untaken one, so a selection costs one wavefront argmax.
+__device__ void moe_route_lds(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) L.tokmask[e] = 0;
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int per = (E + 63) / 64;   // logits per lane, <= 16
     for (int t = wave; t < m; t += 4) {
         const float *lg = logits + (size_t)t * E;
         float v[16];
-        uint32_t taken = 0;
+        uint32_t avail = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int e = lane + 64 * j;
             const bool in = j < per && e < E;
-            v[j] = in ? lg[e] : 0.0f;
-            if (!in) taken |= 1u << j;
+            v[j] = in ? lg[e] : -INFINITY;
+            if (in) avail |= 1u << j;
         }
+        auto local_best = [&](float &lv, int &li) {
+            lv = -INFINITY;
+            li = INT_MAX;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if ((avail & (1u << j)) && beats(v[j], lane + 64 * j, lv, li)) {
+                    lv = v[j];
+                    li = lane + 64 * j;
+                }
+        };
+        float lv;
+        int li;
+        local_best(lv, li);
         float my_v = -INFINITY;   // lane s keeps the s-th selection
         int my_i = 0;
         for (int s = 0; s < topk; ++s) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int e = lane + 64 * j;
-                if (!(taken & (1u << j)) && (bi == INT_MAX || beats(v[j], e, bv, bi))) {
-                    bv = v[j];
-                    bi = e;
-                }
-            }
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                if (oi != INT_MAX && (bi == INT_MAX || beats(ov, oi, bv, bi))) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
+            float bv = lv;
+            int bi = li;
+            wave_argmax(bv, bi);
             if (lane == s) {
                 my_v = bv;
                 my_i = bi;
             }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+            if ((bi & 63) == lane) {
+                avail &= ~(1u << (bi >> 6));
+                local_best(lv, li);
+            }
         }
-        // softmax over the selected logits (selection 0 is the largest)
-        const float vmax = __shfl(my_v, 0, 64);
+        const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
         const float ex = lane < topk ? expf(my_v - vmax) : 0.0f;
-        float den = ex;
-        for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+        const float den = wave_sum(ex);
         if (lane < topk) {
-            ids[t * topk + lane] = my_i;
-            wts[t * topk + lane] = ex / den;
-            atomicOr(&tokmask[my_i], 1 << t);
-            jof[my_i][t] = (unsigned char)lane;
+            L.sel_i[t][lane] = my_i;
+            L.sel_w[t][lane] = ex / den;
+            atomicOr(&L.tokmask[my_i], 1 << t);
+            L.jof[my_i][t] = (unsigned char)lane;
         }
     }
     __syncthreads();
@@ -109,37 +163,33 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
     const int epp = (E + 255) / 256;     // experts per thread, <= 4
     const int e0 = threadIdx.x * epp;
     int c = 0;
-    for (int e = e0; e < min(E, e0 + epp); ++e) c += tokmask[e] != 0;
+    for (int e = e0; e < min(E, e0 + epp); ++e) c += L.tokmask[e] != 0;
     int incl = c;   // inclusive scan over the workgroup
     for (int off = 1; off < 64; off <<= 1) {
         const int o = __shfl_up(incl, off, 64);
         if (lane >= off) incl += o;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) L.wsum[wave] = incl;
     __syncthreads();
     int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
+    for (int w = 0; w < wave; ++w) base += L.wsum[w];
     int pos = base + incl - c;
     for (int e = e0; e < min(E, e0 + epp); ++e) {
-        const int mask = tokmask[e];
+        const int mask = L.tokmask[e];
         if (!mask) continue;
-        MoeExpert me;
+        MoeExpert &me = L.ex[pos++];
         me.expert = e;
-        me.cnt = 0;
-        for (int t = 0; t < 8; ++t) {
-            me.tok[t] = 0;
-            me.pair[t] = 0;
-        }
+        int cnt = 0;
         for (int t = 0; t < 8; ++t)
             if (mask & (1 << t)) {
-                me.tok[me.cnt] = t;
-                me.pair[me.cnt] = t * topk + jof[e][t];
-                ++me.cnt;
+                me.tok[cnt] = t;
+                me.pair[cnt] = t * topk + L.jof[e][t];
+                ++cnt;
             }
-        me.pad[0] = me.pad[1] = 0;
-        route->ex[pos++] = me;
+        me.cnt = cnt;
     }
-    if (threadIdx.x == 255) route->n_distinct = base + incl;
+    if (threadIdx.x == 255) L.n_distinct = base + incl;
+    __syncthreads();
 }
 
 // Stages rows rows[0..cnt) of a [*, k] bf16 matrix into the swizzled LDS
@@ -169,7 +219,10 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
         const float a = gl / (1.0f + expf(-gl)) * up;
         act[(size_t)prs[mm] * I + row] = (uint16_t)f32_to_bf16_bits(a);
     };
-    if constexpr (CPL > 0) {
+    // Preloading both tiles is kept to MT <= 2 (the common case: most experts
+    // serve one or two tokens), so that the 8-token branch does not set the
+    // register budget of the whole kernel.
+    if constexpr (CPL > 0 && MT <= 2) {
         TileRegs<MT, 1, 1, CPL> tg, tu;
         gemv_tile_load(tg, gc, gs, I, H, row0);
         gemv_tile_load(tu, uc, us, I, H, row0);
@@ -185,26 +238,53 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
     }
 }
 
+// Routing + gate/up: every workgroup computes the routing in LDS (cheap,
+// and it saves a launch), takes the distinct expert blockIdx.y, and
+// workgroup (0, 0) publishes ids, weights and the route for the down pass.
 template <int CPL>
-__global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, nvfp4_moe_weights e,
-                                                    const MoeRoute *__restrict__ route, uint16_t *__restrict__ act) {
-    const int u = blockIdx.y;
-    if (u >= route->n_distinct) return;
-    const MoeExpert *me = &route->ex[u];
-    const int ex = me->expert;
-    const int cnt = me->cnt;
-    const int H = e.hidden, I = e.inter;
+__global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+                                                    int m, int E, int topk, nvfp4_moe_weights e,
+                                                    int32_t *__restrict__ ids, float *__restrict__ wts,
+                                                    MoeRoute *__restrict__ route, uint16_t *__restrict__ act) {
     extern __shared__ uint4 smem[];
+    RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // reused for the activations afterwards
+    __shared__ int tok[8], prs[8];
+    __shared__ int s_ex, s_cnt, s_nd;
+    moe_route_lds(logits, m, E, topk, L);
+    const int u = blockIdx.y;
+    if (blockIdx.x == 0 && u == 0) {
+        for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
+            ids[p] = L.sel_i[p / topk][p % topk];
+            wts[p] = L.sel_w[p / topk][p % topk];
+        }
+        for (int q = threadIdx.x; q < L.n_distinct; q += blockDim.x) route->ex[q] = L.ex[q];
+        if (threadIdx.x == 0) route->n_distinct = L.n_distinct;
+    }
+    if (threadIdx.x == 0) {
+        s_nd = L.n_distinct;
+        if (u < L.n_distinct) {
+            s_ex = L.ex[u].expert;
+            s_cnt = L.ex[u].cnt;
+        }
+    }
+    if (threadIdx.x < 8 && u < L.n_distinct) {
+        tok[threadIdx.x] = L.ex[u].tok[threadIdx.x];
+        prs[threadIdx.x] = L.ex[u].pair[threadIdx.x];
+    }
+    __syncthreads();   // the routing scratch is free from here on
+    if (u >= s_nd) return;
+    const int ex = s_ex, cnt = s_cnt;
+    const int H = e.hidden, I = e.inter;
     const size_t wsz = (size_t)I * H;
     const uint8_t *gc = e.gate_codes + (size_t)ex * (wsz / 2), *gs = e.gate_scales + (size_t)ex * (wsz / 16);
     const uint8_t *uc = e.up_codes + (size_t)ex * (wsz / 2), *us = e.up_scales + (size_t)ex * (wsz / 16);
     const float gdec = e.gate_global[ex].dec, udec = e.up_global[ex].dec;
     const int row0 = blockIdx.x * kMoeRows;
     const int mt = round_up_mt(cnt);
-    if (mt == 1) gate_up_body<1, CPL>(smem, x, me->tok, me->pair, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else if (mt == 2) gate_up_body<2, CPL>(smem, x, me->tok, me->pair, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else if (mt == 4) gate_up_body<4, CPL>(smem, x, me->tok, me->pair, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else gate_up_body<8, CPL>(smem, x, me->tok, me->pair, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    if (mt == 1) gate_up_body<1, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    else if (mt == 2) gate_up_body<2, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    else if (mt == 4) gate_up_body<4, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    else gate_up_body<8, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
 }
 
 template <int MT, int CPL>
@@ -283,9 +363,10 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
 }
 
 template <int CPL>
-static void launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const nvfp4_moe_weights &e,
-                           const MoeRoute *route, uint16_t *act) {
-    hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, e, route, act);
+static void launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
+                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
+                           uint16_t *act) {
+    hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act);
 }
 template <int CPL>
 static void launch_down(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk, const float *wts,
@@ -343,19 +424,16 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
     uint16_t *act = reinterpret_cast<uint16_t *>(ws + L.act);
     float *dbuf = reinterpret_cast<float *>(ws + L.dbuf);
     const int maxd = min(E, m * top_k);
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), 0, s, router_logits, m, E, top_k, topk_ids, topk_w, route);
-    int rc = check_launch("moe_w4a16_gemv(route)");
-    if (rc) return rc;
     const nvfp4_moe_weights ev = *e;
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kMoeRows - 1) / kMoeRows, maxd);
-    const size_t lds1 = (size_t)8 * H * 2, lds2 = (size_t)8 * I * 2;
+    const size_t lds1 = std::max((size_t)8 * H * 2, sizeof(RouteLds)), lds2 = (size_t)8 * I * 2;
     switch (cpl_for(H)) {
-        case 1: launch_gate_up<1>(g1, lds1, s, x_bf16, ev, route, act); break;
-        case 2: launch_gate_up<2>(g1, lds1, s, x_bf16, ev, route, act); break;
-        case 4: launch_gate_up<4>(g1, lds1, s, x_bf16, ev, route, act); break;
-        default: launch_gate_up<0>(g1, lds1, s, x_bf16, ev, route, act); break;
+        case 1: launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 2: launch_gate_up<2>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 4: launch_gate_up<4>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        default: launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
     }
-    rc = check_launch("moe_w4a16_gemv(gate_up)");
+    int rc = check_launch("moe_w4a16_gemv(gate_up)");
     if (rc) return rc;
     switch (cpl_for(I)) {
         case 1: launch_down<1>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;

@@ -5,7 +5,8 @@
 // Pass 1 streams the bf16 tensor once (16-byte loads), keeps the largest
 // |w| as an integer (non-negative bf16 magnitudes order like unsigned
 // integers) and folds it into the global struct with one atomic max per
-// wavefront.  Pass 2 streams it again: one thread encodes 32 consecutive
+// workgroup (at most two workgroups per CU, each striding over the
+// tensor).  Pass 2 streams it again: one thread encodes 32 consecutive
 // elements of a row (two 16-element blocks) from four 16-byte loads into one
 // 16-byte code store and one 2-byte scale store.  Every fp32 operation is a
 // single correctly rounded IEEE operation (no contraction, division is the
@@ -37,9 +38,16 @@ __global__ __launch_bounds__(256) void k_quant_absmax(const uint4 *__restrict__ 
         mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
         mx = max(mx, max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16)));
     }
-    // wave max, then one atomic per wave on the fp32 bit pattern of amax
+    // wave max, workgroup max, then one atomic per workgroup on the fp32 bit
+    // pattern of amax (atomics on one word serialize: keep them few)
+    __shared__ uint32_t wmax[4];
     for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    if ((threadIdx.x & 63) == 0 && mx) atomicMax(reinterpret_cast<unsigned int *>(&g->amax), mx << 16);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t m4 = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        if (m4) atomicMax(reinterpret_cast<unsigned int *>(&g->amax), m4 << 16);
+    }
 }
 
 // Nearest E4M3FN byte to s >= 0: ties to even mantissa, subnormals kept,
@@ -158,7 +166,7 @@ extern "C" int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint
     int rc = check_launch("nvfp4_quantize(clear)");
     if (rc) return rc;
     const int64_t nvec = count / 8;
-    hipLaunchKernelGGL(k_quant_absmax, dim3(grid_for(nvec, 16)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_quant_absmax, dim3(grid_for(nvec, 2)), dim3(256), 0, s,
                        reinterpret_cast<const uint4 *>(w_bf16), nvec, global);
     rc = check_launch("nvfp4_quantize(absmax)");
     if (rc) return rc;
