@@ -78,14 +78,15 @@ constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
 constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
 constexpr int kLmParts = 256;     // ArgPart[ntiles][MT]
 
-// Persistent LM-head pass: workgroup g scores tiles [g * tpw, (g + 1) * tpw)
-// of the global tiling (16 * R rows per tile).  With a fixed chunk count the
-// next tile's loads are issued before the current tile is computed, so the
-// workgroup streams without gaps; the activations are staged once.
+// Persistent LM-head pass over the global tiling (16 * R rows per tile):
+// the grid is the resident capacity and workgroup g scores tiles g, g + G,
+// g + 2G, ... so that at any moment the whole chip sweeps one contiguous band
+// of the matrix and every workgroup ends within one tile of the others.  The
+// activations are loaded once per workgroup.
 template <int MT, int R, int KS, int CPL, bool BF16KEY>
 __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                               int v, int k, int tpw, char *__restrict__ ws, int32_t *__restrict__ out_idx,
+                                               int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
                                                float *__restrict__ out_max) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
@@ -99,8 +100,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
 
     constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
     const int ntiles = (v + rows - 1) / rows;
-    const int t_begin = blockIdx.x * tpw;
-    const int t_end = min(ntiles, t_begin + tpw);
+    const int t_begin = blockIdx.x, t_step = gridDim.x;
     const float dec = g->dec;
     // lane m of every slot keeps the best of its rows for activation row m
     ArgPart best{-INFINITY, -INFINITY, INT_MAX, 0};
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         // cover the latency
         XRegs<CPL> xr;
         load_xregs<KS, CPL>(xr, x);
-        for (int t = t_begin; t < t_end; ++t) {
+        for (int t = t_begin; t < ntiles; t += t_step) {
             TileRegs<MT, R, KS, CPL> cur;
             gemv_tile_load(cur, codes, scales, v, k, t * rows);
             gemv_tile_compute_x1(cur, xr, v, t * rows, red, epi);
@@ -126,10 +126,10 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         gemv_tile_load(cur, codes, scales, v, k, t_begin * rows);
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        for (int t = t_begin; t < t_end; ++t) {
+        for (int t = t_begin; t < ntiles; t += t_step) {
             TileRegs<MT, R, KS, CPL> nxt;
-            if (t + 1 < t_end)
-                gemv_tile_load(nxt, codes, scales, v, k, (t + 1) * rows);
+            if (t + t_step < ntiles)
+                gemv_tile_load(nxt, codes, scales, v, k, (t + t_step) * rows);
             else
                 nxt = cur;
             gemv_tile_compute(cur, xs, v, k, t * rows, red, epi);
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     } else {
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        for (int t = t_begin; t < t_end; ++t) gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
+        for (int t = t_begin; t < ntiles; t += t_step) gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
     }
 
     // workgroup combine: 16 slots x MT candidates -> MT partials
@@ -268,15 +268,13 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *w, void *
     return check_launch("w4a16_gemv");
 }
 
-// Grid of the persistent LM-head kernel: each workgroup gets the same
-// number of tiles (the last fewer).
+// Grid of the persistent LM-head kernel: as many workgroups as are resident
+// at once (a second round of workgroups would leave the chip half idle in
+// its tail), never more than there are tiles.
 template <class K>
-static int lm_grid(K kernel, size_t lds, int ntiles, int &tpw) {
-    // twice the resident capacity: a second wave of workgroups fills the
-    // slots of the first as they finish, which evens out the tail
-    const int cap = 2 * num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
-    tpw = (ntiles + cap - 1) / cap;
-    return (ntiles + tpw - 1) / tpw;
+static int lm_grid(K kernel, size_t lds, int ntiles) {
+    const int cap = num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
+    return ntiles < cap ? ntiles : cap;
 }
 
 template <int MT, int R, int KS, int CPL>
@@ -284,17 +282,14 @@ static void launch_lm_cfg(size_t lds, hipStream_t s, const uint16_t *h, int m, c
                           int32_t *oi, float *om, bool bk) {
     if constexpr (KS == 1) {
         const int ntiles = (v + 16 * R - 1) / (16 * R);
-        int tpw = 1;
         if (bk) {
             auto kern = k_lmhead<MT, R, KS, CPL, true>;
-            const int grid = lm_grid(kern, lds, ntiles, tpw);
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, tpw,
-                               ws, oi, om);
+            hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales,
+                               w->global, v, w->k, ws, oi, om);
         } else {
             auto kern = k_lmhead<MT, R, KS, CPL, false>;
-            const int grid = lm_grid(kern, lds, ntiles, tpw);
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, tpw,
-                               ws, oi, om);
+            hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales,
+                               w->global, v, w->k, ws, oi, om);
         }
     }
 }
