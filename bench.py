@@ -125,8 +125,11 @@ def main():
     out_max = torch.empty(M, dtype=torch.float32, device=dev)
 
     def step(ws):
-        for name, n, k in PROJ:
-            nv.w4a16_gemv(xs[name], ws[name], out=ys[name])
+        # fc, then q|k|v in one grouped launch (they share the normed hidden
+        # state), then o
+        nv.w4a16_gemv(xs["fc"], ws["fc"], out=ys["fc"])
+        nv.w4a16_gemv_grouped(xs["q"], [ws["q"], ws["k"], ws["v"]], outs=[ys["q"], ys["k"], ys["v"]])
+        nv.w4a16_gemv(xs["o"], ws["o"], out=ys["o"])
         nv.moe_w4a16_gemv(xm, router, TOPK, ws["moe"], workspace=moe_ws, out=ymoe, topk_ids=ids, topk_w=wts)
         nv.lmhead_gemv_argmax(hl, ws["lm"], vocab_rows=VOCAB, workspace=lm_ws, out_idx=out_idx, out_max=out_max)
 
@@ -135,7 +138,8 @@ def main():
     torch.cuda.synchronize()
     n_distinct = len(set(ids.cpu().numpy().ravel().tolist()))
     moe_bytes = n_distinct * 3 * nvfp4_bytes(I, H) + M * H * 2 + M * E * 4 + M * H * 4 + 2 * M * TOPK * 4
-    gemv_bytes = sum(nvfp4_bytes(n, k) + M * k * 2 + M * n * 4 for name, n, k in PROJ)
+    # q, k and v read one activation block (grouped launch)
+    gemv_bytes = sum(nvfp4_bytes(n, k) + M * n * 4 for name, n, k in PROJ) + M * 2 * (4096 + 2048 + 4096)
     lm_bytes = nvfp4_bytes(VOCAB, H) + M * H * 2 + M * 8
     step_bytes = gemv_bytes + moe_bytes + lm_bytes
 
@@ -253,23 +257,58 @@ def _time(torch, fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
+def _time_graph(torch, fn, reps, stream):
+    """Per-launch device time of fn: `reps` launches (rotating weight copies)
+    captured in one HIP graph, replayed 3 times between two events.  Host
+    launch overhead is excluded; the kernel boundaries inside the graph are
+    included, as in a captured draft step."""
+    with torch.cuda.stream(stream):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (3 * reps)
+
+
 def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
-    """Per-row timings (eager, rotating copies), each with its roofline fraction."""
+    """Per-row device timings (graph-captured launches over rotating weight
+    copies), each with its roofline fraction."""
     out = {}
     reps = 30
     for name, n, k in PROJ:
-        ms = _time(torch, lambda i: nv.w4a16_gemv(xs[name], copies[i % NCOPIES][name], out=ys[name]), reps, s)
+        ms = _time_graph(torch, lambda i: nv.w4a16_gemv(xs[name], copies[i % NCOPIES][name], out=ys[name]), reps, s)
         b = nvfp4_bytes(n, k) + M * k * 2 + M * n * 4
         out[f"gemv_{name}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    ms = _time_graph(torch, lambda i: nv.w4a16_gemv_grouped(xs["q"], [copies[i % NCOPIES][nm] for nm in "qkv"],
+                                                            outs=[ys[nm] for nm in "qkv"]), reps, s)
+    b = sum(nvfp4_bytes(n, k) + M * n * 4 for name, n, k in PROJ if name in "qkv") + M * 2048 * 2
+    out["gemv_qkv_grouped"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
     # LM head at both vocabulary sizes of the workload
     for v in (32768, VOCAB):
         ws = nv.lmhead_workspace(M, v, hl.device)
-        ms = _time(torch, lambda i: nv.lmhead_gemv_argmax(hl, copies[i % NCOPIES]["lm"], vocab_rows=v, workspace=ws), reps, s)
+        oi = torch.empty(M, dtype=torch.int32, device=hl.device)
+        om = torch.empty(M, dtype=torch.float32, device=hl.device)
+        ms = _time_graph(torch, lambda i: nv.lmhead_gemv_argmax(hl, copies[i % NCOPIES]["lm"], vocab_rows=v, workspace=ws,
+                                                                out_idx=oi, out_max=om), reps, s)
         b = nvfp4_bytes(v, H) + M * H * 2 + M * 8
         out[f"lmhead_v{v}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                                "drafts_per_s": round(M / (ms * 1e-3), 1)}
     ws = nv.moe_workspace(M, TOPK, copies[0]["moe"], hl.device)
-    ms = _time(torch, lambda i: nv.moe_w4a16_gemv(xm, router, TOPK, copies[i % NCOPIES]["moe"], workspace=ws), reps, s)
+    ymo = torch.empty((M, H), dtype=torch.float32, device=hl.device)
+    ids = torch.empty((M, TOPK), dtype=torch.int32, device=hl.device)
+    wts = torch.empty((M, TOPK), dtype=torch.float32, device=hl.device)
+    ms = _time_graph(torch, lambda i: nv.moe_w4a16_gemv(xm, router, TOPK, copies[i % NCOPIES]["moe"], workspace=ws, out=ymo,
+                                                        topk_ids=ids, topk_w=wts), reps, s)
     out["moe"] = {"ms": round(ms, 5)}
     # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120) at M = 1024
     gen = torch.Generator(device=hl.device)

@@ -133,6 +133,27 @@ int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y
                int32_t y_dtype, void *stream);
 
 /*
+ * w4a16_gemv_grouped -- the same GEMV for `count` weights that share K and
+ * the activations, in one launch: y[i][m][w[i]->n] = x * W^_i transposed,
+ * for i < count.  The head's q, k and v projections read one normed hidden
+ * state, as do an FFN's gate and up ([new.rs] `MtpHead::new` resolves the
+ * `w4a16_gemv_qg` and dual `w4a16_gemv_fused` kernels next to the plain
+ * GEMV; [prefill_weights.rs] installs a fused [q|k|v] weight for prefill).
+ *   w       host array of `count` descriptors (1 <= count <= 8), all with the
+ *           same k; a descriptor with n == 0 contributes nothing and its
+ *           output pointer is not read.
+ *   y       host array of `count` device pointers, each [m][w[i]->n] of
+ *           y_dtype, 4-byte aligned.
+ * Each output is the fp32-accumulated product of w4a16_gemv; the order of
+ * the fp32 partial sums can differ from a call for that weight alone (the
+ * tile shape is chosen for the summed row count).  Outputs must not
+ * overlap.  Errors as w4a16_gemv, plus NVFP4_ERR_ARG for a bad
+ * count or NULL arrays and NVFP4_ERR_SHAPE for mismatched k.
+ */
+int w4a16_gemv_grouped(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *const *w,
+                       void *const *y, int32_t count, int32_t y_dtype, void *stream);
+
+/*
  * w4a16_gemm_m128 -- W4A16 GEMM for prompt-sized row counts, the
  * `w4a16_gemm_m128_dispatch` of [prefill.rs] in its lossless form (NVFP4 ->
  * bf16 dequantization, bf16 matrix products, fp32 accumulation; activations

@@ -58,6 +58,7 @@ def lib():
         EP = ctypes.POINTER(_MoeWeights)
         L.nvfp4_quantize.argtypes = [P, i32, i32, P, P, P, P]
         L.w4a16_gemv.argtypes = [P, i32, WP, P, i32, P]
+        L.w4a16_gemv_grouped.argtypes = [P, i32, ctypes.POINTER(WP), ctypes.POINTER(P), i32, i32, P]
         L.w4a16_gemm_m128.argtypes = [P, i32, WP, P, i32, P]
         L.lmhead_gemv_argmax_workspace_bytes.argtypes = [i32, i32]
         L.lmhead_gemv_argmax_workspace_bytes.restype = sz
@@ -66,7 +67,8 @@ def lib():
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
-        for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemm_m128", "lmhead_gemv_argmax", "moe_w4a16_gemv"):
+        for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
+                  "moe_w4a16_gemv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +188,30 @@ def w4a16_gemv(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: to
     d = w.desc()
     _check(lib().w4a16_gemv(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype), _stream(x)), "w4a16_gemv")
     return out
+
+
+def w4a16_gemv_grouped(x: torch.Tensor, ws, out_dtype=torch.float32, outs=None):
+    """One launch of the GEMV over several weights with the same K (q|k|v,
+    gate|up); returns one output per weight."""
+    x = _as_bf16(x)
+    _dev(x, "x")
+    m = x.shape[0]
+    ws = list(ws)
+    if outs is None:
+        outs = [torch.empty((m, w.n), dtype=out_dtype, device=x.device) for w in ws]
+    outs = list(outs)
+    if len(outs) != len(ws):
+        raise ValueError("w4a16_gemv_grouped: one output per weight")
+    code = _out_code(outs[0].dtype) if outs else 0
+    for o in outs:
+        if _out_code(o.dtype) != code:
+            raise ValueError("w4a16_gemv_grouped: all outputs need one dtype")
+    descs = [w.desc() for w in ws]
+    WP = ctypes.POINTER(_Weight)
+    warr = (WP * len(ws))(*[ctypes.pointer(d) for d in descs])
+    yarr = (ctypes.c_void_p * len(ws))(*[_ptr(o) for o in outs])
+    _check(lib().w4a16_gemv_grouped(_ptr(x), m, warr, yarr, len(ws), code, _stream(x)), "w4a16_gemv_grouped")
+    return outs
 
 
 def w4a16_gemm_m128(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: torch.Tensor | None = None):

@@ -20,15 +20,48 @@
 
 namespace nvfp4 {
 
+// Up to kMaxGroups weights that share K and the activations, scored in one
+// launch: the grid is the concatenation of every group's row tiles (tile0
+// holds the prefix sums) and each workgroup picks its group by comparing its
+// tile index with tile0.  One group is the plain GEMV.
+constexpr int kMaxGroups = 8;
+struct GemvGroups {
+    const uint8_t *codes[kMaxGroups];
+    const uint8_t *scales[kMaxGroups];
+    const nvfp4_global *g[kMaxGroups];
+    void *y[kMaxGroups];
+    int n[kMaxGroups];
+    int tile0[kMaxGroups + 1];
+    int count;
+};
+
 template <int MT, int R, int KS, int CPL>
-__global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
-                                             const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                             int n, int k, void *__restrict__ y, int bf16out) {
+__global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
+                                             int bf16out) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
     constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
-    const int row0 = blockIdx.x * rows;
+    // group of this workgroup: selects with constant indices keep the table
+    // in scalar registers (a dynamic index would copy it to private memory)
+    const int tile = blockIdx.x;
+    const uint8_t *codes = grp.codes[0];
+    const uint8_t *scales = grp.scales[0];
+    const nvfp4_global *g = grp.g[0];
+    void *y = grp.y[0];
+    int n = grp.n[0], t0 = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i) {
+        if (i < grp.count && tile >= grp.tile0[i]) {
+            codes = grp.codes[i];
+            scales = grp.scales[i];
+            g = grp.g[i];
+            y = grp.y[i];
+            n = grp.n[i];
+            t0 = grp.tile0[i];
+        }
+    }
+    const int row0 = (tile - t0) * rows;
     const float dec = g->dec;
     auto epi = [&](int row, int mm, float v) {
         if (mm >= m_rt) return;
@@ -253,18 +286,36 @@ static TileChoice canonical(TileChoice tc) {
 }
 
 template <int MT, int R, int KS, int CPL>
-static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w,
-                            void *y, int bf16) {
-    hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, w->codes, w->scales, w->global, w->n,
-                       w->k, y, bf16);
+static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const GemvGroups &grp,
+                            int k, int bf16) {
+    hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, grp, k, bf16);
 }
 
+// One launch over `count` weights with a common K (their tiles concatenated);
+// the tile shape is chosen for the total row count.
 template <int MT>
-static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16, hipStream_t s) {
-    const TileChoice tc = canonical(choose_tile(w->n, w->k, MT, 2 * num_cus(), 0));
+static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
+                         hipStream_t s) {
+    const int k = w[0]->k;
+    int total_n = 0;
+    for (int i = 0; i < count; ++i) total_n += w[i]->n;
+    const TileChoice tc = canonical(choose_tile(total_n, k, MT, 2 * num_cus(), 0));
     const int rows = 16 * tc.R / tc.KS;
-    const dim3 grid((w->n + rows - 1) / rows);
-    NVFP4_TILE_SWITCH(launch_gemv_cfg, MT, tc, grid, gemv_lds_bytes(MT, w->k, tc), s, x, m, w, y, bf16);
+    GemvGroups grp{};
+    grp.count = count;
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        grp.codes[i] = w[i]->codes;
+        grp.scales[i] = w[i]->scales;
+        grp.g[i] = w[i]->global;
+        grp.y[i] = y[i];
+        grp.n[i] = w[i]->n;
+        grp.tile0[i] = tiles;
+        tiles += (w[i]->n + rows - 1) / rows;
+    }
+    for (int i = count; i <= kMaxGroups; ++i) grp.tile0[i] = tiles;
+    if (tiles == 0) return ok();
+    NVFP4_TILE_SWITCH(launch_gemv_cfg, MT, tc, dim3(tiles), gemv_lds_bytes(MT, k, tc), s, x, m, grp, k, bf16);
     return check_launch("w4a16_gemv");
 }
 
@@ -310,28 +361,49 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
 
 using namespace nvfp4;
 
-extern "C" int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,
-                          void *stream) {
-    int rc = validate_weight(w, "w4a16_gemv");
-    if (rc) return rc;
-    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "w4a16_gemv: m=%d outside 1..8", m);
-    if (w->n == 0) return ok();   // empty output: nothing to read or write
-    if (!x_bf16 || !y) return fail(NVFP4_ERR_ARG, "w4a16_gemv: NULL x or y");
+static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *const *w, void *const *y, int count,
+                       int32_t y_dtype, void *stream, const char *who) {
+    if (count < 1 || count > kMaxGroups) return fail(NVFP4_ERR_ARG, "%s: count=%d outside 1..%d", who, count, kMaxGroups);
+    if (!w) return fail(NVFP4_ERR_ARG, "%s: NULL weight list", who);
+    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "%s: m=%d outside 1..8", who, m);
     if (y_dtype != NVFP4_OUT_F32 && y_dtype != NVFP4_OUT_BF16)
-        return fail(NVFP4_ERR_ARG, "w4a16_gemv: unknown y_dtype %d", y_dtype);
-    if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemv: x not 16-byte aligned");
-    if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemv: y not 4-byte aligned");
+        return fail(NVFP4_ERR_ARG, "%s: unknown y_dtype %d", who, y_dtype);
+    int total_n = 0;
+    for (int i = 0; i < count; ++i) {
+        int rc = validate_weight(w[i], who);
+        if (rc) return rc;
+        if (w[i]->k != w[0]->k)
+            return fail(NVFP4_ERR_SHAPE, "%s: weight %d has k=%d, weight 0 has k=%d", who, i, w[i]->k, w[0]->k);
+        if (w[i]->n > 0 && (!y || !y[i])) return fail(NVFP4_ERR_ARG, "%s: NULL output %d", who, i);
+        if (w[i]->n > 0 && !aligned(y[i], 4)) return fail(NVFP4_ERR_ALIGN, "%s: output %d not 4-byte aligned", who, i);
+        total_n += w[i]->n;
+    }
+    if (total_n == 0) return ok();   // empty outputs: nothing to read or write
+    if (!x_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL x", who);
+    if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "%s: x not 16-byte aligned", who);
     const int mt = round_up_mt(m);
-    if ((size_t)mt * w->k * 2 > (size_t)kLdsBytes)
-        return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemv: %d (rounded-up) rows x k=%d activations exceed LDS", mt, w->k);
+    if ((size_t)mt * w[0]->k * 2 > (size_t)kLdsBytes)
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w[0]->k);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int bf16 = y_dtype == NVFP4_OUT_BF16;
     switch (mt) {
-        case 1: return launch_gemv_m<1>(x_bf16, m, w, y, bf16, s);
-        case 2: return launch_gemv_m<2>(x_bf16, m, w, y, bf16, s);
-        case 4: return launch_gemv_m<4>(x_bf16, m, w, y, bf16, s);
-        default: return launch_gemv_m<8>(x_bf16, m, w, y, bf16, s);
+        case 1: return launch_gemv_m<1>(x_bf16, m, w, y, count, bf16, s);
+        case 2: return launch_gemv_m<2>(x_bf16, m, w, y, count, bf16, s);
+        case 4: return launch_gemv_m<4>(x_bf16, m, w, y, count, bf16, s);
+        default: return launch_gemv_m<8>(x_bf16, m, w, y, count, bf16, s);
     }
+}
+
+extern "C" int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,
+                          void *stream) {
+    const nvfp4_weight *ws[1] = {w};
+    void *ys[1] = {y};
+    return gemv_common(x_bf16, m, ws, ys, 1, y_dtype, stream, "w4a16_gemv");
+}
+
+extern "C" int w4a16_gemv_grouped(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *const *w, void *const *y,
+                                  int32_t count, int32_t y_dtype, void *stream) {
+    return gemv_common(x_bf16, m, w, y, count, y_dtype, stream, "w4a16_gemv_grouped");
 }
 
 extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows) {
