@@ -122,19 +122,24 @@ __device__ __forceinline__ void gemv_tile_load(TileRegs<MT, R, KS, CPL> &t, cons
     const int rg = wave / KS;
     const int rbase = row0 + (rg * 4 + slot) * R;
     const int c_lo = ks * 16 * CPL;
+    // rows past n load row n - 1 instead (no branch around the loads); their
+    // sums are never passed to the epilogue
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = rbase + r;
-        const bool ok = row < n;
-        const uint8_t *cp = codes + (size_t)(ok ? row : 0) * (size_t)(k >> 1);
-        const uint8_t *sp = scales + (size_t)(ok ? row : 0) * (size_t)(k >> 4);
+        const int row = min(rbase + r, n - 1);
+        const uint8_t *cp = codes + (size_t)row * (size_t)(k >> 1);
+        const uint8_t *sp = scales + (size_t)row * (size_t)(k >> 4);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = c_lo + tl + 16 * j;
-            t.c[r][j] = ok ? ld_stream16(cp + 16 * (size_t)c) : make_uint4(0, 0, 0, 0);
-            t.s[r][j] = ok ? ld_stream2(sp + 2 * (size_t)c) : 0u;
+            t.c[r][j] = ld_stream16(cp + 16 * (size_t)c);
+            t.s[r][j] = ld_stream2(sp + 2 * (size_t)c);
         }
     }
+    // keep every load of the tile ahead of the arithmetic that follows (the
+    // scheduler would otherwise sink some of them next to their first use
+    // and serialise their latency)
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int MT, int R, int KS, int CPL, class Epi>
@@ -295,14 +300,9 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
         uint32_t sw[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = rbase + r;
-            if (row < n) {
-                cw[r] = ld_stream16(codes + (size_t)row * (size_t)(k >> 1) + 16 * (size_t)c);
-                sw[r] = ld_stream2(scales + (size_t)row * (size_t)(k >> 4) + 2 * (size_t)c);
-            } else {
-                cw[r] = make_uint4(0, 0, 0, 0);
-                sw[r] = 0;
-            }
+            const int row = min(rbase + r, n - 1);   // rows past n: never passed to the epilogue
+            cw[r] = ld_stream16(codes + (size_t)row * (size_t)(k >> 1) + 16 * (size_t)c);
+            sw[r] = ld_stream2(scales + (size_t)row * (size_t)(k >> 4) + 2 * (size_t)c);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[r], sw[r], xs, C, c, acc[r]);

@@ -27,7 +27,7 @@ namespace nvfp4 {
 
 constexpr int kMoeMaxTopK = 16;
 constexpr int kMoeMaxExperts = 1024;
-constexpr int kMoeHeader = 12288;   // route header bytes at the start of the workspace
+constexpr int kMoeHeader = 16384;   // route header bytes at the start of the workspace
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
 
 // One distinct expert of a call: the tokens that chose it (ascending) and,
@@ -41,43 +41,20 @@ struct MoeExpert {
 };
 struct MoeRoute {
     int n_distinct;
-    int pad[3];
+    int n_pairs;
+    int pad[2];
     MoeExpert ex[128];   // ascending expert id
+    // flat plan for the down pass, read in one round: per distinct expert its
+    // first pair position and down-projection scale, per pair position (in
+    // (expert, token) order) the token, the pair index and its weight
+    int ex_id[128];
+    int pb[129];
+    float ddec[128];
+    int pos_tok[128];
+    int pos_pair[128];
+    float pos_w[128];
 };
 static_assert(sizeof(MoeRoute) <= kMoeHeader, "route header");
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float &v, int &i) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
-    if (beats(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
-}
-
-// Argmax of (v, i) over the wavefront (larger v, then lower i); every lane
-// gets the result.  DPP within each 16-lane row, then the four row winners
-// are compared in a fixed order.
-__device__ __forceinline__ void wave_argmax(float &v, int &i) {
-    argmax_dpp<0xB1>(v, i);    // xor 1
-    argmax_dpp<0x4E>(v, i);    // xor 2
-    argmax_dpp<0x141>(v, i);   // half mirror
-    argmax_dpp<0x140>(v, i);   // mirror
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (beats(rv, ri, bv, bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
-}
 
 // Sum over the wavefront in a fixed order; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -102,52 +79,85 @@ struct RouteLds {
 
 // Top-k by logit (lower id first on ties), softmax over the selected logits,
 // then the distinct experts in ascending id with their tokens and pairs.
-// One wavefront per token; each lane holds up to 16 logits and its own best
-// untaken one, so a selection costs one wavefront argmax.
-__device__ void moe_route_lds(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
+// One wavefront per token.  Lane l holds the logits of experts
+// [l * PER, (l + 1) * PER), sorted once (larger logit first, lower id first
+// on ties), so its head is its best untaken expert.  A selection is a DPP max
+// of the heads, a ballot of the lanes whose head equals it and the lowest
+// such lane -- its experts all have lower ids than those of higher lanes, so
+// it holds the lowest-id maximum -- which then pops its head.  The dependent
+// chain of a selection is a few dozen instructions.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Top-k of one token's logits; lane s < topk receives the s-th selection.
+template <int PER>
+__device__ __forceinline__ void route_token(const float *__restrict__ lg, int E, int topk, int lane, float &my_v,
+                                            int &my_i) {
+    float v[PER];
+    int id[PER];
+    int rem = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int e = lane * PER + j;
+        const bool in = e < E;
+        v[j] = in ? lg[e] : -INFINITY;
+        id[j] = in ? e : INT_MAX;
+        rem += in;
+    }
+    // odd-even transposition sort: larger logit first, lower id on ties
+    // (entries past E carry id INT_MAX and sort last)
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+#pragma unroll
+        for (int j = r & 1; j + 1 < PER; j += 2) {
+            const bool sw = v[j + 1] > v[j] || (v[j + 1] == v[j] && id[j + 1] < id[j]);
+            const float tv = v[j];
+            const int ti = id[j];
+            v[j] = sw ? v[j + 1] : v[j];
+            id[j] = sw ? id[j + 1] : id[j];
+            v[j + 1] = sw ? tv : v[j + 1];
+            id[j + 1] = sw ? ti : id[j + 1];
+        }
+    my_v = -INFINITY;
+    my_i = 0;
+    for (int s = 0; s < topk; ++s) {
+        const float mx = wave_max(rem > 0 ? v[0] : -INFINITY);
+        uint64_t ball = __ballot(rem > 0 && v[0] == mx);
+        if (!ball) ball = __ballot(rem > 0);   // only with NaN logits: any untaken expert, never out of range
+        const int wl = (int)__builtin_ctzll(ball);
+        const int wid = __builtin_amdgcn_readlane(id[0], wl);
+        if (lane == s) {
+            my_v = mx;
+            my_i = wid;
+        }
+        const bool pop = lane == wl;
+#pragma unroll
+        for (int j = 0; j + 1 < PER; ++j) {
+            v[j] = pop ? v[j + 1] : v[j];
+            id[j] = pop ? id[j + 1] : id[j];
+        }
+        rem -= pop;
+    }
+}
+
+template <int PER>
+__device__ __forceinline__ void moe_route_per(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) L.tokmask[e] = 0;
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int per = (E + 63) / 64;   // logits per lane, <= 16
     for (int t = wave; t < m; t += 4) {
-        const float *lg = logits + (size_t)t * E;
-        float v[16];
-        uint32_t avail = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = lane + 64 * j;
-            const bool in = j < per && e < E;
-            v[j] = in ? lg[e] : -INFINITY;
-            if (in) avail |= 1u << j;
-        }
-        auto local_best = [&](float &lv, int &li) {
-            lv = -INFINITY;
-            li = INT_MAX;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if ((avail & (1u << j)) && beats(v[j], lane + 64 * j, lv, li)) {
-                    lv = v[j];
-                    li = lane + 64 * j;
-                }
-        };
-        float lv;
-        int li;
-        local_best(lv, li);
-        float my_v = -INFINITY;   // lane s keeps the s-th selection
-        int my_i = 0;
-        for (int s = 0; s < topk; ++s) {
-            float bv = lv;
-            int bi = li;
-            wave_argmax(bv, bi);
-            if (lane == s) {
-                my_v = bv;
-                my_i = bi;
-            }
-            if ((bi & 63) == lane) {
-                avail &= ~(1u << (bi >> 6));
-                local_best(lv, li);
-            }
-        }
+        float my_v;
+        int my_i;
+        route_token<PER>(logits + (size_t)t * E, E, topk, lane, my_v, my_i);
         const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
         const float ex = lane < topk ? expf(my_v - vmax) : 0.0f;
         const float den = wave_sum(ex);
@@ -159,37 +169,47 @@ __device__ void moe_route_lds(const float *__restrict__ logits, int m, int E, in
         }
     }
     __syncthreads();
-    // compact the experts with a nonzero token mask, ascending id
-    const int epp = (E + 255) / 256;     // experts per thread, <= 4
-    const int e0 = threadIdx.x * epp;
-    int c = 0;
-    for (int e = e0; e < min(E, e0 + epp); ++e) c += L.tokmask[e] != 0;
-    int incl = c;   // inclusive scan over the workgroup
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) L.wsum[wave] = incl;
-    __syncthreads();
+    // compact the experts with a nonzero token mask, ascending id: thread q
+    // looks at experts q, q + 256, ...; a ballot and the lane's count of
+    // lower set lanes place each one
     int base = 0;
-    for (int w = 0; w < wave; ++w) base += L.wsum[w];
-    int pos = base + incl - c;
-    for (int e = e0; e < min(E, e0 + epp); ++e) {
-        const int mask = L.tokmask[e];
-        if (!mask) continue;
-        MoeExpert &me = L.ex[pos++];
-        me.expert = e;
-        int cnt = 0;
-        for (int t = 0; t < 8; ++t)
-            if (mask & (1 << t)) {
-                me.tok[cnt] = t;
-                me.pair[cnt] = t * topk + L.jof[e][t];
-                ++cnt;
-            }
-        me.cnt = cnt;
+    for (int e0 = 0; e0 < E; e0 += 256) {
+        const int e = e0 + (int)threadIdx.x;
+        const int mask = e < E ? L.tokmask[e] : 0;
+        const uint64_t ball = __ballot(mask != 0);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0));
+        if (lane == 0) L.wsum[wave] = __popcll(ball);
+        __syncthreads();
+        int pos = base;
+        for (int w = 0; w < wave; ++w) pos += L.wsum[w];
+        pos += below;
+        const int total = L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3];
+        if (mask) {
+            MoeExpert &me = L.ex[pos];
+            me.expert = e;
+            int cnt = 0;
+            for (int t = 0; t < m; ++t)
+                if (mask & (1 << t)) {
+                    me.tok[cnt] = t;
+                    me.pair[cnt] = t * topk + L.jof[e][t];
+                    ++cnt;
+                }
+            me.cnt = cnt;
+        }
+        base += total;
+        __syncthreads();   // wsum is rewritten by the next round
     }
-    if (threadIdx.x == 255) L.n_distinct = base + incl;
+    if (threadIdx.x == 0) L.n_distinct = base;
     __syncthreads();
+}
+
+__device__ __forceinline__ void moe_route_lds(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
+    const int per = (E + 63) / 64;
+    if (per <= 1) moe_route_per<1>(logits, m, E, topk, L);
+    else if (per <= 2) moe_route_per<2>(logits, m, E, topk, L);
+    else if (per <= 4) moe_route_per<4>(logits, m, E, topk, L);
+    else if (per <= 8) moe_route_per<8>(logits, m, E, topk, L);
+    else moe_route_per<16>(logits, m, E, topk, L);
 }
 
 // Stages rows rows[0..cnt) of a [*, k] bf16 matrix into the swizzled LDS
@@ -257,8 +277,26 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
             ids[p] = L.sel_i[p / topk][p % topk];
             wts[p] = L.sel_w[p / topk][p % topk];
         }
-        for (int q = threadIdx.x; q < L.n_distinct; q += blockDim.x) route->ex[q] = L.ex[q];
-        if (threadIdx.x == 0) route->n_distinct = L.n_distinct;
+        for (int q = threadIdx.x; q < L.n_distinct; q += blockDim.x) {
+            route->ex[q] = L.ex[q];
+            route->ex_id[q] = L.ex[q].expert;
+            route->ddec[q] = e.down_global[L.ex[q].expert].dec;
+        }
+        if (threadIdx.x == 0) {
+            route->n_distinct = L.n_distinct;
+            int pb = 0;
+            for (int q = 0; q < L.n_distinct; ++q) {
+                const MoeExpert &me = L.ex[q];
+                route->pb[q] = pb;
+                for (int c = 0; c < me.cnt; ++c, ++pb) {
+                    route->pos_tok[pb] = me.tok[c];
+                    route->pos_pair[pb] = me.pair[c];
+                    route->pos_w[pb] = L.sel_w[me.tok[c]][me.pair[c] - me.tok[c] * topk];
+                }
+            }
+            route->pb[L.n_distinct] = pb;
+            route->n_pairs = pb;
+        }
     }
     if (threadIdx.x == 0) {
         s_nd = L.n_distinct;
@@ -349,6 +387,118 @@ __global__ __launch_bounds__(256) void k_moe_down(nvfp4_moe_weights e, int m, in
     if (threadIdx.x == 0) st_dev(&tickets[blockIdx.x], 0u);   // ready for the next call
 }
 
+// Down pass when every (token, slot) activation row fits in LDS (the usual
+// decode case: m * top_k <= 31 at inter = 1024).  Workgroup w owns output rows
+// [w * kDownRows, (w + 1) * kDownRows) of every routed expert: its 16 slots
+// take (expert, row) items in turn, all of a batch's weight loads in flight at
+// once, and write d into LDS; the workgroup then forms y = sum of w * d per
+// token in ascending expert order.  No scratch buffer, no ticket, one pass.
+constexpr int kDownRows = 8;
+constexpr int kDownBatch = 4;   // items per slot in flight
+
+template <int CPL>
+__global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
+                                                      const float *__restrict__ wts, const MoeRoute *__restrict__ route,
+                                                      const uint16_t *__restrict__ act, float *__restrict__ y) {
+    extern __shared__ uint4 smem[];
+    __shared__ int s_ex[128], s_pb[129];
+    __shared__ float s_dec[128], s_w[128];
+    __shared__ int s_tok[128], s_pair[128];
+    __shared__ float contrib[128][kDownRows];
+    const int H = e.hidden, I = e.inter, C = I >> 5;
+    // the plan in LDS, one round of loads
+    const int nd = route->n_distinct, P = route->n_pairs;
+    for (int i = threadIdx.x; i <= nd; i += blockDim.x) {
+        s_pb[i] = route->pb[i];
+        if (i < nd) {
+            s_ex[i] = route->ex_id[i];
+            s_dec[i] = route->ddec[i];
+        }
+    }
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        s_tok[i] = route->pos_tok[i];
+        s_pair[i] = route->pos_pair[i];
+        s_w[i] = route->pos_w[i];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tl = lane & 15;
+    const int sl = wave * 4 + (lane >> 4);
+    const int r0 = blockIdx.x * kDownRows;
+    const int nitems = nd * kDownRows;
+    const size_t wsz = (size_t)H * I;
+    for (int b0 = 0; b0 < nitems; b0 += 16 * kDownBatch) {
+        // weight loads of this batch first, then (first batch only) the
+        // activation image, so that both are in flight together
+        uint4 cw[kDownBatch][CPL];
+        uint32_t sw[kDownBatch][CPL];
+#pragma unroll
+        for (int n = 0; n < kDownBatch; ++n) {
+            // items past the end load a valid row (the last one); their
+            // results are never used
+            const int it = min(b0 + sl + 16 * n, nitems - 1);
+            const int u = it / kDownRows, row = min(r0 + it % kDownRows, H - 1);
+            const uint8_t *dc = e.down_codes + (size_t)s_ex[u] * (wsz / 2) + (size_t)row * (I / 2);
+            const uint8_t *ds = e.down_scales + (size_t)s_ex[u] * (wsz / 16) + (size_t)row * (I / 16);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = tl + 16 * j;
+                cw[n][j] = ld_stream16(dc + 16 * c);
+                sw[n][j] = ld_stream2(ds + 2 * c);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any arithmetic
+        if (b0 == 0) {
+            stage_rows(smem, act, s_pair, P, P, I);   // row pos of the image = pair position pos
+            __syncthreads();
+        }
+#pragma unroll
+        for (int n = 0; n < kDownBatch; ++n) {
+            const int it = b0 + sl + 16 * n;
+            if (it >= nitems) continue;   // uniform over the slot
+            const int u = it / kDownRows, r = it % kDownRows;
+            for (int pos = s_pb[u]; pos < s_pb[u + 1]; ++pos) {
+                float acc[1] = {0.0f};
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)pos * 4 * C, C, tl + 16 * j, acc);
+                const float d = row16_sum(acc[0]);
+                if (tl == 0) contrib[pos][r] = d * s_dec[u];
+            }
+        }
+    }
+    __syncthreads();
+    // y[t][row] = sum over token t's pairs, in ascending expert order, of
+    // w * d: one thread per (token, row); the positions are read four at a
+    // time so the LDS reads overlap
+    const int i = threadIdx.x;
+    if (i < m * kDownRows) {
+        const int t = i / kDownRows, r = i % kDownRows, row = r0 + r;
+        float acc = 0.0f;
+        int pos = 0;
+        for (; pos + 4 <= P; pos += 4) {
+            int tk[4];
+            float wv[4], cv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tk[q] = s_tok[pos + q];
+                wv[q] = s_w[pos + q];
+                cv[q] = contrib[pos + q][r];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (tk[q] == t) acc = __builtin_fmaf(wv[q], cv[q], acc);
+        }
+        for (; pos < P; ++pos)
+            if (s_tok[pos] == t) acc = __builtin_fmaf(s_w[pos], contrib[pos][r], acc);
+        if (row < H) y[(size_t)t * H + row] = acc;
+    }
+}
+
+template <int CPL>
+static void launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk,
+                             const float *wts, const MoeRoute *route, const uint16_t *act, float *y) {
+    hipLaunchKernelGGL(k_moe_down_rows<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, y);
+}
+
 struct MoeLayout {
     size_t tickets, act, dbuf, total;
 };
@@ -435,6 +585,17 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
     }
     int rc = check_launch("moe_w4a16_gemv(gate_up)");
     if (rc) return rc;
+    const size_t pairs = (size_t)m * top_k;
+    if (pairs <= 128 && pairs * I * 2 <= (size_t)kLdsBytes - 16384 && cpl_for(I) != 0) {
+        const dim3 g3((H + kDownRows - 1) / kDownRows);
+        const size_t lds3 = pairs * I * 2;
+        switch (cpl_for(I)) {
+            case 1: launch_down_rows<1>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
+            case 2: launch_down_rows<2>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
+            default: launch_down_rows<4>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
+        }
+        return check_launch("moe_w4a16_gemv(down)");
+    }
     switch (cpl_for(I)) {
         case 1: launch_down<1>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
         case 2: launch_down<2>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
