@@ -10,14 +10,20 @@
 // (hardware E2M1 -> fp32 convert, times the E4M3 block scale, packed to
 // bf16 -- exact, since e2m1 * e4m3 has at most 6 significant bits).  The
 // next step's global loads are issued before the current step's MFMAs.
-// LDS rows are padded to 144 bytes so the 16 rows read by one MFMA operand
-// load fall in distinct banks.  The global scale is applied in the epilogue.
+// LDS chunks are XOR-swizzled (lds_off) to spread the 16 rows of an operand
+// load and the rows of a staging store over the banks.  The global scale is
+// applied in the epilogue.
 #include "common.hpp"
 
 namespace nvfp4 {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdsRow = kBK * 2 + 16;   // bytes per padded LDS row
+constexpr int kLdsRow = kBK * 2;   // bytes per LDS row (64 bf16 of one K step)
+
+// Byte offset of 16-byte chunk c (8 bf16) of tile row r in LDS.  The chunk is
+// stored at position c ^ ((r / 2) % 8), so that the 16 rows one MFMA operand
+// load reads at a fixed chunk land in different bank groups.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsRow + 16 * (c ^ ((r >> 1) & 7)); }
 
 // Two E2M1 codes (byte SEL of word) times sf, packed as two bf16 (exact).
 template <int SEL>
@@ -81,18 +87,17 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
     for (int k0 = 0; k0 < K; k0 += kBK) {
         // stage: activations as they are, weights dequantized
         {
-            uint4 *pa = reinterpret_cast<uint4 *>(lds_a + srow * kLdsRow + 64 * shalf);
-            pa[0] = xr[0];
-            pa[1] = xr[1];
-            pa[2] = xr[2];
-            pa[3] = xr[3];
-            const float sf0 = e4m3_to_f32(sr & 0xFFu), sf1 = e4m3_to_f32(sr >> 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4 *>(lds_a + lds_off(srow, 4 * shalf + q)) = xr[q];
+            typedef __attribute__((ext_vector_type(2))) float f32x2;
+            const f32x2 sfv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sr, false);   // E4M3 block scales, exact
+            const float sf0 = sfv.x, sf1 = sfv.y;
             const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
-            uint4 *pb = reinterpret_cast<uint4 *>(lds_b + srow * kLdsRow + 64 * shalf);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const float sf = d < 2 ? sf0 : sf1;
-                pb[d] = make_uint4(dq2<0>(cw[d], sf), dq2<1>(cw[d], sf), dq2<2>(cw[d], sf), dq2<3>(cw[d], sf));
+                *reinterpret_cast<uint4 *>(lds_b + lds_off(srow, 4 * shalf + d)) =
+                    make_uint4(dq2<0>(cw[d], sf), dq2<1>(cw[d], sf), dq2<2>(cw[d], sf), dq2<3>(cw[d], sf));
             }
         }
         __syncthreads();
@@ -100,11 +105,11 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 af[4], bfr[4];
-            const int koff = 64 * ks + 16 * (lane >> 4);
+            const int kc = 4 * ks + (lane >> 4);   // 16-byte chunk of the K step
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8 *>(lds_a + (64 * wm + 16 * i + (lane & 15)) * kLdsRow + koff);
-                bfr[i] = *reinterpret_cast<const bf16x8 *>(lds_b + (64 * wn + 16 * i + (lane & 15)) * kLdsRow + koff);
+                af[i] = *reinterpret_cast<const bf16x8 *>(lds_a + lds_off(64 * wm + 16 * i + (lane & 15), kc));
+                bfr[i] = *reinterpret_cast<const bf16x8 *>(lds_b + lds_off(64 * wn + 16 * i + (lane & 15), kc));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
