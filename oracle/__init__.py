@@ -61,6 +61,7 @@ def lib():
         L.orc_gemm_sample.argtypes = [P, P, P, f32, i64, P, P, i64, P]
         L.orc_lmhead_argmax.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32,
                                         P, P, P, P]
+        L.orc_lmhead_logprob.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32, P]
         L.orc_moe.argtypes = [P, i64, P, i64, i64, i64, i64,
                               P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -183,6 +184,20 @@ def lmhead_argmax(h_bf16, codes, scales, g_dec, vrows=0, flags=0, want_logits=Fa
     if want_logits:
         return idx, mx, logits, bound
     return idx, mx
+
+
+def lmhead_logprob(h_bf16, codes, scales, g_dec, vrows=0, flags=0):
+    """Top-1 log-probability per activation row (fp64): the argmax key minus
+    the log-sum-exp of all keys of the first `vrows` rows."""
+    h = _c(h_bf16, np.uint16)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    m, k = h.shape
+    n = codes.shape[0]
+    v = n if vrows <= 0 else min(vrows, n)
+    lp = np.zeros(m, np.float64)
+    lib().orc_lmhead_logprob(_p(h), m, _p(codes), _p(scales), float(g_dec), k, v, int(flags), _p(lp))
+    return lp
 
 
 # ---- MoE ------------------------------------------------------------------------------

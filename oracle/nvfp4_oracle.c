@@ -305,6 +305,40 @@ ORC_API void orc_lmhead_argmax(const uint16_t *h, int64_t m, const uint8_t *code
 }
 
 /* ------------------------------------------------------------------ */
+/* Top-1 log-probability of the LM head's argmax ([mtp_head.rs] `MtpHead`
+ * fields: the batched argmax that also writes each row's top-1
+ * log-probability, and the stored confidence of the last draft):
+ *   lp = key[idx] - log(sum over r < vrows of exp(key[r]))
+ * with key = the fp32 logit, or its bf16 rounding when flags bit 0 is set
+ * (the same keys the argmax compares), idx the argmax of orc_lmhead_argmax.
+ * The log-sum-exp is taken in fp64 after subtracting the largest key; any
+ * NaN or infinite key makes lp NaN, as does a vocabulary of -inf keys.      */
+/* ------------------------------------------------------------------ */
+ORC_API void orc_lmhead_logprob(const uint16_t *h, int64_t m, const uint8_t *codes,
+                                const uint8_t *scales, float g_dec, int64_t k, int64_t vrows,
+                                uint32_t flags, double *out_lp) {
+    float *key = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
+    for (int64_t i = 0; i < m; ++i) {
+        float best = -INFINITY, kbest = 0.0f;
+        int have = 0;
+        double kmax = -INFINITY;
+        for (int64_t r = 0; r < vrows; ++r) {
+            const uint8_t *crow = codes + r * (k / 2);
+            const uint8_t *srow = scales + r * (k / 16);
+            const float logit = (float)((double)g_dec * dot_row(h + i * k, crow, srow, k));
+            key[r] = (flags & 1u) ? orc_bf16_round(logit) : logit;
+            if (key[r] > best) { best = key[r]; kbest = key[r]; have = 1; }
+            if ((double)key[r] > kmax) kmax = (double)key[r];
+        }
+        if (!have && vrows > 0) kbest = key[0];   /* the argmax keeps index 0 */
+        double sum = 0.0;
+        for (int64_t r = 0; r < vrows; ++r) sum += exp((double)key[r] - kmax);
+        out_lp[i] = (double)kbest - (kmax + log(sum));
+    }
+    free(key);
+}
+
+/* ------------------------------------------------------------------ */
 /* MoE FFN of the draft head: top-k experts by router logit, softmax over
  * the selected logits, SiLU-gated expert MLP, weighted sum
  * ([new.rs]: `moe_topk_softmax`, `moe_silu_mul`, `moe_weighted_sum_blend`,
