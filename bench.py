@@ -303,6 +303,17 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
         b = nvfp4_bytes(v, H) + M * H * 2 + M * 8
         out[f"lmhead_v{v}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                                "drafts_per_s": round(M / (ms * 1e-3), 1)}
+    # the same head with the top-1 log-probability (online log-sum-exp in the same pass)
+    ws = nv.lmhead_workspace(M, VOCAB, hl.device)
+    oi = torch.empty(M, dtype=torch.int32, device=hl.device)
+    om = torch.empty(M, dtype=torch.float32, device=hl.device)
+    olp = torch.empty(M, dtype=torch.float32, device=hl.device)
+    ms = _time_graph(torch, lambda i: nv.lmhead_gemv_argmax_logprob(hl, copies[i % NCOPIES]["lm"], vocab_rows=VOCAB,
+                                                                    workspace=ws, out_idx=oi, out_max=om,
+                                                                    out_logprob=olp), reps, s)
+    b = nvfp4_bytes(VOCAB, H) + M * H * 2 + M * 12
+    out[f"lmhead_logprob_v{VOCAB}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                       "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "drafts_per_s": round(M / (ms * 1e-3), 1)}
     ws = nv.moe_workspace(M, TOPK, copies[0]["moe"], hl.device)
     ymo = torch.empty((M, H), dtype=torch.float32, device=hl.device)
     ids = torch.empty((M, TOPK), dtype=torch.int32, device=hl.device)

@@ -194,6 +194,25 @@ int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
                        size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * lmhead_gemv_argmax_logprob -- lmhead_gemv_argmax that also returns, per
+ * activation row, the top-1 log-probability of the selected token: the
+ * batched argmax of [mtp_head.rs] (`MtpHead` fields) that writes each row's
+ * top-1 log-probability for the draft confidence stop.  In the same pass over
+ * the weights (no extra bytes read) each slot keeps an online log-sum-exp of
+ * the keys, merged with the argmax partials:
+ *   out_logprob[i] = key[out_idx[i]] - log(sum over r < V of exp(key[r]))
+ * in fp32, with the keys of lmhead_gemv_argmax (fp32 logits, or their bf16
+ * rounding with NVFP4_ARGMAX_BF16_KEYS).  A NaN or +inf key, or a vocabulary
+ * whose keys are all -inf, gives NaN.  All other arguments, the workspace
+ * (the same size) and the errors as lmhead_gemv_argmax; out_logprob [m] fp32,
+ * 4-byte aligned, must not be NULL.  One launch.
+ */
+int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                               int32_t vocab_rows, int32_t *out_idx, float *out_max,
+                               float *out_logprob, void *workspace, size_t ws_bytes,
+                               uint32_t flags, void *stream);
+
+/*
  * moe_w4a16_gemv -- routed-expert MoE FFN for decode rows: the
  * `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain named in
  * [new.rs] `MtpHead::new`, on NVFP4 experts.

@@ -63,12 +63,13 @@ def lib():
         L.lmhead_gemv_argmax_workspace_bytes.argtypes = [i32, i32]
         L.lmhead_gemv_argmax_workspace_bytes.restype = sz
         L.lmhead_gemv_argmax.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P]
+        L.lmhead_gemv_argmax_logprob.argtypes = [P, i32, WP, i32, P, P, P, P, sz, u32, P]
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
-                  "moe_w4a16_gemv"):
+                  "lmhead_gemv_argmax_logprob", "moe_w4a16_gemv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -252,6 +253,30 @@ def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf1
                                     NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
            "lmhead_gemv_argmax")
     return out_idx, out_max
+
+
+def lmhead_gemv_argmax_logprob(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,
+                               workspace: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                               out_max: torch.Tensor | None = None, out_logprob: torch.Tensor | None = None):
+    """lmhead_gemv_argmax plus the top-1 log-probability of each selected token."""
+    h = _as_bf16(h)
+    _dev(h, "h")
+    m = h.shape[0]
+    if workspace is None:
+        v = w.n if vocab_rows <= 0 else min(vocab_rows, w.n)
+        workspace = lmhead_workspace(m, v, h.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    if out_logprob is None:
+        out_logprob = torch.empty(m, dtype=torch.float32, device=h.device)
+    d = w.desc()
+    _check(lib().lmhead_gemv_argmax_logprob(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(out_idx), _ptr(out_max),
+                                            _ptr(out_logprob), _ptr(workspace), workspace.numel(),
+                                            NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
+           "lmhead_gemv_argmax_logprob")
+    return out_idx, out_max, out_logprob
 
 
 def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:

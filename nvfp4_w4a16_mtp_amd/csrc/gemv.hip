@@ -94,33 +94,61 @@ struct ArgPart {
     float key;    // compared value (fp32 logit or its bf16 rounding)
     float val;    // fp32 logit of that row
     int idx;
-    int pad;
+    float lm;     // log-sum-exp state of the keys seen: their largest finite
+    float ls;     // or +inf key lm, and ls = sum of exp(key - lm) (NaN-sticky)
+    int pad[3];
 };
 
+// Merges two log-sum-exp states (lm, ls).  -inf keys never enter a state, so
+// a state with lm = -inf has ls = 0.
+__device__ __forceinline__ void lse_merge(float &lm, float &ls, float om, float os) {
+    const float mn = fmaxf(lm, om);
+    if (mn == -INFINITY) {
+        ls += os;
+    } else {
+        ls = ls * __expf(lm - mn) + os * __expf(om - mn);
+        lm = mn;
+    }
+}
+
+template <bool LP>
+__device__ __forceinline__ void argpart_combine(ArgPart &b, const ArgPart &o) {
+    if constexpr (LP) lse_merge(b.lm, b.ls, o.lm, o.ls);
+    if (beats(o.key, o.idx, b.key, b.idx)) {
+        b.key = o.key;
+        b.val = o.val;
+        b.idx = o.idx;
+    }
+}
+
+template <bool LP>
 __device__ __forceinline__ void argpart_shfl_combine(ArgPart &b, int off) {
     ArgPart o;
     o.key = __shfl_xor(b.key, off, 64);
     o.val = __shfl_xor(b.val, off, 64);
     o.idx = __shfl_xor(b.idx, off, 64);
-    o.pad = 0;
-    if (beats(o.key, o.idx, b.key, b.idx)) b = o;
+    if constexpr (LP) {
+        o.lm = __shfl_xor(b.lm, off, 64);
+        o.ls = __shfl_xor(b.ls, off, 64);
+    }
+    argpart_combine<LP>(b, o);
 }
 
 // Workspace layout of lmhead_gemv_argmax.
 constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
 constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
-constexpr int kLmParts = 256;     // ArgPart[ntiles][MT]
+constexpr int kLmParts = 256;     // ArgPart[grid][MT]
 
 // Persistent LM-head pass over the global tiling (16 * R rows per tile):
 // the grid is the resident capacity and workgroup g scores tiles g, g + G,
 // g + 2G, ... so that at any moment the whole chip sweeps one contiguous band
 // of the matrix and every workgroup ends within one tile of the others.  The
 // activations are loaded once per workgroup.
-template <int MT, int R, int KS, int CPL, bool BF16KEY>
+template <int MT, int R, int KS, int CPL, bool BF16KEY, bool LP>
 __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
-                                               float *__restrict__ out_max) {
+                                               float *__restrict__ out_max, float *__restrict__ out_lp) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
@@ -136,12 +164,22 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     const int t_begin = blockIdx.x, t_step = gridDim.x;
     const float dec = g->dec;
     // lane m of every slot keeps the best of its rows for activation row m
-    ArgPart best{-INFINITY, -INFINITY, INT_MAX, 0};
+    // (scalars rather than an ArgPart: a struct captured by the lambda below
+    // is kept in scratch memory by the compiler)
+    float b_key = -INFINITY, b_val = -INFINITY, b_lm = -INFINITY, b_ls = 0.0f;
+    int b_idx = INT_MAX;
     auto epi = [&](int row, int mm, float s) {
         const float logit = s * dec;
         const float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
         if (row == 0) st_dev(&row0[mm], logit);
-        if (beats(key, row, best.key, best.idx)) best = ArgPart{key, logit, row, 0};
+        if constexpr (LP) {
+            if (key != -INFINITY) lse_merge(b_lm, b_ls, key, 1.0f);   // exp(-inf) adds nothing
+        }
+        if (beats(key, row, b_key, b_idx)) {
+            b_key = key;
+            b_val = logit;
+            b_idx = row;
+        }
     };
     if constexpr (MT == 1 && CPL > 0) {
         // one activation row: it lives in registers; each tile's loads are
@@ -177,19 +215,20 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     // workgroup combine: 16 slots x MT candidates -> MT partials
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane >> 4, t = lane & 15;
-    if (t < MT) cand[wave * 4 + slot][t] = best;
+    if (t < MT) cand[wave * 4 + slot][t] = ArgPart{b_key, b_val, b_idx, b_lm, b_ls, {0, 0, 0}};
     __syncthreads();
     if (threadIdx.x < MT) {
         const int mm = threadIdx.x;
-        ArgPart b{-INFINITY, -INFINITY, INT_MAX, 0};
-        for (int s = 0; s < 16; ++s) {
-            const ArgPart c = cand[s][mm];
-            if (beats(c.key, c.idx, b.key, b.idx)) b = c;
-        }
+        ArgPart b = cand[0][mm];
+        for (int s = 1; s < 16; ++s) argpart_combine<LP>(b, cand[s][mm]);
         ArgPart *dst = parts + (size_t)blockIdx.x * MT + mm;
         st_dev(&dst->key, b.key);
         st_dev(&dst->val, b.val);
         st_dev(&dst->idx, b.idx);
+        if constexpr (LP) {
+            st_dev(&dst->lm, b.lm);
+            st_dev(&dst->ls, b.ls);
+        }
     }
     wait_mem();   // partials and row-0 logits have reached device scope
     __syncthreads();
@@ -201,7 +240,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     const int nparts = gridDim.x;
     ArgPart b[MT];
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, 0};
+    for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
     // U partials per thread per round: all their loads are issued before any
     // is compared, so a round costs one memory latency, not U of them
     constexpr int U = 16 / MT;
@@ -214,22 +253,25 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
             for (int mm = 0; mm < MT; ++mm) {
                 if (p < nparts) {
                     const ArgPart *src = parts + (size_t)p * MT + mm;
-                    c[u][mm] = ArgPart{ld_dev(&src->key), ld_dev(&src->val), ld_dev(&src->idx), 0};
+                    c[u][mm].key = ld_dev(&src->key);
+                    c[u][mm].val = ld_dev(&src->val);
+                    c[u][mm].idx = ld_dev(&src->idx);
+                    c[u][mm].lm = LP ? ld_dev(&src->lm) : -INFINITY;
+                    c[u][mm].ls = LP ? ld_dev(&src->ls) : 0.0f;
                 } else {
-                    c[u][mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, 0};
+                    c[u][mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int mm = 0; mm < MT; ++mm)
-                if (beats(c[u][mm].key, c[u][mm].idx, b[mm].key, b[mm].idx)) b[mm] = c[u][mm];
+            for (int mm = 0; mm < MT; ++mm) argpart_combine<LP>(b[mm], c[u][mm]);
     }
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) argpart_shfl_combine(b[mm], off);
+        for (int off = 32; off > 0; off >>= 1) argpart_shfl_combine<LP>(b[mm], off);
     if (lane == 0) {
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) wbest[wave][mm] = b[mm];
@@ -238,18 +280,19 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     if (threadIdx.x < m_rt) {
         const int mm = threadIdx.x;
         ArgPart f = wbest[0][mm];
-        for (int w = 1; w < 4; ++w) {
-            const ArgPart c = wbest[w][mm];
-            if (beats(c.key, c.idx, f.key, f.idx)) f = c;
-        }
+        for (int w = 1; w < 4; ++w) argpart_combine<LP>(f, wbest[w][mm]);
         // nothing above -inf: the scan keeps its initial index 0
+        float wkey = f.key;
         if (!(f.key > -INFINITY)) {
+            const float l0 = ld_dev(&row0[mm]);
             out_idx[mm] = 0;
-            out_max[mm] = ld_dev(&row0[mm]);
+            out_max[mm] = l0;
+            wkey = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(l0)) : l0;
         } else {
             out_idx[mm] = f.idx;
             out_max[mm] = f.val;
         }
+        if constexpr (LP) out_lp[mm] = wkey - (f.lm + __logf(f.ls));
     }
     if (threadIdx.x == 0) st_dev(ticket, 0u);   // ready for the next call
 }
@@ -328,32 +371,34 @@ static int lm_grid(K kernel, size_t lds, int ntiles) {
     return ntiles < cap ? ntiles : cap;
 }
 
-template <int MT, int R, int KS, int CPL>
-static void launch_lm_cfg(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws,
-                          int32_t *oi, float *om, bool bk) {
-    if constexpr (KS == 1) {
-        const int ntiles = (v + 16 * R - 1) / (16 * R);
-        if (bk) {
-            auto kern = k_lmhead<MT, R, KS, CPL, true>;
-            hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales,
-                               w->global, v, w->k, ws, oi, om);
-        } else {
-            auto kern = k_lmhead<MT, R, KS, CPL, false>;
-            hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales,
-                               w->global, v, w->k, ws, oi, om);
-        }
-    }
+template <int MT, int CPL, bool BK, bool LP>
+static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
+                             char *ws, int32_t *oi, float *om, float *olp) {
+    auto kern = k_lmhead<MT, 2, 1, CPL, BK, LP>;
+    const int ntiles = (v + 31) / 32;
+    hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales, w->global,
+                       v, w->k, ws, oi, om, olp);
 }
 
-// The LM head keeps KS = 1 and R = 2 (two tiles of loads in flight per
-// wavefront fit in registers); there are at most ceil(V / 16) partials.
+// The LM head keeps KS = 1 and R = 2 (32-row tiles); there are at most
+// ceil(V / 32) partials.  A fixed chunk count when K = 2048.
 template <int MT>
 static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
-                           bool bk, hipStream_t s) {
-    TileChoice tc{2, 1, 0};
-    if (w->k % 512 == 0 && (w->k / 512 == 4)) tc.CPL = 4;
-    tc = canonical(tc);
-    NVFP4_TILE_SWITCH(launch_lm_cfg, MT, tc, gemv_lds_bytes(MT, w->k, tc), s, h, m, w, v, ws, oi, om, bk);
+                           float *olp, bool bk, hipStream_t s) {
+    const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
+    const size_t lds = gemv_lds_bytes(MT, w->k, tc);
+    const bool lp = olp != nullptr;
+    if (tc.CPL == 4) {
+        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp)
+                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp)
+                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+    } else {
+        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp)
+                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp)
+                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+    }
     return check_launch("lmhead_gemv_argmax");
 }
 
@@ -412,34 +457,48 @@ extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_ro
     return (size_t)kLmParts + (size_t)sizeof(ArgPart) * mt * (size_t)((vocab_rows + 15) / 16);
 }
 
-extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
-                                  int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
-                                  uint32_t flags, void *stream) {
-    int rc = validate_weight(w, "lmhead_gemv_argmax");
+static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
+                         int32_t *out_idx, float *out_max, float *out_lp, void *workspace, size_t ws_bytes,
+                         uint32_t flags, void *stream, const char *who) {
+    int rc = validate_weight(w, who);
     if (rc) return rc;
-    if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax: NULL h/out_idx/out_max");
-    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "lmhead_gemv_argmax: m=%d outside 1..8", m);
-    if (vocab_rows < 0) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax: vocab_rows=%d < 0", vocab_rows);
-    if (flags & ~NVFP4_ARGMAX_BF16_KEYS) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax: unknown flags 0x%x", flags);
+    if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "%s: NULL h/out_idx/out_max", who);
+    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "%s: m=%d outside 1..8", who, m);
+    if (vocab_rows < 0) return fail(NVFP4_ERR_ARG, "%s: vocab_rows=%d < 0", who, vocab_rows);
+    if (flags & ~NVFP4_ARGMAX_BF16_KEYS) return fail(NVFP4_ERR_ARG, "%s: unknown flags 0x%x", who, flags);
     const int v = (vocab_rows == 0 || vocab_rows > w->n) ? w->n : vocab_rows;
-    if (v < 1) return fail(NVFP4_ERR_SHAPE, "lmhead_gemv_argmax: empty vocabulary");
-    if (!aligned(h_bf16, 16) || !aligned(out_idx, 4) || !aligned(out_max, 4))
-        return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax: h needs 16-byte, outputs 4-byte alignment");
+    if (v < 1) return fail(NVFP4_ERR_SHAPE, "%s: empty vocabulary", who);
+    if (!aligned(h_bf16, 16) || !aligned(out_idx, 4) || !aligned(out_max, 4) || (out_lp && !aligned(out_lp, 4)))
+        return fail(NVFP4_ERR_ALIGN, "%s: h needs 16-byte, outputs 4-byte alignment", who);
     const int mt = round_up_mt(m);
     if ((size_t)mt * w->k * 2 > (size_t)kLdsBytes - 4096)
-        return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: %d (rounded-up) rows x k=%d activations exceed LDS", mt,
-                    w->k);
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w->k);
     const size_t need = lmhead_gemv_argmax_workspace_bytes(m, v);
     if (!workspace || ws_bytes < need)
-        return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax: workspace needs %zu bytes for %d rows", need, v);
-    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax: workspace not 256-byte aligned");
+        return fail(NVFP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes for %d rows", who, need, v);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "%s: workspace not 256-byte aligned", who);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
     switch (mt) {
-        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
-        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
-        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
-        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, bk, s);
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
+        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
+        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
+        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
     }
+}
+
+extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
+                                  int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
+                                  uint32_t flags, void *stream) {
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, workspace, ws_bytes, flags, stream,
+                         "lmhead_gemv_argmax");
+}
+
+extern "C" int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                                          int32_t vocab_rows, int32_t *out_idx, float *out_max, float *out_logprob,
+                                          void *workspace, size_t ws_bytes, uint32_t flags, void *stream) {
+    if (!out_logprob) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_logprob: NULL out_logprob");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, workspace, ws_bytes, flags, stream,
+                         "lmhead_gemv_argmax_logprob");
 }
