@@ -217,6 +217,9 @@ def main():
     }
     if not a.no_rows:
         result["rows"] = rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s)
+        del copies
+        torch.cuda.empty_cache()
+        result["rows_deepseek_shaped"] = deepseek_rows(nv, torch, M, s)
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(M, step_bytes, n_distinct)
     print(json.dumps(result), flush=True)
@@ -332,6 +335,70 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         out[f"gemm_{name}_m{m}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
         del w, x, y
+    return out
+
+
+DS_H, DS_V, DS_I, DS_E = 7168, 129280, 2048, 256
+
+
+def deepseek_rows(nv, torch, M, s):
+    """DeepSeek-shaped head (hidden 7168, vocabulary 129280, 256 experts of
+    width 2048, top-8): LM head + argmax, the routed MoE (a different routing
+    per launch, so experts stream from HBM) and a 18432 x 7168 GEMV (four
+    rotated copies), graph-timed like the other rows."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    out = {}
+
+    def q(n, k, into=None):
+        w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        return nv.nvfp4_quantize(w, out=into)
+
+    reps = 30
+    lm = q(DS_V, DS_H)
+    hl = (torch.randn((M, DS_H), generator=gen, device=dev)).to(torch.bfloat16)
+    ws = nv.lmhead_workspace(M, DS_V, dev)
+    oi = torch.empty(M, dtype=torch.int32, device=dev)
+    om = torch.empty(M, dtype=torch.float32, device=dev)
+    ms = _time_graph(torch, lambda i: nv.lmhead_gemv_argmax(hl, lm, workspace=ws, out_idx=oi, out_max=om), reps, s)
+    b = nvfp4_bytes(DS_V, DS_H) + M * DS_H * 2 + M * 8
+    out["lmhead_v129280_k7168"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                   "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "drafts_per_s": round(M / (ms * 1e-3), 1)}
+    del lm
+    ex = {}
+    for proj, rows, cols in (("gate", DS_I, DS_H), ("up", DS_I, DS_H), ("down", DS_H, DS_I)):
+        codes = torch.empty((DS_E, rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((DS_E, rows, cols // 16), dtype=torch.uint8, device=dev)
+        glob = torch.empty((DS_E, 4), dtype=torch.float32, device=dev)
+        for e in range(DS_E):
+            q(rows, cols, into=nv.NVFP4Weight(codes[e], scales[e], glob[e], rows, cols))
+        ex[proj] = (codes, scales, glob)
+    experts = nv.NVFP4Experts(*ex["gate"], *ex["up"], *ex["down"])
+    xm = torch.randn((M, DS_H), generator=gen, device=dev).to(torch.bfloat16)
+    routers = [torch.randn((M, DS_E), generator=gen, device=dev) for _ in range(reps)]
+    mws = nv.moe_workspace(M, TOPK, experts, dev)
+    ym = torch.empty((M, DS_H), dtype=torch.float32, device=dev)
+    ids = torch.empty((M, TOPK), dtype=torch.int32, device=dev)
+    wts = torch.empty((M, TOPK), dtype=torch.float32, device=dev)
+    nd = []
+    for r in routers:
+        nv.moe_w4a16_gemv(xm, r, TOPK, experts, workspace=mws, out=ym, topk_ids=ids, topk_w=wts)
+        nd.append(len(set(ids.cpu().numpy().ravel().tolist())))
+    ms = _time_graph(torch, lambda i: nv.moe_w4a16_gemv(xm, routers[i % reps], TOPK, experts, workspace=mws, out=ym,
+                                                        topk_ids=ids, topk_w=wts), reps, s)
+    b = float(np.mean(nd)) * 3 * nvfp4_bytes(DS_I, DS_H) + M * DS_H * 6 + M * DS_E * 4
+    out["moe_256x2048x7168_top8"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                     "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "mean_distinct_experts": float(np.mean(nd))}
+    del ex, experts
+    gws = [q(18432, DS_H) for _ in range(4)]
+    xg = torch.randn((M, DS_H), generator=gen, device=dev).to(torch.bfloat16)
+    yg = torch.empty((M, 18432), dtype=torch.float32, device=dev)
+    ms = _time_graph(torch, lambda i: nv.w4a16_gemv(xg, gws[i % 4], out=yg), reps, s)
+    b = nvfp4_bytes(18432, DS_H) + M * DS_H * 2 + M * 18432 * 4
+    out["gemv_18432x7168"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del gws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -127,7 +127,7 @@ int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint8_t *codes,
  *   y       [m][w->n], fp32 (y_dtype NVFP4_OUT_F32) or bf16 rounded to
  *           nearest-even from the fp32 sum (NVFP4_OUT_BF16); 4-byte aligned.
  * fp32 accumulation; one pass over codes and scales; one launch.  The
- * activations are staged in LDS: round_up_pow2(m) * k * 2 <= 65536.
+ * activations are staged in LDS: round_up_pow2(m) * k * 2 <= 155648.
  */
 int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
                int32_t y_dtype, void *stream);
@@ -219,8 +219,9 @@ int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_we
  *   x_bf16         [m][H] bf16, 16-byte aligned; m in 1..8.
  *   router_logits  [m][E] fp32 (the router projection's output).
  *   top_k          1..min(E, 16).
- *   y              out [m][H] fp32: sum_j w[j] * down_e(j)(a_j), j in
- *                  descending-logit order.
+ *   y              out [m][H] fp32: sum_j w[j] * down_e(j)(a_j), summed
+ *                  in fp32 in an order fixed by the routing (the same
+ *                  inputs give the same bits).
  *   topk_ids       out [m][top_k] int32: experts by descending logit, the
  *                  lower id first among equal logits.
  *   topk_w         out [m][top_k] fp32: softmax over the selected logits.
@@ -231,7 +232,9 @@ int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_we
  * Per selected expert: g = gate x, u = up x (fp32),
  * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
  * read once per call however many rows select it.  Requires H, I % 32 == 0
- * and H, I <= 3968.  Two launches (routing + gate/up, down + combine).
+ * and round_up(m, 1|2|4|8) * max(H, I) * 2 <= 159744 bytes of LDS (H up to
+ * 9984 at m = 8); NVFP4_ERR_UNSUPPORTED otherwise.  Two
+ * launches (routing + gate/up, down + combine).
  */
 size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
 int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,

@@ -74,6 +74,23 @@ int blocks_per_cu(const void *kernel, int block, size_t lds) {
     return v;
 }
 
+// Raises a kernel's dynamic LDS limit to `bytes` (needed above 64 KiB); the
+// largest value set so far is remembered per (device, kernel).
+int allow_lds(const void *kernel, size_t bytes, const char *who) {
+    if (bytes <= 65536) return NVFP4_OK;
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, size_t> done;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(mu);
+    size_t &cur = done[std::make_pair(dev, kernel)];
+    if (cur >= bytes) return NVFP4_OK;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: %zu bytes of LDS per workgroup are not available", who, bytes);
+    cur = bytes;
+    return NVFP4_OK;
+}
+
 }  // namespace nvfp4
 
 extern "C" const char *nvfp4_mtp_last_error(void) { return nvfp4::g_msg; }

@@ -27,6 +27,7 @@ int num_cus();
 // Resident workgroups per CU for a kernel at a block size and dynamic LDS
 // (hipOccupancyMaxActiveBlocksPerMultiprocessor, cached; at least 1).
 int blocks_per_cu(const void *kernel, int block, size_t lds);
+int allow_lds(const void *kernel, size_t bytes, const char *who);
 
 // ----------------------------------------------------------- bf16 / fp32 --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

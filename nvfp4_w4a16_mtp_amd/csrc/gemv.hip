@@ -331,6 +331,7 @@ static TileChoice canonical(TileChoice tc) {
 template <int MT, int R, int KS, int CPL>
 static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const GemvGroups &grp,
                             int k, int bf16) {
+    if (allow_lds(reinterpret_cast<const void *>(k_gemv<MT, R, KS, CPL>), lds, "w4a16_gemv")) return;
     hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, grp, k, bf16);
 }
 
@@ -358,7 +359,9 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
     }
     for (int i = count; i <= kMaxGroups; ++i) grp.tile0[i] = tiles;
     if (tiles == 0) return ok();
+    ok();   // clears the message that a refused LDS request would leave
     NVFP4_TILE_SWITCH(launch_gemv_cfg, MT, tc, dim3(tiles), gemv_lds_bytes(MT, k, tc), s, x, m, grp, k, bf16);
+    if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
     return check_launch("w4a16_gemv");
 }
 
@@ -375,6 +378,7 @@ template <int MT, int CPL, bool BK, bool LP>
 static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
                              char *ws, int32_t *oi, float *om, float *olp) {
     auto kern = k_lmhead<MT, 2, 1, CPL, BK, LP>;
+    if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
     const int ntiles = (v + 31) / 32;
     hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales, w->global,
                        v, w->k, ws, oi, om, olp);
@@ -388,6 +392,7 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
+    ok();   // clears the message that a refused LDS request would leave
     if (tc.CPL == 4) {
         if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp)
                    : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp);
@@ -399,6 +404,7 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
         else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp)
                 : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp);
     }
+    if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
     return check_launch("lmhead_gemv_argmax");
 }
 
@@ -427,7 +433,7 @@ static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
     if (!x_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL x", who);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "%s: x not 16-byte aligned", who);
     const int mt = round_up_mt(m);
-    if ((size_t)mt * w[0]->k * 2 > (size_t)kLdsBytes)
+    if ((size_t)mt * w[0]->k * 2 > kMaxLds)
         return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w[0]->k);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int bf16 = y_dtype == NVFP4_OUT_BF16;
@@ -471,7 +477,7 @@ static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *
     if (!aligned(h_bf16, 16) || !aligned(out_idx, 4) || !aligned(out_max, 4) || (out_lp && !aligned(out_lp, 4)))
         return fail(NVFP4_ERR_ALIGN, "%s: h needs 16-byte, outputs 4-byte alignment", who);
     const int mt = round_up_mt(m);
-    if ((size_t)mt * w->k * 2 > (size_t)kLdsBytes - 4096)
+    if ((size_t)mt * w->k * 2 > kMaxLds)
         return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w->k);
     const size_t need = lmhead_gemv_argmax_workspace_bytes(m, v);
     if (!workspace || ws_bytes < need)

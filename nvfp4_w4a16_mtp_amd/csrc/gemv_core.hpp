@@ -315,7 +315,8 @@ struct TileChoice {
     int R, KS, CPL;   // CPL 0: generic loop
 };
 
-constexpr int kLdsBytes = 64 * 1024;   // LDS budget of one workgroup
+constexpr int kLdsBytes = 64 * 1024;   // LDS budget of one workgroup when choosing a K split
+constexpr size_t kMaxLds = 160 * 1024 - 8192;   // largest activation image (LDS per workgroup, static LDS aside)
 
 // LDS bytes of a GEMV workgroup: the activation image plus, with a K split,
 // 16 * R * MT fp32 partial sums.

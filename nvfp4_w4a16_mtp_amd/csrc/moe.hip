@@ -29,6 +29,7 @@ constexpr int kMoeMaxTopK = 16;
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeHeader = 16384;   // route header bytes at the start of the workspace
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
+constexpr size_t kMoeMaxLds = 160 * 1024 - 4096;   // dynamic LDS of one workgroup, static LDS aside
 
 // One distinct expert of a call: the tokens that chose it (ascending) and,
 // for each, the index t * top_k + j of its (token, slot) pair.
@@ -513,15 +514,21 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
 }
 
 template <int CPL>
-static void launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
-                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
-                           uint16_t *act) {
+static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
+                          int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
+                          uint16_t *act) {
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL>), lds, "moe_w4a16_gemv");
+    if (rc) return rc;
     hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act);
+    return check_launch("moe_w4a16_gemv(gate_up)");
 }
 template <int CPL>
-static void launch_down(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk, const float *wts,
-                        const MoeRoute *route, const uint16_t *act, float *dbuf, unsigned int *tickets, float *y) {
+static int launch_down(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk, const float *wts,
+                       const MoeRoute *route, const uint16_t *act, float *dbuf, unsigned int *tickets, float *y) {
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_down<CPL>), lds, "moe_w4a16_gemv");
+    if (rc) return rc;
     hipLaunchKernelGGL(k_moe_down<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, dbuf, tickets, y);
+    return check_launch("moe_w4a16_gemv(down)");
 }
 
 static int cpl_for(int k) {
@@ -556,8 +563,11 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
         return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: top_k=%d outside 1..min(E, %d)", top_k, kMoeMaxTopK);
     if (H < 32 || I < 32 || H % 32 || I % 32)
         return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: hidden/inter must be multiples of 32");
-    if ((size_t)8 * H * 2 > (size_t)kLdsBytes - 1024 || (size_t)8 * I * 2 > (size_t)kLdsBytes - 1024)
-        return fail(NVFP4_ERR_UNSUPPORTED, "moe_w4a16_gemv: hidden/inter above %d", (kLdsBytes - 1024) / 16);
+    // an expert serves at most m tokens: its activation rows are staged for
+    // round_up(m) of them (up to 160 KiB of LDS per workgroup)
+    const int mt = round_up_mt(m);
+    if ((size_t)mt * H * 2 > kMoeMaxLds || (size_t)mt * I * 2 > kMoeMaxLds)
+        return fail(NVFP4_ERR_UNSUPPORTED, "moe_w4a16_gemv: %d rows x hidden %d / inter %d exceed the LDS", mt, H, I);
     if (!aligned(x_bf16, 16) || !aligned(e->gate_codes, 16) || !aligned(e->up_codes, 16) || !aligned(e->down_codes, 16))
         return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: x and codes need 16-byte alignment");
     if (!aligned(e->gate_scales, 2) || !aligned(e->up_scales, 2) || !aligned(e->down_scales, 2) ||
@@ -576,14 +586,14 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
     const int maxd = min(E, m * top_k);
     const nvfp4_moe_weights ev = *e;
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kMoeRows - 1) / kMoeRows, maxd);
-    const size_t lds1 = std::max((size_t)8 * H * 2, sizeof(RouteLds)), lds2 = (size_t)8 * I * 2;
+    const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
+    int rc;
     switch (cpl_for(H)) {
-        case 1: launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        case 2: launch_gate_up<2>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        case 4: launch_gate_up<4>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        default: launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 1: rc = launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 2: rc = launch_gate_up<2>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 4: rc = launch_gate_up<4>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        default: rc = launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
     }
-    int rc = check_launch("moe_w4a16_gemv(gate_up)");
     if (rc) return rc;
     const size_t pairs = (size_t)m * top_k;
     if (pairs <= 128 && pairs * I * 2 <= (size_t)kLdsBytes - 16384 && cpl_for(I) != 0) {
@@ -597,10 +607,9 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
         return check_launch("moe_w4a16_gemv(down)");
     }
     switch (cpl_for(I)) {
-        case 1: launch_down<1>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
-        case 2: launch_down<2>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
-        case 4: launch_down<4>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
-        default: launch_down<0>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y); break;
+        case 1: return launch_down<1>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
+        case 2: return launch_down<2>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
+        case 4: return launch_down<4>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
+        default: return launch_down<0>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
     }
-    return check_launch("moe_w4a16_gemv(down)");
 }

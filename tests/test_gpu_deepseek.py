@@ -1,0 +1,79 @@
+"""GPU parity on DeepSeek-shaped heads (hidden 7168, vocabulary 129280,
+256-expert MoE with expert width 2048): the LM-head GEMV + argmax (and its
+log-probability), the routed MoE and the decode GEMV, against the oracle.
+K = 7168 is not a multiple of 2048, so these take the generic K loop of the
+GEMV core; m = 8 needs more than 64 KiB of LDS for the activation image."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_w4a16_mtp_amd import synth
+from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_u8
+
+pytestmark = pytest.mark.gpu
+
+H, V, I = 7168, 129280, 2048
+
+
+def _w(codes, scales, g_dec):
+    import nvfp4_w4a16_mtp_amd as nv
+    return nv.NVFP4Weight.from_parts(dev_u8(codes), dev_u8(scales), float(g_dec))
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_gemv(orc, m):
+    import nvfp4_w4a16_mtp_amd as nv
+    codes, scales, g = synth.quantized_domain_weight(np.random.default_rng([110, m]), 1536, H)
+    x = synth.acts_bf16(111 + m, m, H)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    assert_close(y, orc.gemv(x, codes, scales, g), f"gemv 1536x{H} m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_lmhead_reduced_rows(orc, m):
+    """The first 8192 rows of a 129280 x 7168 head: planted winners, log-probability."""
+    import nvfp4_w4a16_mtp_amd as nv
+    vr = 8192
+    codes, scales, g = synth.quantized_domain_weight(np.random.default_rng(120), vr, H)
+    g = np.float32(g * 200.0)
+    h = synth.acts_bf16(121, m, H)
+    info = synth.plant_lmhead_rows(codes, scales, h, seed=122, n_near=4)
+    idx, mx, lp = nv.lmhead_gemv_argmax_logprob(dev_bf16(h), _w(codes, scales, g))
+    assert list(idx.cpu().numpy()) == [info["star"][i] for i in range(m)]
+    ridx, rmx = orc.lmhead_argmax(h, codes, scales, g)
+    assert_close(mx.cpu().numpy(), rmx, "max logit")
+    assert_close(lp.cpu().numpy(), orc.lmhead_logprob(h, codes, scales, g), "logprob")
+
+
+def test_lmhead_full_vocabulary(orc):
+    """All 129280 rows at m = 1 with a planted winner near the end."""
+    import nvfp4_w4a16_mtp_amd as nv
+    codes, scales, g = synth.quantized_domain_weight(np.random.default_rng(130), V, H)
+    h = synth.acts_bf16(131, 1, H)
+    info = synth.plant_lmhead_rows(codes, scales, h, seed=132, n_near=4)
+    idx, mx = nv.lmhead_gemv_argmax(dev_bf16(h), _w(codes, scales, g))
+    assert int(idx.item()) == info["star"][0]
+    _, rmx = orc.lmhead_argmax(h, codes, scales, g)
+    assert_close(mx.cpu().numpy(), rmx, "max logit")
+
+
+@pytest.mark.parametrize("m,topk", [(1, 8), (4, 8), (8, 8)])
+def test_moe(orc, m, topk):
+    """32 experts of the DeepSeek expert shape (gate/up 2048 x 7168, down
+    7168 x 2048); m = 8 stages 8 activation rows of 7168 in LDS."""
+    import nvfp4_w4a16_mtp_amd as nv
+    E = 32
+    ex = synth.moe_quantized_experts(140 + m, E, H, I)
+    x = synth.acts_bf16(141 + m, m, H)
+    r = synth.router_logits(142 + m, m, E)
+
+    def glob4(g):
+        a = np.zeros((len(g), 4), np.float32)
+        a[:, 0] = g
+        return torch.from_numpy(a).cuda()
+    dex = nv.NVFP4Experts(*[dev_u8(t) if i % 3 != 2 else glob4(t) for i, t in enumerate([p for proj in ex for p in proj])])
+    y, ids, wts = nv.moe_w4a16_gemv(dev_bf16(x), dev_f32(r), topk, dex)
+    ry, rids, rw = orc.moe(x, r, topk, *ex)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert_close(wts.cpu().numpy(), rw, "weights")
+    assert_close(y.cpu().numpy(), ry, f"moe m={m}")
