@@ -62,6 +62,8 @@ def lib():
         L.orc_lmhead_argmax.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32,
                                         P, P, P, P]
         L.orc_lmhead_logprob.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32, P]
+        L.orc_lmhead_masked.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32, P, i64, P, P, P]
+        L.orc_embed_rows.argtypes = [P, i64, P, i64, i64, P]
         L.orc_moe.argtypes = [P, i64, P, i64, i64, i64, i64,
                               P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -198,6 +200,39 @@ def lmhead_logprob(h_bf16, codes, scales, g_dec, vrows=0, flags=0):
     lp = np.zeros(m, np.float64)
     lib().orc_lmhead_logprob(_p(h), m, _p(codes), _p(scales), float(g_dec), k, v, int(flags), _p(lp))
     return lp
+
+
+def lmhead_masked(h_bf16, codes, scales, g_dec, mask=None, vrows=0, flags=0):
+    """Grammar-masked argmax over the first `vrows` rows: mask is uint32
+    [m][words] (bit r % 32 of word r / 32 allows row r) or None.  Returns
+    (idx, max logit, top-1 log-probability over the allowed rows)."""
+    h = _c(h_bf16, np.uint16)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    m, k = h.shape
+    n = codes.shape[0]
+    v = n if vrows <= 0 else min(vrows, n)
+    words = 0
+    if mask is not None:
+        mask = _c(mask, np.uint32)
+        assert mask.shape[0] == m
+        words = mask.shape[1]
+    idx = np.zeros(m, np.int32)
+    mx = np.zeros(m, np.float32)
+    lp = np.zeros(m, np.float64)
+    lib().orc_lmhead_masked(_p(h), m, _p(codes), _p(scales), float(g_dec), k, v, int(flags), _p(mask), words,
+                            _p(idx), _p(mx), _p(lp))
+    return idx, mx, lp
+
+
+def embed_rows(idx, table_bf16):
+    """Rows table[idx[i]] (bf16 bits), zero rows for out-of-range ids."""
+    idx = _c(idx, np.int32)
+    table = _c(table_bf16, np.uint16)
+    vocab, hidden = table.shape
+    out = np.zeros((len(idx), hidden), np.uint16)
+    lib().orc_embed_rows(_p(idx), len(idx), _p(table), vocab, hidden, _p(out))
+    return out
 
 
 # ---- MoE ------------------------------------------------------------------------------

@@ -339,6 +339,66 @@ ORC_API void orc_lmhead_logprob(const uint16_t *h, int64_t m, const uint8_t *cod
 }
 
 /* ------------------------------------------------------------------ */
+/* Grammar-masked LM-head argmax ([v4_mtp.rs] `argmax_grammar_masked`):
+ * token r is allowed when bit r % 32 of mask word r / 32 of the row's mask
+ * is set (mask_words words per activation row); the ascending strict-greater
+ * scan runs over the allowed tokens only and starts at index 0 with -inf, so
+ * an empty allowed set (or one whose keys are all -inf or NaN) gives index 0.
+ * out_max is the fp32 logit of the returned row.  out_lp (optional) is the
+ * top-1 log-probability over the allowed tokens: key[idx] minus the
+ * log-sum-exp of the allowed keys, NaN when that set has no finite mass.
+ * mask == NULL allows every row (then this equals orc_lmhead_argmax and
+ * orc_lmhead_logprob).                                                  */
+/* ------------------------------------------------------------------ */
+ORC_API void orc_lmhead_masked(const uint16_t *h, int64_t m, const uint8_t *codes,
+                               const uint8_t *scales, float g_dec, int64_t k, int64_t vrows,
+                               uint32_t flags, const uint32_t *mask, int64_t mask_words,
+                               int32_t *out_idx, float *out_max, double *out_lp) {
+    float *key = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
+    float *logit = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
+    char *allowed = (char *)malloc((size_t)(vrows > 0 ? vrows : 1));
+    for (int64_t i = 0; i < m; ++i) {
+        float best = -INFINITY;
+        int32_t bi = 0;
+        double kmax = -INFINITY;
+        for (int64_t r = 0; r < vrows; ++r) {
+            const uint8_t *crow = codes + r * (k / 2);
+            const uint8_t *srow = scales + r * (k / 16);
+            logit[r] = (float)((double)g_dec * dot_row(h + i * k, crow, srow, k));
+            key[r] = (flags & 1u) ? orc_bf16_round(logit[r]) : logit[r];
+            allowed[r] = mask == NULL ||
+                         (r / 32 < mask_words && ((mask[i * mask_words + r / 32] >> (r % 32)) & 1u));
+            if (!allowed[r]) continue;
+            if (key[r] > best) { best = key[r]; bi = (int32_t)r; }
+            if ((double)key[r] > kmax) kmax = (double)key[r];
+        }
+        out_idx[i] = bi;
+        out_max[i] = vrows > 0 ? logit[bi] : 0.0f;
+        if (out_lp) {
+            double sum = 0.0;
+            for (int64_t r = 0; r < vrows; ++r)
+                if (allowed[r]) sum += exp((double)key[r] - kmax);
+            /* an empty allowed set has no probability mass: not measured */
+            out_lp[i] = sum > 0.0 ? (double)key[bi] - (kmax + log(sum)) : NAN;
+        }
+    }
+    free(key);
+    free(logit);
+    free(allowed);
+}
+
+/* Embedding rows of the draft tokens ([mtp_head.rs] `embed_from_argmax`,
+ * which also stores the draft id on the device for deferred readback):
+ * out[i][:] = table[idx[i]][:] (bf16 rows of `hidden`), a zero row for an
+ * index outside [0, vocab).                                               */
+ORC_API void orc_embed_rows(const int32_t *idx, int64_t m, const uint16_t *table, int64_t vocab,
+                            int64_t hidden, uint16_t *out) {
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t c = 0; c < hidden; ++c)
+            out[i * hidden + c] = (idx[i] >= 0 && idx[i] < vocab) ? table[(int64_t)idx[i] * hidden + c] : 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* MoE FFN of the draft head: top-k experts by router logit, softmax over
  * the selected logits, SiLU-gated expert MLP, weighted sum
  * ([new.rs]: `moe_topk_softmax`, `moe_silu_mul`, `moe_weighted_sum_blend`,
