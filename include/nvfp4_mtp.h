@@ -213,6 +213,47 @@ int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_we
                                uint32_t flags, void *stream);
 
 /*
+ * lmhead_gemv_argmax_masked -- lmhead_gemv_argmax restricted to the tokens a
+ * grammar allows: the device-side form of the masked argmax of [v4_mtp.rs]
+ * `argmax_grammar_masked`, which needs no logits readback.
+ *   allow_mask    device uint32 [m][mask_words]: token r is allowed for
+ *                 activation row i when bit r % 32 of word r / 32 of row i is
+ *                 set; tokens past the mask are not allowed.  4-byte aligned.
+ *   out_logprob   NULL, or [m] fp32: the top-1 log-probability over the
+ *                 allowed tokens (key[idx] minus the log-sum-exp of the
+ *                 allowed keys); NaN when no allowed key has finite mass.
+ * A disallowed token is scored as a -inf key, so the scan of
+ * lmhead_gemv_argmax applies: the lowest-index maximum among the allowed
+ * tokens, and index 0 (with row 0's logit in out_max) when nothing allowed
+ * exceeds -inf, including an empty allowed set -- the pad draft of the scan.
+ * Workspace, errors and the other arguments as lmhead_gemv_argmax.  One
+ * launch; the mask word of each 32-row tile is loaded with its weights.
+ */
+int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                              int32_t vocab_rows, const uint32_t *allow_mask, int32_t mask_words,
+                              int32_t *out_idx, float *out_max, float *out_logprob,
+                              void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * embed_from_argmax -- the draft tokens' embedding rows, gathered on the
+ * device: the `embed_from_argmax` step of [mtp_head.rs] (`MtpHead` fields),
+ * which feeds the next draft step and stores the draft id in device memory
+ * for deferred readback, so that a chain of draft steps needs no host round
+ * trip ([v4_mtp.rs] `propose` feeds each draft into the next step).
+ *   idx         device int32 [m] (e.g. out_idx of lmhead_gemv_argmax).
+ *   table_bf16  device bf16 [vocab][hidden], 16-byte aligned; hidden % 8 == 0.
+ *   out_bf16    device bf16, row i at out_bf16 + i * out_stride (elements;
+ *               out_stride >= hidden, a multiple of 8), 16-byte aligned --
+ *               e.g. the first half of the next step's fc input row.
+ *   id_log      NULL, or device int32 [m]: receives idx (the chain's record).
+ * An index outside [0, vocab) gives a zero row (id_log still records it).
+ * m == 0 does nothing.  One launch.
+ */
+int embed_from_argmax(const int32_t *idx, int32_t m, const uint16_t *table_bf16, int32_t vocab,
+                      int32_t hidden, uint16_t *out_bf16, int64_t out_stride, int32_t *id_log,
+                      void *stream);
+
+/*
  * moe_w4a16_gemv -- routed-expert MoE FFN for decode rows: the
  * `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain named in
  * [new.rs] `MtpHead::new`, on NVFP4 experts.

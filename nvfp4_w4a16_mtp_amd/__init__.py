@@ -64,12 +64,14 @@ def lib():
         L.lmhead_gemv_argmax_workspace_bytes.restype = sz
         L.lmhead_gemv_argmax.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P]
         L.lmhead_gemv_argmax_logprob.argtypes = [P, i32, WP, i32, P, P, P, P, sz, u32, P]
+        L.lmhead_gemv_argmax_masked.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, sz, u32, P]
+        L.embed_from_argmax.argtypes = [P, i32, P, i32, i32, P, ctypes.c_int64, P, P]
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
-                  "lmhead_gemv_argmax_logprob", "moe_w4a16_gemv"):
+                  "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "moe_w4a16_gemv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -277,6 +279,57 @@ def lmhead_gemv_argmax_logprob(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int 
                                             NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
            "lmhead_gemv_argmax_logprob")
     return out_idx, out_max, out_logprob
+
+
+def lmhead_gemv_argmax_masked(h: torch.Tensor, w: NVFP4Weight, allow_mask: torch.Tensor, vocab_rows: int = 0,
+                              bf16_keys: bool = False, with_logprob: bool = False,
+                              workspace: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                              out_max: torch.Tensor | None = None, out_logprob: torch.Tensor | None = None):
+    """Grammar-masked LM-head argmax.  allow_mask: int32/uint32 [m][words] on
+    the device (bit r % 32 of word r / 32 allows token r)."""
+    h = _as_bf16(h)
+    _dev(h, "h")
+    _dev(allow_mask, "allow_mask")
+    m = h.shape[0]
+    if allow_mask.dim() != 2 or allow_mask.shape[0] != m or allow_mask.element_size() != 4:
+        raise ValueError("allow_mask must be a [m][words] 32-bit tensor")
+    allow_mask = allow_mask.contiguous()
+    if workspace is None:
+        v = w.n if vocab_rows <= 0 else min(vocab_rows, w.n)
+        workspace = lmhead_workspace(m, v, h.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    if with_logprob and out_logprob is None:
+        out_logprob = torch.empty(m, dtype=torch.float32, device=h.device)
+    d = w.desc()
+    _check(lib().lmhead_gemv_argmax_masked(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(allow_mask),
+                                           allow_mask.shape[1], _ptr(out_idx), _ptr(out_max), _ptr(out_logprob),
+                                           _ptr(workspace), workspace.numel(),
+                                           NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
+           "lmhead_gemv_argmax_masked")
+    return (out_idx, out_max, out_logprob) if with_logprob else (out_idx, out_max)
+
+
+def embed_from_argmax(idx: torch.Tensor, table: torch.Tensor, out: torch.Tensor | None = None,
+                      id_log: torch.Tensor | None = None):
+    """Rows table[idx[i]] of a bf16 [vocab][hidden] table (zero rows for
+    out-of-range ids) into out (rows may be strided, e.g. half of a wider
+    activation row); id_log, if given, receives the ids."""
+    _dev(idx, "idx")
+    _dev(table, "table")
+    if table.dtype != torch.bfloat16 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("table must be a contiguous bf16 [vocab][hidden] tensor")
+    m = idx.numel()
+    vocab, hidden = table.shape
+    if out is None:
+        out = torch.empty((m, hidden), dtype=torch.bfloat16, device=table.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape[1] != hidden or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [m][hidden] with unit column stride")
+    _check(lib().embed_from_argmax(_ptr(idx), m, _ptr(table), vocab, hidden, _ptr(out), out.stride(0), _ptr(id_log),
+                                   _stream(table)), "embed_from_argmax")
+    return out
 
 
 def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:

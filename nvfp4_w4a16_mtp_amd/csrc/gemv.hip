@@ -148,7 +148,8 @@ template <int MT, int R, int KS, int CPL, bool BF16KEY, bool LP>
 __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
-                                               float *__restrict__ out_max, float *__restrict__ out_lp) {
+                                               float *__restrict__ out_max, float *__restrict__ out_lp,
+                                               const uint32_t *__restrict__ mask, int mask_words) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
@@ -168,10 +169,23 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     // is kept in scratch memory by the compiler)
     float b_key = -INFINITY, b_val = -INFINITY, b_lm = -INFINITY, b_ls = 0.0f;
     int b_idx = INT_MAX;
+    // Grammar mask word of a tile (tiles are 32 rows, 32-aligned) for the
+    // activation row this lane serves in the epilogue; all ones without a mask.
+    // Loaded with the tile's weights, so it adds no latency to the epilogue.
+    static_assert(GemvTile<R, KS>::kRowsPerTile == 32, "one mask word per tile");
+    const int mrow = min(min((int)(threadIdx.x & 15), MT - 1), m_rt - 1);
+    auto load_mask = [&](int tile) -> uint32_t {
+        if (mask == nullptr) return ~0u;
+        return tile < mask_words ? mask[(size_t)mrow * mask_words + tile] : 0u;
+    };
+    uint32_t mword = ~0u;
     auto epi = [&](int row, int mm, float s) {
         const float logit = s * dec;
-        const float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
+        float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
         if (row == 0) st_dev(&row0[mm], logit);
+        // grammar mask: a disallowed row is scored as -inf (mword holds this
+        // lane's mask word of the current 32-row tile)
+        if (!((mword >> (row & 31)) & 1u)) key = -INFINITY;
         if constexpr (LP) {
             if (key != -INFINITY) lse_merge(b_lm, b_ls, key, 1.0f);   // exp(-inf) adds nothing
         }
@@ -190,26 +204,36 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         for (int t = t_begin; t < ntiles; t += t_step) {
             TileRegs<MT, R, KS, CPL> cur;
             gemv_tile_load(cur, codes, scales, v, k, t * rows);
+            mword = load_mask(t);
             gemv_tile_compute_x1(cur, xr, v, t * rows, red, epi);
         }
     } else if constexpr (CPL > 0) {
         TileRegs<MT, R, KS, CPL> cur;
         gemv_tile_load(cur, codes, scales, v, k, t_begin * rows);
+        uint32_t mcur = load_mask(t_begin);
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
         for (int t = t_begin; t < ntiles; t += t_step) {
             TileRegs<MT, R, KS, CPL> nxt;
-            if (t + t_step < ntiles)
+            uint32_t mnxt = mcur;
+            if (t + t_step < ntiles) {
                 gemv_tile_load(nxt, codes, scales, v, k, (t + t_step) * rows);
-            else
+                mnxt = load_mask(t + t_step);
+            } else {
                 nxt = cur;
+            }
+            mword = mcur;
             gemv_tile_compute(cur, xs, v, k, t * rows, red, epi);
             cur = nxt;
+            mcur = mnxt;
         }
     } else {
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        for (int t = t_begin; t < ntiles; t += t_step) gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
+        for (int t = t_begin; t < ntiles; t += t_step) {
+            mword = load_mask(t);
+            gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
+        }
     }
 
     // workgroup combine: 16 slots x MT candidates -> MT partials
@@ -292,7 +316,8 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
             out_idx[mm] = f.idx;
             out_max[mm] = f.val;
         }
-        if constexpr (LP) out_lp[mm] = wkey - (f.lm + __logf(f.ls));
+        // no mass (nothing allowed, or only -inf keys): not measured
+        if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
     }
     if (threadIdx.x == 0) st_dev(ticket, 0u);   // ready for the next call
 }
@@ -376,33 +401,33 @@ static int lm_grid(K kernel, size_t lds, int ntiles) {
 
 template <int MT, int CPL, bool BK, bool LP>
 static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
-                             char *ws, int32_t *oi, float *om, float *olp) {
+                             char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words) {
     auto kern = k_lmhead<MT, 2, 1, CPL, BK, LP>;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
     const int ntiles = (v + 31) / 32;
     hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales, w->global,
-                       v, w->k, ws, oi, om, olp);
+                       v, w->k, ws, oi, om, olp, mask, mask_words);
 }
 
 // The LM head keeps KS = 1 and R = 2 (32-row tiles); there are at most
 // ceil(V / 32) partials.  A fixed chunk count when K = 2048.
 template <int MT>
 static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
-                           float *olp, bool bk, hipStream_t s) {
+                           float *olp, const uint32_t *mask, int mask_words, bool bk, hipStream_t s) {
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
     ok();   // clears the message that a refused LDS request would leave
     if (tc.CPL == 4) {
-        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp)
-                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp);
-        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp)
-                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
+                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
+        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
+                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
     } else {
-        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp)
-                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp);
-        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp)
-                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp);
+        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
+                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
+        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
+                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
     }
     if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
     return check_launch("lmhead_gemv_argmax");
@@ -464,8 +489,8 @@ extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_ro
 }
 
 static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
-                         int32_t *out_idx, float *out_max, float *out_lp, void *workspace, size_t ws_bytes,
-                         uint32_t flags, void *stream, const char *who) {
+                         int32_t *out_idx, float *out_max, float *out_lp, const uint32_t *mask, int32_t mask_words,
+                         void *workspace, size_t ws_bytes, uint32_t flags, void *stream, const char *who) {
     int rc = validate_weight(w, who);
     if (rc) return rc;
     if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "%s: NULL h/out_idx/out_max", who);
@@ -487,24 +512,35 @@ static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *
     char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
     switch (mt) {
-        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
-        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
-        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
-        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, bk, s);
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
+        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
+        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
+        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
     }
 }
 
 extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
                                   int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
                                   uint32_t flags, void *stream) {
-    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, workspace, ws_bytes, flags, stream,
-                         "lmhead_gemv_argmax");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, workspace, ws_bytes, flags,
+                         stream, "lmhead_gemv_argmax");
 }
 
 extern "C" int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
                                           int32_t vocab_rows, int32_t *out_idx, float *out_max, float *out_logprob,
                                           void *workspace, size_t ws_bytes, uint32_t flags, void *stream) {
     if (!out_logprob) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_logprob: NULL out_logprob");
-    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, workspace, ws_bytes, flags, stream,
-                         "lmhead_gemv_argmax_logprob");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, nullptr, 0, workspace, ws_bytes,
+                         flags, stream, "lmhead_gemv_argmax_logprob");
+}
+
+extern "C" int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                                         int32_t vocab_rows, const uint32_t *allow_mask, int32_t mask_words,
+                                         int32_t *out_idx, float *out_max, float *out_logprob, void *workspace,
+                                         size_t ws_bytes, uint32_t flags, void *stream) {
+    if (!allow_mask) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_masked: NULL allow_mask");
+    if (mask_words < 0) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_masked: mask_words=%d < 0", mask_words);
+    if (!aligned(allow_mask, 4)) return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax_masked: mask not 4-byte aligned");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, allow_mask, mask_words, workspace,
+                         ws_bytes, flags, stream, "lmhead_gemv_argmax_masked");
 }
