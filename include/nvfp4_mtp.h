@@ -254,6 +254,25 @@ int embed_from_argmax(const int32_t *idx, int32_t m, const uint16_t *table_bf16,
                       void *stream);
 
 /*
+ * lmhead_gemv_argmax_embed -- the LM head's argmax with the embedding gather
+ * of the selected tokens done by its last workgroup: one launch for the tail
+ * of a draft step and the head of the next (the gather of embed_from_argmax
+ * without a kernel boundary or a second read of the index).
+ *   allow_mask, mask_words   as lmhead_gemv_argmax_masked, or NULL / 0.
+ *   out_logprob              NULL, or as lmhead_gemv_argmax_logprob.
+ *   table_bf16, table_vocab, hidden, out_embed, out_stride, id_log
+ *                            as embed_from_argmax (table_vocab may differ
+ *                            from the head's rows; hidden % 8 == 0).
+ * out_idx, out_max, the workspace and the errors as lmhead_gemv_argmax.
+ */
+int lmhead_gemv_argmax_embed(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                             int32_t vocab_rows, const uint32_t *allow_mask, int32_t mask_words,
+                             int32_t *out_idx, float *out_max, float *out_logprob,
+                             const uint16_t *table_bf16, int32_t table_vocab, int32_t hidden,
+                             uint16_t *out_embed, int64_t out_stride, int32_t *id_log,
+                             void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
  * moe_w4a16_gemv -- routed-expert MoE FFN for decode rows: the
  * `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain named in
  * [new.rs] `MtpHead::new`, on NVFP4 experts.

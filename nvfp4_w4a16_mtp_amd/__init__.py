@@ -66,12 +66,15 @@ def lib():
         L.lmhead_gemv_argmax_logprob.argtypes = [P, i32, WP, i32, P, P, P, P, sz, u32, P]
         L.lmhead_gemv_argmax_masked.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, sz, u32, P]
         L.embed_from_argmax.argtypes = [P, i32, P, i32, i32, P, ctypes.c_int64, P, P]
+        L.lmhead_gemv_argmax_embed.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, i32, i32, P, ctypes.c_int64, P,
+                                               P, sz, u32, P]
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
-                  "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "moe_w4a16_gemv"):
+                  "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
+                  "moe_w4a16_gemv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -330,6 +333,44 @@ def embed_from_argmax(idx: torch.Tensor, table: torch.Tensor, out: torch.Tensor 
     _check(lib().embed_from_argmax(_ptr(idx), m, _ptr(table), vocab, hidden, _ptr(out), out.stride(0), _ptr(id_log),
                                    _stream(table)), "embed_from_argmax")
     return out
+
+
+def lmhead_gemv_argmax_embed(h: torch.Tensor, w: NVFP4Weight, table: torch.Tensor, out_embed: torch.Tensor,
+                             vocab_rows: int = 0, allow_mask: torch.Tensor | None = None, bf16_keys: bool = False,
+                             id_log: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             out_idx: torch.Tensor | None = None, out_max: torch.Tensor | None = None,
+                             out_logprob: torch.Tensor | None = None):
+    """LM-head argmax whose last workgroup also writes table[idx[i]] into
+    out_embed row i (bf16, unit column stride) and idx into id_log."""
+    h = _as_bf16(h)
+    _dev(h, "h")
+    _dev(table, "table")
+    m = h.shape[0]
+    if table.dtype != torch.bfloat16 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("table must be a contiguous bf16 [vocab][hidden] tensor")
+    vocab, hidden = table.shape
+    if out_embed.dtype != torch.bfloat16 or out_embed.dim() != 2 or out_embed.shape != (m, hidden) \
+            or out_embed.stride(1) != 1:
+        raise ValueError("out_embed must be bf16 [m][hidden] with unit column stride")
+    words = 0
+    if allow_mask is not None:
+        _dev(allow_mask, "allow_mask")
+        allow_mask = allow_mask.contiguous()
+        words = allow_mask.shape[1]
+    if workspace is None:
+        v = w.n if vocab_rows <= 0 else min(vocab_rows, w.n)
+        workspace = lmhead_workspace(m, v, h.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    d = w.desc()
+    _check(lib().lmhead_gemv_argmax_embed(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(allow_mask), words,
+                                          _ptr(out_idx), _ptr(out_max), _ptr(out_logprob), _ptr(table), vocab, hidden,
+                                          _ptr(out_embed), out_embed.stride(0), _ptr(id_log), _ptr(workspace),
+                                          workspace.numel(), NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
+           "lmhead_gemv_argmax_embed")
+    return out_idx, out_max
 
 
 def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:

@@ -139,6 +139,17 @@ constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
 constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
 constexpr int kLmParts = 256;     // ArgPart[grid][MT]
 
+// Optional gather of the selected tokens' embedding rows by the last
+// workgroup (the next draft step's input, device-resident): table [vocab][units
+// x 16 B], row i written at out + i * stride_units, id_log[i] = index.
+struct EmbedOut {
+    const uint4 *table;   // nullptr: no gather
+    uint4 *out;
+    int32_t *id_log;
+    int64_t stride_units;
+    int vocab, units;
+};
+
 // Persistent LM-head pass over the global tiling (16 * R rows per tile):
 // the grid is the resident capacity and workgroup g scores tiles g, g + G,
 // g + 2G, ... so that at any moment the whole chip sweeps one contiguous band
@@ -149,13 +160,14 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
                                                float *__restrict__ out_max, float *__restrict__ out_lp,
-                                               const uint32_t *__restrict__ mask, int mask_words) {
+                                               const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
     __shared__ ArgPart cand[16][MT];
     __shared__ ArgPart wbest[4][MT];
     __shared__ int s_last;
+    __shared__ int s_sel[MT];
     unsigned int *ticket = reinterpret_cast<unsigned int *>(ws + kLmTicket);
     float *row0 = reinterpret_cast<float *>(ws + kLmRow0);
     ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
@@ -318,6 +330,18 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         }
         // no mass (nothing allowed, or only -inf keys): not measured
         if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
+        s_sel[mm] = f.key > -INFINITY ? f.idx : 0;
+    }
+    if (emb.table != nullptr) {
+        __syncthreads();
+        for (int mm = 0; mm < m_rt; ++mm) {
+            const int id = s_sel[mm];
+            const bool in = id >= 0 && id < emb.vocab;
+            const uint4 *src = emb.table + (size_t)(in ? id : 0) * emb.units;
+            uint4 *dst = emb.out + (size_t)mm * emb.stride_units;
+            for (int u = threadIdx.x; u < emb.units; u += blockDim.x) dst[u] = in ? src[u] : make_uint4(0, 0, 0, 0);
+            if (threadIdx.x == 0 && emb.id_log != nullptr) emb.id_log[mm] = id;
+        }
     }
     if (threadIdx.x == 0) st_dev(ticket, 0u);   // ready for the next call
 }
@@ -401,33 +425,35 @@ static int lm_grid(K kernel, size_t lds, int ntiles) {
 
 template <int MT, int CPL, bool BK, bool LP>
 static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
-                             char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words) {
+                             char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words,
+                             const EmbedOut &emb) {
     auto kern = k_lmhead<MT, 2, 1, CPL, BK, LP>;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
     const int ntiles = (v + 31) / 32;
     hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales, w->global,
-                       v, w->k, ws, oi, om, olp, mask, mask_words);
+                       v, w->k, ws, oi, om, olp, mask, mask_words, emb);
 }
 
 // The LM head keeps KS = 1 and R = 2 (32-row tiles); there are at most
 // ceil(V / 32) partials.  A fixed chunk count when K = 2048.
 template <int MT>
 static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
-                           float *olp, const uint32_t *mask, int mask_words, bool bk, hipStream_t s) {
+                           float *olp, const uint32_t *mask, int mask_words, const EmbedOut &emb, bool bk,
+                           hipStream_t s) {
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
     ok();   // clears the message that a refused LDS request would leave
     if (tc.CPL == 4) {
-        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
-                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
-        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
-                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
+        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
+        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
     } else {
-        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
-                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
-        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words)
-                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words);
+        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
+        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
     }
     if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
     return check_launch("lmhead_gemv_argmax");
@@ -490,7 +516,8 @@ extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_ro
 
 static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
                          int32_t *out_idx, float *out_max, float *out_lp, const uint32_t *mask, int32_t mask_words,
-                         void *workspace, size_t ws_bytes, uint32_t flags, void *stream, const char *who) {
+                         const EmbedOut &emb, void *workspace, size_t ws_bytes, uint32_t flags, void *stream,
+                         const char *who) {
     int rc = validate_weight(w, who);
     if (rc) return rc;
     if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "%s: NULL h/out_idx/out_max", who);
@@ -512,26 +539,26 @@ static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *
     char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
     switch (mt) {
-        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
-        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
-        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
-        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, bk, s);
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
     }
 }
 
 extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
                                   int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
                                   uint32_t flags, void *stream) {
-    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, workspace, ws_bytes, flags,
-                         stream, "lmhead_gemv_argmax");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, workspace, ws_bytes,
+                         flags, stream, "lmhead_gemv_argmax");
 }
 
 extern "C" int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
                                           int32_t vocab_rows, int32_t *out_idx, float *out_max, float *out_logprob,
                                           void *workspace, size_t ws_bytes, uint32_t flags, void *stream) {
     if (!out_logprob) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_logprob: NULL out_logprob");
-    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, nullptr, 0, workspace, ws_bytes,
-                         flags, stream, "lmhead_gemv_argmax_logprob");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, nullptr, 0, EmbedOut{}, workspace,
+                         ws_bytes, flags, stream, "lmhead_gemv_argmax_logprob");
 }
 
 extern "C" int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
@@ -541,6 +568,30 @@ extern "C" int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, cons
     if (!allow_mask) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_masked: NULL allow_mask");
     if (mask_words < 0) return fail(NVFP4_ERR_ARG, "lmhead_gemv_argmax_masked: mask_words=%d < 0", mask_words);
     if (!aligned(allow_mask, 4)) return fail(NVFP4_ERR_ALIGN, "lmhead_gemv_argmax_masked: mask not 4-byte aligned");
-    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, allow_mask, mask_words, workspace,
-                         ws_bytes, flags, stream, "lmhead_gemv_argmax_masked");
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, allow_mask, mask_words, EmbedOut{},
+                         workspace, ws_bytes, flags, stream, "lmhead_gemv_argmax_masked");
+}
+
+extern "C" int lmhead_gemv_argmax_embed(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
+                                        const uint32_t *allow_mask, int32_t mask_words, int32_t *out_idx,
+                                        float *out_max, float *out_logprob, const uint16_t *table_bf16,
+                                        int32_t table_vocab, int32_t hidden, uint16_t *out_embed, int64_t out_stride,
+                                        int32_t *id_log, void *workspace, size_t ws_bytes, uint32_t flags,
+                                        void *stream) {
+    const char *who = "lmhead_gemv_argmax_embed";
+    if (!table_bf16 || !out_embed) return fail(NVFP4_ERR_ARG, "%s: NULL table or out_embed", who);
+    if (table_vocab < 1 || hidden < 8 || hidden % 8)
+        return fail(NVFP4_ERR_SHAPE, "%s: need table_vocab >= 1 and hidden %% 8 == 0 (vocab=%d hidden=%d)", who,
+                    table_vocab, hidden);
+    if (out_stride < hidden || out_stride % 8)
+        return fail(NVFP4_ERR_SHAPE, "%s: out_stride=%lld must be >= hidden and a multiple of 8", who,
+                    (long long)out_stride);
+    if (!aligned(table_bf16, 16) || !aligned(out_embed, 16) || (id_log && !aligned(id_log, 4)))
+        return fail(NVFP4_ERR_ALIGN, "%s: table/out_embed need 16-byte, id_log 4-byte alignment", who);
+    if (allow_mask && (mask_words < 0 || !aligned(allow_mask, 4)))
+        return fail(NVFP4_ERR_ARG, "%s: bad allow_mask (mask_words=%d)", who, mask_words);
+    const EmbedOut emb{reinterpret_cast<const uint4 *>(table_bf16), reinterpret_cast<uint4 *>(out_embed), id_log,
+                       out_stride / 8, table_vocab, hidden / 8};
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, allow_mask,
+                         allow_mask ? mask_words : 0, emb, workspace, ws_bytes, flags, stream, who);
 }

@@ -188,3 +188,92 @@ def test_chain_in_a_graph():
         chain(again)                                # eager work between replays
         torch.cuda.synchronize()
         assert again == eager
+
+
+@pytest.mark.parametrize("m,masked,logprob", [(1, False, False), (3, True, True), (8, False, True)])
+def test_argmax_embed_fused(orc, m, masked, logprob):
+    """lmhead_gemv_argmax_embed equals lmhead_gemv_argmax(_masked/_logprob)
+    followed by embed_from_argmax, bit for bit, and writes nothing else."""
+    import nvfp4_w4a16_mtp_amd as nv
+    v, k, hidden = 6000, 2048, 1024
+    rng = np.random.default_rng([80, m])
+    codes, scales, g = synth.quantized_domain_weight(rng, v, k)
+    wd = _w(codes, scales, np.float32(g * 300))
+    h = dev_bf16(synth.acts_bf16(81 + m, m, k))
+    table = dev_bf16(synth.acts_bf16(82, 7000, hidden))
+    mask = _dev_mask(_mask_bits(rng.random((m, v)) < 0.2)) if masked else None
+    if masked:
+        ri, rm, rlp = nv.lmhead_gemv_argmax_masked(h, wd, mask, with_logprob=True)
+    else:
+        ri, rm, rlp = nv.lmhead_gemv_argmax_logprob(h, wd)
+    ref_rows = nv.embed_from_argmax(ri, table)
+    buf = torch.full((m, hidden + 64), 5, dtype=torch.int16, device="cuda")
+    out = buf.view(torch.bfloat16)[:, 16:16 + hidden]
+    log = torch.full((m,), -1, dtype=torch.int32, device="cuda")
+    lp = torch.empty(m, dtype=torch.float32, device="cuda") if logprob else None
+    idx, mx = nv.lmhead_gemv_argmax_embed(h, wd, table, out, allow_mask=mask, id_log=log, out_logprob=lp)
+    assert np.array_equal(idx.cpu().numpy(), ri.cpu().numpy())
+    assert np.array_equal(mx.cpu().numpy().view(np.uint32), rm.cpu().numpy().view(np.uint32))
+    if logprob:
+        assert np.array_equal(lp.cpu().numpy().view(np.uint32), rlp.cpu().numpy().view(np.uint32))
+    host = buf.cpu().numpy()
+    assert np.array_equal(host[:, 16:16 + hidden].view(np.uint16), ref_rows.cpu().view(torch.int16).numpy().view(np.uint16))
+    assert (host[:, :16] == 5).all() and (host[:, 16 + hidden:] == 5).all()
+    assert np.array_equal(log.cpu().numpy(), ri.cpu().numpy())
+
+
+def test_fused_chain_in_a_graph():
+    """The chain of test_chain_in_a_graph with the gather fused into the LM
+    head gives the same draft ids on every replay."""
+    import nvfp4_w4a16_mtp_amd as nv
+    H, V, steps = 2048, 32768, 4
+    rng = np.random.default_rng(70)
+    lm = _w(*synth.quantized_domain_weight(rng, V, H))
+    fc_c, fc_s, fc_g = synth.quantized_domain_weight(rng, H, 2 * H)
+    fc = _w(fc_c, fc_s, np.float32(fc_g * 40))
+    table = dev_bf16(synth.acts_bf16(71, V, H))
+    h0 = dev_bf16(synth.acts_bf16(72, 1, H))
+    ws = nv.lmhead_workspace(1, V, "cuda")
+    xin = torch.empty((1, 2 * H), dtype=torch.bfloat16, device="cuda")
+    hcur = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(1, dtype=torch.int32, device="cuda")
+    mx = torch.empty(1, dtype=torch.float32, device="cuda")
+    log = torch.zeros(steps, dtype=torch.int32, device="cuda")
+
+    def unfused(readback):
+        hcur.copy_(h0)
+        for j in range(steps):
+            nv.lmhead_gemv_argmax(hcur, lm, workspace=ws, out_idx=idx, out_max=mx)
+            readback.append(int(idx.item()))
+            nv.embed_from_argmax(idx, table, out=xin[:, :H])
+            xin[:, H:].copy_(hcur)
+            nv.w4a16_gemv(xin, fc, out=hcur)
+
+    def fused():
+        hcur.copy_(h0)
+        for j in range(steps):
+            nv.lmhead_gemv_argmax_embed(hcur, lm, table, xin[:, :H], id_log=log[j:j + 1], workspace=ws, out_idx=idx,
+                                        out_max=mx)
+            xin[:, H:].copy_(hcur)
+            nv.w4a16_gemv(xin, fc, out=hcur)
+
+    eager = []
+    unfused(eager)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fused()
+        torch.cuda.synchronize()
+        assert log.cpu().numpy().tolist() == eager
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fused()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        log.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert log.cpu().numpy().tolist() == eager, rep
+        again = []
+        unfused(again)
+        torch.cuda.synchronize()
+        assert again == eager
