@@ -64,6 +64,10 @@ def lib():
         L.orc_lmhead_logprob.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32, P]
         L.orc_lmhead_masked.argtypes = [P, i64, P, P, f32, i64, i64, ctypes.c_uint32, P, i64, P, P, P]
         L.orc_embed_rows.argtypes = [P, i64, P, i64, i64, P]
+        L.orc_moe_layer.argtypes = [P, i64, P, P, f32, i64, i64, i64, i64,
+                                    P, P, P, P, P, P, P, P, P,
+                                    P, P, f32, P, P, f32, P, P, f32, i64,
+                                    P, P, P, P, P]
         L.orc_moe.argtypes = [P, i64, P, i64, i64, i64, i64,
                               P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -253,3 +257,34 @@ def moe(x_bf16, router, topk, gate, up, down):
     lib().orc_moe(_p(x), m, _p(router), E, topk, H, I, _p(gc), _p(gs), _p(gd), _p(uc), _p(us),
                   _p(ud), _p(dc), _p(ds), _p(dd), _p(y), _p(ids), _p(w))
     return y, ids, w
+
+
+def moe_layer(x_bf16, router, topk, gate, up, down, shared, sgate_bf16=None):
+    """The complete MoE layer: router (codes [E, H/2], scales [E, H/16], g_dec)
+    -> logits; routed experts gate/up/down as in moe(); shared = (gate, up,
+    down), each (codes, scales, g_dec); sgate_bf16: bf16 bits [H] or None.
+    Returns (y, ids, wts, logits)."""
+    x = _c(x_bf16, np.uint16)
+    m, H = x.shape
+    rc, rs, rd = _c(router[0], np.uint8), _c(router[1], np.uint8), float(router[2])
+    E = rc.shape[0]
+    gc, gs, gd = (_c(gate[0], np.uint8), _c(gate[1], np.uint8), _c(gate[2], np.float32))
+    uc, us, ud = (_c(up[0], np.uint8), _c(up[1], np.uint8), _c(up[2], np.float32))
+    dc, ds, dd = (_c(down[0], np.uint8), _c(down[1], np.uint8), _c(down[2], np.float32))
+    I = gc.shape[1]
+    (sgc, sgs, sgd), (suc, sus, sud), (sdc, sds, sdd) = shared
+    sgc, sgs, suc, sus = (_c(a, np.uint8) for a in (sgc, sgs, suc, sus))
+    sdc, sds = _c(sdc, np.uint8), _c(sds, np.uint8)
+    Is = sgc.shape[0]
+    assert rc.shape == (E, H // 2) and sgc.shape == (Is, H // 2) and sdc.shape == (H, Is // 2)
+    sg = None if sgate_bf16 is None else _c(sgate_bf16, np.uint16)
+    y = np.zeros((m, H), np.float32)
+    ids = np.zeros((m, topk), np.int32)
+    wts = np.zeros((m, topk), np.float32)
+    logits = np.zeros((m, E), np.float32)
+    lib().orc_moe_layer(_p(x), m, _p(rc), _p(rs), rd, E, topk, H, I,
+                        _p(gc), _p(gs), _p(gd), _p(uc), _p(us), _p(ud), _p(dc), _p(ds), _p(dd),
+                        _p(sgc), _p(sgs), float(sgd), _p(suc), _p(sus), float(sud), _p(sdc), _p(sds), float(sdd), Is,
+                        _p(sg), _p(y), _p(ids), _p(wts), _p(logits))
+    return y, ids, wts, logits
+

@@ -456,3 +456,52 @@ ORC_API void orc_moe(const uint16_t *x, int64_t m, const float *router, int64_t 
     }
     free(g); free(u); free(a); free(acc); free(taken);
 }
+
+/* ------------------------------------------------------------------ */
+/* The complete MoE layer of the draft head ([new.rs] `MtpHead::new`: the
+ * router `moe_gate` quantized to NVFP4 next to the routed experts, a shared
+ * expert (gate/up/down, NVFP4) and its `shared_expert_gate`, combined by
+ * `moe_weighted_sum_blend`):
+ *   logits = router x (fp32, the NVFP4 GEMV of orc_gemv);
+ *   y      = routed MoE of orc_moe on those logits
+ *            + sigmoid(sgate . x) * shared(x),
+ *   shared(x) = down_s(bf16(silu(gate_s x) * up_s x)),
+ * with sgate a bf16 vector of H (the gate weight kept in bf16); sgate NULL
+ * means an ungated shared expert (factor 1).  The routed part is rounded
+ * to fp32 by orc_moe before the shared term is added in fp64.            */
+/* ------------------------------------------------------------------ */
+ORC_API void orc_moe_layer(const uint16_t *x, int64_t m, const uint8_t *rc, const uint8_t *rs, float rdec,
+                           int64_t E, int64_t topk, int64_t H, int64_t I,
+                           const uint8_t *gc, const uint8_t *gs, const float *gdec,
+                           const uint8_t *uc, const uint8_t *us, const float *udec,
+                           const uint8_t *dc, const uint8_t *ds, const float *ddec,
+                           const uint8_t *sgc, const uint8_t *sgs, float sgdec,
+                           const uint8_t *suc, const uint8_t *sus, float sudec,
+                           const uint8_t *sdc, const uint8_t *sds, float sddec, int64_t Is,
+                           const uint16_t *sgate, float *y, int32_t *ids, float *wts, float *logits) {
+    orc_gemv(x, m, rc, rs, rdec, E, H, logits);
+    orc_moe(x, m, logits, E, topk, H, I, gc, gs, gdec, uc, us, udec, dc, ds, ddec, y, ids, wts);
+    float *g = (float *)malloc(sizeof(float) * Is);
+    float *u = (float *)malloc(sizeof(float) * Is);
+    uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * Is);
+    for (int64_t t = 0; t < m; ++t) {
+        const uint16_t *xt = x + t * H;
+        double sg = 1.0;
+        if (sgate) {
+            double z = 0.0;
+            for (int64_t h = 0; h < H; ++h) z += (double)bf16_to_f32(sgate[h]) * (double)bf16_to_f32(xt[h]);
+            sg = 1.0 / (1.0 + exp(-z));
+        }
+        orc_gemv(xt, 1, sgc, sgs, sgdec, Is, H, g);
+        orc_gemv(xt, 1, suc, sus, sudec, Is, H, u);
+        for (int64_t i = 0; i < Is; ++i) {
+            double gi = g[i];
+            a[i] = f32_to_bf16_rne((float)(gi / (1.0 + exp(-gi)) * (double)u[i]));
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            float d = (float)((double)sddec * dot_row(a, sdc + h * (Is / 2), sds + h * (Is / 16), Is));
+            y[t * H + h] = (float)((double)y[t * H + h] + sg * (double)d);
+        }
+    }
+    free(g); free(u); free(a);
+}
