@@ -301,6 +301,36 @@ int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits
                    int32_t top_k, const nvfp4_moe_weights *e, float *y, int32_t *topk_ids,
                    float *topk_w, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * moe_layer_w4a16 -- the complete MoE layer of the draft head: the NVFP4
+ * router (`moe_gate`, quantized next to the experts in [new.rs]
+ * `MtpHead::new`), the routed experts of moe_w4a16_gemv and the shared
+ * expert with its sigmoid `shared_expert_gate`, blended as the pages'
+ * `moe_weighted_sum_blend`:
+ *   router_logits = router x  (fp32 out [m][E]),
+ *   y = sum_j w[j] * down_e(j)(a_j) + sigmoid(g . x) * down_s(a_s),
+ *   a_s = bf16(silu(gate_s x) * up_s x),
+ * with g = shared_gate_w_bf16 ([H] bf16) or, when it is NULL, a factor 1.
+ *   router        [E][H] NVFP4 (n = num_experts, k = hidden).
+ *   shared_gate, shared_up   [I][H] NVFP4; shared_down [H][I] NVFP4 (the
+ *                 routed experts' width I).
+ *   y, topk_ids, topk_w      as moe_w4a16_gemv.
+ *   workspace     at least moe_layer_w4a16_workspace_bytes(m, top_k, e),
+ *                 256-byte aligned, zero-filled before its first use.
+ * Three launches: one grouped GEMV (router, shared gate, shared up), the
+ * routing with the routed gate/up and the shared activations, and the down
+ * pass over the routed experts and the shared one.  Requires, besides the
+ * limits of moe_w4a16_gemv, (m * top_k + m) * I * 2 <= 153600 bytes (the
+ * activation rows the down pass keeps in LDS); NVFP4_ERR_UNSUPPORTED
+ * otherwise.
+ */
+size_t moe_layer_w4a16_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
+int moe_layer_w4a16(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *router, int32_t top_k,
+                    const nvfp4_moe_weights *e, const nvfp4_weight *shared_gate,
+                    const nvfp4_weight *shared_up, const nvfp4_weight *shared_down,
+                    const uint16_t *shared_gate_w_bf16, float *y, int32_t *topk_ids, float *topk_w,
+                    float *router_logits, void *workspace, size_t ws_bytes, void *stream);
+
 /* Message of the last failing call on this host thread ("" if none); the
  * pointer stays valid until the next call on the same thread. */
 const char *nvfp4_mtp_last_error(void);

@@ -71,10 +71,13 @@ def lib():
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
+        L.moe_layer_w4a16_workspace_bytes.argtypes = [i32, i32, EP]
+        L.moe_layer_w4a16_workspace_bytes.restype = sz
+        L.moe_layer_w4a16.argtypes = [P, i32, WP, i32, EP, WP, WP, WP, P, P, P, P, P, P, sz, P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
-                  "moe_w4a16_gemv"):
+                  "moe_w4a16_gemv", "moe_layer_w4a16"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -403,3 +406,42 @@ def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, exp
                                 _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x)),
            "moe_w4a16_gemv")
     return out, topk_ids, topk_w
+
+
+def moe_layer_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:
+    """Zero-filled workspace for moe_layer_w4a16."""
+    d = experts.desc()
+    nbytes = lib().moe_layer_w4a16_workspace_bytes(m, top_k, ctypes.byref(d))
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_layer_w4a16(x: torch.Tensor, router: NVFP4Weight, top_k: int, experts: NVFP4Experts,
+                    shared_gate: NVFP4Weight, shared_up: NVFP4Weight, shared_down: NVFP4Weight,
+                    shared_gate_w: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, topk_ids: torch.Tensor | None = None,
+                    topk_w: torch.Tensor | None = None, router_logits: torch.Tensor | None = None):
+    """The complete MoE layer; returns (y, topk_ids, topk_w, router_logits)."""
+    x = _as_bf16(x)
+    _dev(x, "x")
+    m = x.shape[0]
+    dev = x.device
+    if workspace is None:
+        workspace = moe_layer_workspace(m, top_k, experts, dev)
+    if out is None:
+        out = torch.empty((m, experts.hidden), dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((m, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((m, top_k), dtype=torch.float32, device=dev)
+    if router_logits is None:
+        router_logits = torch.empty((m, experts.num_experts), dtype=torch.float32, device=dev)
+    if shared_gate_w is not None:
+        shared_gate_w = _as_bf16(shared_gate_w).contiguous()
+    ds = [w.desc() for w in (router, shared_gate, shared_up, shared_down)]
+    d = experts.desc()
+    _check(lib().moe_layer_w4a16(_ptr(x), m, ctypes.byref(ds[0]), top_k, ctypes.byref(d), ctypes.byref(ds[1]),
+                                 ctypes.byref(ds[2]), ctypes.byref(ds[3]), _ptr(shared_gate_w), _ptr(out),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(router_logits), _ptr(workspace),
+                                 workspace.numel(), _stream(x)), "moe_layer_w4a16")
+    return out, topk_ids, topk_w, router_logits
+

@@ -57,6 +57,19 @@ struct MoeRoute {
 };
 static_assert(sizeof(MoeRoute) <= kMoeHeader, "route header");
 
+// The shared expert of the complete MoE layer (all pointers device memory;
+// on == 0 for the routed-only entry point).  Its gate and up outputs come
+// from the grouped GEMV that also produces the router logits.
+struct MoeShared {
+    const float *sg, *su;           // gate / up outputs, fp32 [m][I]
+    uint16_t *sact;                 // its activations, bf16 [m][I]
+    const uint16_t *gate_w;         // shared_expert_gate, bf16 [H], or nullptr (ungated)
+    float *sgate;                   // sigmoid(gate_w . x_t), fp32 [m] (1 when ungated)
+    const uint8_t *dcodes, *dscales;
+    const nvfp4_global *dglob;      // its down projection [H][I]
+    int on;
+};
+
 // Sum over the wavefront in a fixed order; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float v) {
     v = row16_sum(v);
@@ -266,13 +279,37 @@ template <int CPL>
 __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                     int m, int E, int topk, nvfp4_moe_weights e,
                                                     int32_t *__restrict__ ids, float *__restrict__ wts,
-                                                    MoeRoute *__restrict__ route, uint16_t *__restrict__ act) {
+                                                    MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
+                                                    MoeShared sh) {
     extern __shared__ uint4 smem[];
     RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // reused for the activations afterwards
     __shared__ int tok[8], prs[8];
     __shared__ int s_ex, s_cnt, s_nd;
-    moe_route_lds(logits, m, E, topk, L);
     const int u = blockIdx.y;
+    // shared expert: the workgroups of the first expert column form 16 of its
+    // activations per token each (loads issued before the routing, stored after)
+    const int I = e.inter, H = e.hidden;
+    const int si = blockIdx.x * kMoeRows + (threadIdx.x & 15), st = threadIdx.x >> 4;
+    const bool s_act = sh.on && u == 0 && st < m && si < I;
+    float sgv = 0.0f, suv = 0.0f;
+    if (s_act) {
+        sgv = sh.sg[(size_t)st * I + si];
+        suv = sh.su[(size_t)st * I + si];
+    }
+    moe_route_lds(logits, m, E, topk, L);
+    if (s_act) sh.sact[(size_t)st * I + si] = (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv);
+    // shared_expert_gate: the last workgroup of the first column, one wavefront per token
+    if (sh.on && u == 0 && blockIdx.x == gridDim.x - 1) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        for (int t = wave; t < m; t += 4) {
+            float z = 0.0f;
+            if (sh.gate_w != nullptr)
+                for (int h = lane; h < H; h += 64)
+                    z = __builtin_fmaf(bf16_bits_to_f32(sh.gate_w[h]), bf16_bits_to_f32(x[(size_t)t * H + h]), z);
+            z = wave_sum(z);
+            if (lane == 0) sh.sgate[t] = sh.gate_w != nullptr ? 1.0f / (1.0f + expf(-z)) : 1.0f;
+        }
+    }
     if (blockIdx.x == 0 && u == 0) {
         for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
             ids[p] = L.sel_i[p / topk][p % topk];
@@ -313,7 +350,6 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
     __syncthreads();   // the routing scratch is free from here on
     if (u >= s_nd) return;
     const int ex = s_ex, cnt = s_cnt;
-    const int H = e.hidden, I = e.inter;
     const size_t wsz = (size_t)I * H;
     const uint8_t *gc = e.gate_codes + (size_t)ex * (wsz / 2), *gs = e.gate_scales + (size_t)ex * (wsz / 16);
     const uint8_t *uc = e.up_codes + (size_t)ex * (wsz / 2), *us = e.up_scales + (size_t)ex * (wsz / 16);
@@ -396,30 +432,48 @@ __global__ __launch_bounds__(256) void k_moe_down(nvfp4_moe_weights e, int m, in
 // token in ascending expert order.  No scratch buffer, no ticket, one pass.
 constexpr int kDownRows = 8;
 constexpr int kDownBatch = 4;   // items per slot in flight
+constexpr int kDownMaxExperts = 129;   // routed (<= 128) + the shared one
+constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the shared expert
 
 template <int CPL>
 __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
                                                       const float *__restrict__ wts, const MoeRoute *__restrict__ route,
-                                                      const uint16_t *__restrict__ act, float *__restrict__ y) {
+                                                      const uint16_t *__restrict__ act, float *__restrict__ y,
+                                                      MoeShared sh) {
     extern __shared__ uint4 smem[];
-    __shared__ int s_ex[128], s_pb[129];
-    __shared__ float s_dec[128], s_w[128];
-    __shared__ int s_tok[128], s_pair[128];
-    __shared__ float contrib[128][kDownRows];
+    __shared__ int s_ex[kDownMaxExperts], s_pb[kDownMaxExperts + 1];
+    __shared__ float s_dec[kDownMaxExperts], s_w[kDownMaxPos];
+    __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
+    __shared__ float contrib[kDownMaxPos][kDownRows];
     const int H = e.hidden, I = e.inter, C = I >> 5;
-    // the plan in LDS, one round of loads
-    const int nd = route->n_distinct, P = route->n_pairs;
-    for (int i = threadIdx.x; i <= nd; i += blockDim.x) {
+    // the plan in LDS, one round of loads; with a shared expert it follows
+    // the routed ones as expert nd (id -1), its m positions after the pairs,
+    // weighted by the shared gate, activation rows from sh.sact
+    const int nr = route->n_distinct, P0 = route->n_pairs;
+    const int nd = nr + (sh.on ? 1 : 0), P = P0 + (sh.on ? m : 0);
+    for (int i = threadIdx.x; i <= nr; i += blockDim.x) {
         s_pb[i] = route->pb[i];
-        if (i < nd) {
+        if (i < nr) {
             s_ex[i] = route->ex_id[i];
             s_dec[i] = route->ddec[i];
         }
     }
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    for (int i = threadIdx.x; i < P0; i += blockDim.x) {
         s_tok[i] = route->pos_tok[i];
         s_pair[i] = route->pos_pair[i];
         s_w[i] = route->pos_w[i];
+    }
+    if (sh.on) {
+        if (threadIdx.x == 0) {
+            s_ex[nr] = -1;
+            s_dec[nr] = sh.dglob->dec;
+            s_pb[nr + 1] = P;
+        }
+        if (threadIdx.x < m) {
+            s_tok[P0 + threadIdx.x] = threadIdx.x;
+            s_pair[P0 + threadIdx.x] = threadIdx.x;   // row of sh.sact
+            s_w[P0 + threadIdx.x] = sh.sgate[threadIdx.x];
+        }
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tl = lane & 15;
@@ -438,8 +492,10 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
             // results are never used
             const int it = min(b0 + sl + 16 * n, nitems - 1);
             const int u = it / kDownRows, row = min(r0 + it % kDownRows, H - 1);
-            const uint8_t *dc = e.down_codes + (size_t)s_ex[u] * (wsz / 2) + (size_t)row * (I / 2);
-            const uint8_t *ds = e.down_scales + (size_t)s_ex[u] * (wsz / 16) + (size_t)row * (I / 16);
+            const bool shared_row = s_ex[u] < 0;
+            const uint8_t *dc = (shared_row ? sh.dcodes : e.down_codes + (size_t)s_ex[u] * (wsz / 2)) + (size_t)row * (I / 2);
+            const uint8_t *ds = (shared_row ? sh.dscales : e.down_scales + (size_t)s_ex[u] * (wsz / 16)) +
+                                (size_t)row * (I / 16);
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = tl + 16 * j;
@@ -449,7 +505,8 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
         }
         __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any arithmetic
         if (b0 == 0) {
-            stage_rows(smem, act, s_pair, P, P, I);   // row pos of the image = pair position pos
+            stage_rows(smem, act, s_pair, P0, P0, I);   // row pos of the image = pair position pos
+            if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
             __syncthreads();
         }
 #pragma unroll
@@ -495,9 +552,13 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
 }
 
 template <int CPL>
-static void launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk,
-                             const float *wts, const MoeRoute *route, const uint16_t *act, float *y) {
-    hipLaunchKernelGGL(k_moe_down_rows<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, y);
+static int launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk,
+                            const float *wts, const MoeRoute *route, const uint16_t *act, float *y,
+                            const MoeShared &sh) {
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_down_rows<CPL>), lds, "moe_w4a16_gemv");
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_moe_down_rows<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, y, sh);
+    return check_launch("moe_w4a16_gemv(down)");
 }
 
 struct MoeLayout {
@@ -516,10 +577,10 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
 template <int CPL>
 static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
-                          uint16_t *act) {
+                          uint16_t *act, const MoeShared &sh) {
     const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL>), lds, "moe_w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act);
+    hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act, sh);
     return check_launch("moe_w4a16_gemv(gate_up)");
 }
 template <int CPL>
@@ -546,70 +607,156 @@ extern "C" size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const
     return moe_layout(m, top_k, e->hidden, e->inter).total;
 }
 
-extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits, int32_t top_k,
-                              const nvfp4_moe_weights *e, float *y, int32_t *topk_ids, float *topk_w, void *workspace,
-                              size_t ws_bytes, void *stream) {
-    if (!e) return fail(NVFP4_ERR_ARG, "moe_w4a16_gemv: NULL expert descriptor");
-    if (!x_bf16 || !router_logits || !y || !topk_ids || !topk_w)
-        return fail(NVFP4_ERR_ARG, "moe_w4a16_gemv: NULL x/router_logits/y/topk_ids/topk_w");
+// Checks shared by the routed MoE and the complete layer.
+static int moe_validate(const uint16_t *x_bf16, int32_t m, int32_t top_k, const nvfp4_moe_weights *e, const float *y,
+                        const int32_t *topk_ids, const float *topk_w, const char *who) {
+    if (!e) return fail(NVFP4_ERR_ARG, "%s: NULL expert descriptor", who);
+    if (!x_bf16 || !y || !topk_ids || !topk_w) return fail(NVFP4_ERR_ARG, "%s: NULL x/y/topk_ids/topk_w", who);
     if (!e->gate_codes || !e->gate_scales || !e->gate_global || !e->up_codes || !e->up_scales || !e->up_global ||
         !e->down_codes || !e->down_scales || !e->down_global)
-        return fail(NVFP4_ERR_ARG, "moe_w4a16_gemv: NULL expert weight pointer");
-    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: m=%d outside 1..8", m);
+        return fail(NVFP4_ERR_ARG, "%s: NULL expert weight pointer", who);
+    if (m < 1 || m > 8) return fail(NVFP4_ERR_SHAPE, "%s: m=%d outside 1..8", who, m);
     const int E = e->num_experts, H = e->hidden, I = e->inter;
-    if (E < 1 || E > kMoeMaxExperts)
-        return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: num_experts=%d outside 1..%d", E, kMoeMaxExperts);
+    if (E < 1 || E > kMoeMaxExperts) return fail(NVFP4_ERR_SHAPE, "%s: num_experts=%d outside 1..%d", who, E, kMoeMaxExperts);
     if (top_k < 1 || top_k > kMoeMaxTopK || top_k > E)
-        return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: top_k=%d outside 1..min(E, %d)", top_k, kMoeMaxTopK);
-    if (H < 32 || I < 32 || H % 32 || I % 32)
-        return fail(NVFP4_ERR_SHAPE, "moe_w4a16_gemv: hidden/inter must be multiples of 32");
+        return fail(NVFP4_ERR_SHAPE, "%s: top_k=%d outside 1..min(E, %d)", who, top_k, kMoeMaxTopK);
+    if (H < 32 || I < 32 || H % 32 || I % 32) return fail(NVFP4_ERR_SHAPE, "%s: hidden/inter must be multiples of 32", who);
     // an expert serves at most m tokens: its activation rows are staged for
     // round_up(m) of them (up to 160 KiB of LDS per workgroup)
     const int mt = round_up_mt(m);
     if ((size_t)mt * H * 2 > kMoeMaxLds || (size_t)mt * I * 2 > kMoeMaxLds)
-        return fail(NVFP4_ERR_UNSUPPORTED, "moe_w4a16_gemv: %d rows x hidden %d / inter %d exceed the LDS", mt, H, I);
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d rows x hidden %d / inter %d exceed the LDS", who, mt, H, I);
     if (!aligned(x_bf16, 16) || !aligned(e->gate_codes, 16) || !aligned(e->up_codes, 16) || !aligned(e->down_codes, 16))
-        return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: x and codes need 16-byte alignment");
-    if (!aligned(e->gate_scales, 2) || !aligned(e->up_scales, 2) || !aligned(e->down_scales, 2) ||
-        !aligned(router_logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
-        return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: scales 2-byte, logits/outputs 4-byte alignment");
-    const MoeLayout L = moe_layout(m, top_k, H, I);
-    if (!workspace || ws_bytes < L.total)
-        return fail(NVFP4_ERR_WORKSPACE, "moe_w4a16_gemv: workspace needs %zu bytes", L.total);
-    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: workspace not 256-byte aligned");
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    char *ws = reinterpret_cast<char *>(workspace);
+        return fail(NVFP4_ERR_ALIGN, "%s: x and codes need 16-byte alignment", who);
+    if (!aligned(e->gate_scales, 2) || !aligned(e->up_scales, 2) || !aligned(e->down_scales, 2) || !aligned(y, 4) ||
+        !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+        return fail(NVFP4_ERR_ALIGN, "%s: scales 2-byte, outputs 4-byte alignment", who);
+    return NVFP4_OK;
+}
+
+// Routing + gate/up, then the down pass (row-owner when the activation rows
+// fit in LDS -- always with a shared expert -- else the ticket pass).
+static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_logits, int32_t top_k,
+                      const nvfp4_moe_weights *e, float *y, int32_t *topk_ids, float *topk_w, char *ws,
+                      const MoeLayout &L, const MoeShared &sh, hipStream_t s) {
     MoeRoute *route = reinterpret_cast<MoeRoute *>(ws);
     unsigned int *tickets = reinterpret_cast<unsigned int *>(ws + L.tickets);
     uint16_t *act = reinterpret_cast<uint16_t *>(ws + L.act);
     float *dbuf = reinterpret_cast<float *>(ws + L.dbuf);
+    const int E = e->num_experts, H = e->hidden, I = e->inter, mt = round_up_mt(m);
     const int maxd = min(E, m * top_k);
     const nvfp4_moe_weights ev = *e;
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kMoeRows - 1) / kMoeRows, maxd);
     const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
     int rc;
     switch (cpl_for(H)) {
-        case 1: rc = launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        case 2: rc = launch_gate_up<2>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        case 4: rc = launch_gate_up<4>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
-        default: rc = launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act); break;
+        case 1: rc = launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
+        case 2: rc = launch_gate_up<2>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
+        case 4: rc = launch_gate_up<4>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
+        default: rc = launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
     }
     if (rc) return rc;
-    const size_t pairs = (size_t)m * top_k;
-    if (pairs <= 128 && pairs * I * 2 <= (size_t)kLdsBytes - 16384 && cpl_for(I) != 0) {
+    const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
+    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows
+    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : (size_t)kLdsBytes - 16384;
+    if (pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0) {
         const dim3 g3((H + kDownRows - 1) / kDownRows);
-        const size_t lds3 = pairs * I * 2;
+        const size_t lds3 = pos * I * 2;
         switch (cpl_for(I)) {
-            case 1: launch_down_rows<1>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
-            case 2: launch_down_rows<2>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
-            default: launch_down_rows<4>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y); break;
+            case 1: return launch_down_rows<1>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y, sh);
+            case 2: return launch_down_rows<2>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y, sh);
+            default: return launch_down_rows<4>(g3, lds3, s, ev, m, top_k, topk_w, route, act, y, sh);
         }
-        return check_launch("moe_w4a16_gemv(down)");
     }
+    if (sh.on) return fail(NVFP4_ERR_UNSUPPORTED, "moe_layer_w4a16: %zu activation rows of inter %d exceed the LDS", pos, I);
     switch (cpl_for(I)) {
         case 1: return launch_down<1>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
         case 2: return launch_down<2>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
         case 4: return launch_down<4>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
         default: return launch_down<0>(g2, lds2, s, ev, m, top_k, topk_w, route, act, dbuf, tickets, y);
     }
+}
+
+extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits, int32_t top_k,
+                              const nvfp4_moe_weights *e, float *y, int32_t *topk_ids, float *topk_w, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    int rc = moe_validate(x_bf16, m, top_k, e, y, topk_ids, topk_w, "moe_w4a16_gemv");
+    if (rc) return rc;
+    if (!router_logits) return fail(NVFP4_ERR_ARG, "moe_w4a16_gemv: NULL router_logits");
+    if (!aligned(router_logits, 4)) return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: router_logits not 4-byte aligned");
+    const MoeLayout L = moe_layout(m, top_k, e->hidden, e->inter);
+    if (!workspace || ws_bytes < L.total)
+        return fail(NVFP4_ERR_WORKSPACE, "moe_w4a16_gemv: workspace needs %zu bytes", L.total);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: workspace not 256-byte aligned");
+    return moe_launch(x_bf16, m, router_logits, top_k, e, y, topk_ids, topk_w, reinterpret_cast<char *>(workspace), L,
+                      MoeShared{}, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Workspace of the complete layer: the routed MoE's, then the shared
+// expert's gate and up outputs (fp32), its activations (bf16) and the gate
+// values (fp32), each 256-byte aligned.
+struct LayerLayout {
+    MoeLayout moe;
+    size_t sg, su, sact, sgate, total;
+};
+static LayerLayout layer_layout(int m, int topk, int H, int I) {
+    LayerLayout L;
+    L.moe = moe_layout(m, topk, H, I);
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    L.sg = up(L.moe.total);
+    L.su = L.sg + up((size_t)m * I * 4);
+    L.sact = L.su + up((size_t)m * I * 4);
+    L.sgate = L.sact + up((size_t)m * I * 2);
+    L.total = L.sgate + 256;
+    return L;
+}
+
+extern "C" size_t moe_layer_w4a16_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e) {
+    if (!e || m < 1 || top_k < 1 || e->hidden < 1 || e->inter < 1) return 0;
+    return layer_layout(m, top_k, e->hidden, e->inter).total;
+}
+
+extern "C" int moe_layer_w4a16(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *router, int32_t top_k,
+                               const nvfp4_moe_weights *e, const nvfp4_weight *shared_gate,
+                               const nvfp4_weight *shared_up, const nvfp4_weight *shared_down,
+                               const uint16_t *shared_gate_w_bf16, float *y, int32_t *topk_ids, float *topk_w,
+                               float *router_logits, void *workspace, size_t ws_bytes, void *stream) {
+    const char *who = "moe_layer_w4a16";
+    int rc = moe_validate(x_bf16, m, top_k, e, y, topk_ids, topk_w, who);
+    if (rc) return rc;
+    const int E = e->num_experts, H = e->hidden, I = e->inter;
+    for (const nvfp4_weight *w : {router, shared_gate, shared_up, shared_down}) {
+        rc = validate_weight(w, who);
+        if (rc) return rc;
+    }
+    if (router->n != E || router->k != H)
+        return fail(NVFP4_ERR_SHAPE, "%s: router is %dx%d, need %dx%d", who, router->n, router->k, E, H);
+    if (shared_gate->n != I || shared_gate->k != H || shared_up->n != I || shared_up->k != H || shared_down->n != H ||
+        shared_down->k != I)
+        return fail(NVFP4_ERR_SHAPE, "%s: the shared expert must be gate/up %dx%d and down %dx%d", who, I, H, H, I);
+    if (!router_logits || !aligned(router_logits, 4))
+        return fail(NVFP4_ERR_ARG, "%s: router_logits must be a 4-byte aligned device buffer", who);
+    const LayerLayout L = layer_layout(m, top_k, H, I);
+    if (!workspace || ws_bytes < L.total) return fail(NVFP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, L.total);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "%s: workspace not 256-byte aligned", who);
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *sg = reinterpret_cast<float *>(ws + L.sg), *su = reinterpret_cast<float *>(ws + L.su);
+    // 1. router logits and the shared expert's gate and up: one grouped GEMV
+    const nvfp4_weight *ws3[3] = {router, shared_gate, shared_up};
+    void *ys3[3] = {router_logits, sg, su};
+    rc = w4a16_gemv_grouped(x_bf16, m, ws3, ys3, 3, NVFP4_OUT_F32, stream);
+    if (rc) return rc;
+    // 2-3. routed experts with the shared expert folded into the down pass
+    MoeShared sh{};
+    sh.sg = sg;
+    sh.su = su;
+    sh.sact = reinterpret_cast<uint16_t *>(ws + L.sact);
+    sh.gate_w = shared_gate_w_bf16;
+    sh.sgate = reinterpret_cast<float *>(ws + L.sgate);
+    sh.dcodes = shared_down->codes;
+    sh.dscales = shared_down->scales;
+    sh.dglob = shared_down->global;
+    sh.on = 1;
+    return moe_launch(x_bf16, m, router_logits, top_k, e, y, topk_ids, topk_w, ws, L.moe, sh,
+                      reinterpret_cast<hipStream_t>(stream));
 }
