@@ -338,6 +338,22 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
     ms = _time_graph(torch, lambda i: nv.moe_w4a16_gemv(xm, router, TOPK, copies[i % NCOPIES]["moe"], workspace=ws, out=ymo,
                                                         topk_ids=ids, topk_w=wts), reps, s)
     out["moe"] = {"ms": round(ms, 5)}
+    # the complete MoE layer: NVFP4 router + routed experts + gated shared expert
+    gen2 = torch.Generator(device=hl.device)
+    gen2.manual_seed(2)
+
+    def qw(n, k):
+        return nv.nvfp4_quantize((torch.randn((n, k), generator=gen2, device=hl.device) * 0.02).to(torch.bfloat16))
+    lay = [(qw(E, H), qw(I, H), qw(I, H), qw(H, I)) for _ in range(NCOPIES)]
+    sgw = (torch.randn(H, generator=gen2, device=hl.device) * 0.02).to(torch.bfloat16)
+    lws = nv.moe_layer_workspace(M, TOPK, copies[0]["moe"], hl.device)
+    rl = torch.empty((M, E), dtype=torch.float32, device=hl.device)
+    ms = _time_graph(torch, lambda i: nv.moe_layer_w4a16(xm, lay[i % NCOPIES][0], TOPK, copies[i % NCOPIES]["moe"],
+                                                         *lay[i % NCOPIES][1:], shared_gate_w=sgw, workspace=lws,
+                                                         out=ymo, topk_ids=ids, topk_w=wts, router_logits=rl), reps, s)
+    nvfp4_lay = nvfp4_bytes(E, H) + 3 * nvfp4_bytes(I, H)
+    out["moe_layer_router_shared"] = {"ms": round(ms, 5), "extra_weight_bytes": nvfp4_lay}
+    del lay
     # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120) at M = 1024
     gen = torch.Generator(device=hl.device)
     gen.manual_seed(1)
