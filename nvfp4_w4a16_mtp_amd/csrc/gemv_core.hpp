@@ -276,8 +276,62 @@ __device__ __forceinline__ void gemv_tile_compute_x1(const TileRegs<1, R, KS, CP
     gemv_tile_finish<1, R, KS, CPL>(acc, n, row0, red, epi);
 }
 
-// Generic shape (any K % 32 == 0): loop over the lane's chunks.
-template <int MT, int R, int KS, class Epi>
+// One stage of the pipelined loop: chunks c0, c0 + 16, ... of the slot's R
+// rows, the first `left` of them (a stage count that is the same in every
+// lane keeps the branch uniform).
+template <int U, int R>
+__device__ __forceinline__ void stage_load(uint4 (&cw)[U][R], uint32_t (&sw)[U][R], const uint8_t *const (&cp)[R],
+                                           const uint8_t *const (&sp)[R], int c0, int left) {
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+        if (q < left) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                cw[q][r] = ld_stream16(cp[r] + 16 * (size_t)(c0 + 16 * q));
+                sw[q][r] = ld_stream2(sp[r] + 2 * (size_t)(c0 + 16 * q));
+            }
+        }
+    }
+}
+
+template <int MT, int U, int R>
+__device__ __forceinline__ void stage_fma(const uint4 (&cw)[U][R], const uint32_t (&sw)[U][R], const uint4 *xs, int C,
+                                          int c0, int left, float (&acc)[R][MT]) {
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+        if (q < left) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[q][r], sw[q][r], xs, C, c0 + 16 * q, acc[r]);
+        }
+    }
+}
+
+// R rows (code and scale row pointers cp, sp) against the activation image,
+// for a lane that owns chunks tl, tl + 16, ... of C (C % 16 == 0): stages of
+// U chunks, the loads of stage s + 1 in flight while stage s is computed.
+template <int MT, int R, int U>
+__device__ __forceinline__ void pipe_rows(const uint4 *xs, const uint8_t *const (&cp)[R], const uint8_t *const (&sp)[R],
+                                          int C, int tl, float (&acc)[R][MT]) {
+    const int nc = C >> 4;
+    const int ns = (nc + U - 1) / U;
+    uint4 ca[U][R], cb[U][R];
+    uint32_t sa[U][R], sb[U][R];
+    stage_load<U, R>(ca, sa, cp, sp, tl, nc);
+    for (int st = 0; st < ns; st += 2) {
+        if (st + 1 < ns) stage_load<U, R>(cb, sb, cp, sp, tl + 16 * U * (st + 1), nc - U * (st + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        stage_fma<MT, U, R>(ca, sa, xs, C, tl + 16 * U * st, nc - U * st, acc);
+        if (st + 1 >= ns) break;
+        if (st + 2 < ns) stage_load<U, R>(ca, sa, cp, sp, tl + 16 * U * (st + 2), nc - U * (st + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        stage_fma<MT, U, R>(cb, sb, xs, C, tl + 16 * U * (st + 1), nc - U * (st + 1), acc);
+    }
+}
+
+// Generic shape (any K % 32 == 0): loop over the lane's chunks.  U > 0:
+// pipelined stages of U chunks where every lane owns the same number of
+// chunks; U = 0: one chunk at a time (the fewest registers).
+template <int MT, int R, int KS, int U = (R >= 4 ? 1 : 4 / R), class Epi>
 __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, int n, int k, int row0, float *red,
                                                Epi &&epi) {
@@ -295,17 +349,30 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
-    for (int c = c_lo + tl; c < c_hi; c += 16) {
-        uint4 cw[R];
-        uint32_t sw[R];
+    if (U > 0 && KS == 1 && (C & 15) == 0) {
+        // every lane owns the same C / 16 chunks: pipelined stages
+        const uint8_t *cp[R], *sp[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = min(rbase + r, n - 1);   // rows past n: never passed to the epilogue
-            cw[r] = ld_stream16(codes + (size_t)row * (size_t)(k >> 1) + 16 * (size_t)c);
-            sw[r] = ld_stream2(scales + (size_t)row * (size_t)(k >> 4) + 2 * (size_t)c);
+            cp[r] = codes + (size_t)row * (size_t)(k >> 1);
+            sp[r] = scales + (size_t)row * (size_t)(k >> 4);
         }
+        constexpr int UP = U > 0 ? U : 1;
+        pipe_rows<MT, R, UP>(xs, cp, sp, C, tl, acc);
+    } else {
+        for (int c = c_lo + tl; c < c_hi; c += 16) {
+            uint4 cw[R];
+            uint32_t sw[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[r], sw[r], xs, C, c, acc[r]);
+            for (int r = 0; r < R; ++r) {
+                const int row = min(rbase + r, n - 1);   // rows past n: never passed to the epilogue
+                cw[r] = ld_stream16(codes + (size_t)row * (size_t)(k >> 1) + 16 * (size_t)c);
+                sw[r] = ld_stream2(scales + (size_t)row * (size_t)(k >> 4) + 2 * (size_t)c);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[r], sw[r], xs, C, c, acc[r]);
+        }
     }
     gemv_tile_finish<MT, R, KS, 0>(acc, n, row0, red, epi);
 }

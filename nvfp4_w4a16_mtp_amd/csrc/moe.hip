@@ -28,6 +28,10 @@ namespace nvfp4 {
 constexpr int kMoeMaxTopK = 16;
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeHeader = 16384;   // route header bytes at the start of the workspace
+#ifndef NVFP4_PAIR_U
+#define NVFP4_PAIR_U 1
+#endif
+constexpr int kPairU = NVFP4_PAIR_U;   // chunks per pipeline stage of the gate|up row pair
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
 constexpr size_t kMoeMaxLds = 160 * 1024 - 4096;   // dynamic LDS of one workgroup, static LDS aside
 
@@ -267,8 +271,35 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
     } else {
         stage_rows(xs, x, tok, cnt, MT, H);
         __syncthreads();
-        gemv_tile_loop<MT, 1, 1>(xs, gc, gs, I, H, row0, nullptr, epi_g);
-        gemv_tile_loop<MT, 1, 1>(xs, uc, us, I, H, row0, nullptr, epi_u);
+        bool pair = false;
+        if constexpr (MT <= 2) pair = ((H >> 5) & 15) == 0;
+        if (pair) {
+            // the gate row and the up row of a lane's slot stream as one
+            // two-row pipeline (a 16-row tile: one row per slot; kept to
+            // MT <= 2 for the register budget, as above)
+            const int lane = threadIdx.x & 63, slot = lane >> 4, tl = lane & 15;
+            const int row = row0 + (threadIdx.x >> 6) * 4 + slot;
+            const int rc = min(row, I - 1);   // rows past I: never passed to the epilogue
+            const uint8_t *const cp[2] = {gc + (size_t)rc * (size_t)(H >> 1), uc + (size_t)rc * (size_t)(H >> 1)};
+            const uint8_t *const sp[2] = {gs + (size_t)rc * (size_t)(H >> 4), us + (size_t)rc * (size_t)(H >> 4)};
+            float acc[2][MT];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
+            pipe_rows<MT, 2, kPairU>(xs, cp, sp, H >> 5, tl, acc);
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm) {
+                const float g = row16_sum(acc[0][mm]), u = row16_sum(acc[1][mm]);
+                if (tl == mm && row < I) {
+                    epi_g(row, mm, g);
+                    epi_u(row, mm, u);
+                }
+            }
+        } else {
+            gemv_tile_loop<MT, 1, 1, 0>(xs, gc, gs, I, H, row0, nullptr, epi_g);
+            gemv_tile_loop<MT, 1, 1, 0>(xs, uc, us, I, H, row0, nullptr, epi_u);
+        }
     }
 }
 
@@ -377,7 +408,7 @@ __device__ __forceinline__ void down_body(uint4 *xs, const uint16_t *act, const 
     } else {
         stage_rows(xs, act, prs, cnt, MT, I);
         __syncthreads();
-        gemv_tile_loop<MT, 1, 1>(xs, dc, ds, H, I, row0, nullptr, epi);
+        gemv_tile_loop<MT, 1, 1, 0>(xs, dc, ds, H, I, row0, nullptr, epi);
     }
 }
 
