@@ -150,45 +150,88 @@ struct EmbedOut {
     int vocab, units;
 };
 
-// Persistent LM-head pass over the global tiling (16 * R rows per tile):
-// the grid is the resident capacity and workgroup g scores tiles g, g + G,
-// g + 2G, ... so that at any moment the whole chip sweeps one contiguous band
-// of the matrix and every workgroup ends within one tile of the others.  The
-// activations are loaded once per workgroup.
-template <int MT, int R, int KS, int CPL, bool BF16KEY, bool LP>
-__global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
-                                               const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                               int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
-                                               float *__restrict__ out_max, float *__restrict__ out_lp,
-                                               const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb) {
+// Wavefronts per LM-head workgroup: one workgroup per CU holding as many
+// wavefronts as the kernel's registers leave resident (3 per SIMD up to 170
+// VGPRs, 4 up to 128 for the one-row generic loop, 2 up to 256, 1 beyond).
+template <int MT, int CPL>
+constexpr int lm_waves() {
+    return MT == 1 && CPL == 0 ? 16 : MT <= 2 ? 12 : MT == 4 ? 8 : 4;
+}
+
+// Rows per slot of an LM-head unit: one activation row takes 4-row units
+// (short units keep the wavefronts' end times close together); more rows
+// take 8-row units, whose activation reads from LDS serve two rows.
+#ifndef NVFP4_LM_R1
+#define NVFP4_LM_R1 1
+#endif
+template <int MT>
+constexpr int lm_rows_per_slot() {
+    return MT == 1 && NVFP4_LM_R1 ? 1 : 2;
+}
+
+// Next position in a workgroup's unit sequence: wavefronts draw from an LDS
+// counter (positions 0 .. NW-1 are the wavefronts' first units).
+template <int NW>
+__device__ __forceinline__ int lm_draw(int *q, int lane) {
+    int g = 0;
+    if (lane == 0) g = atomicAdd(q, 1);
+    return NW + __builtin_amdgcn_readfirstlane(g);
+}
+
+// Combines per-wavefront candidates wb[0..NW)[m] inside one wavefront:
+// lane w * MT + m takes entry (w, m), xor shuffles fold the w bits, and lane
+// m < MT ends with the combination for activation row m.
+template <int MT, int NW, bool LP>
+__device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], int lane) {
+    constexpr int NWP = NW <= 4 ? 4 : NW <= 8 ? 8 : 16;
+    static_assert(NWP * MT <= 64 && (MT & (MT - 1)) == 0, "one wavefront holds every (wave, row) entry");
+    const int w = lane / MT, mm = lane % MT;
+    ArgPart c = w < NW ? wb[w][mm] : ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
+#pragma unroll
+    for (int off = NWP * MT / 2; off >= MT; off >>= 1) argpart_shfl_combine<LP>(c, off);
+    return c;
+}
+
+// Persistent LM-head pass.  The vocabulary is cut into units of 4 * R rows,
+// one wavefront's tile.  Workgroup b (one per CU) owns units b, b + G,
+// b + 2G, ... (G = gridDim.x), so that at any moment the chip sweeps one
+// contiguous band of the matrix; inside the workgroup the units go to
+// whichever wavefront is free next (an LDS counter), so wavefronts that the
+// CU's arbitration serves less take fewer units and all of them end
+// together.  The activations are loaded once per workgroup.
+template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW>
+__global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
+                                                   const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
+                                                   int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
+                                                   float *__restrict__ out_max, float *__restrict__ out_lp,
+                                                   const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
-    float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
-    __shared__ ArgPart cand[16][MT];
-    __shared__ ArgPart wbest[4][MT];
-    __shared__ int s_last;
+    __shared__ ArgPart wbest[NW][MT];
+    __shared__ int s_last, s_q;
     __shared__ int s_sel[MT];
     unsigned int *ticket = reinterpret_cast<unsigned int *>(ws + kLmTicket);
     float *row0 = reinterpret_cast<float *>(ws + kLmRow0);
     ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
 
-    constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
-    const int ntiles = (v + rows - 1) / rows;
-    const int t_begin = blockIdx.x, t_step = gridDim.x;
+    constexpr int rows = 4 * R;
+    static_assert(32 % rows == 0, "a unit lies inside one 32-row mask word");
+    const int nunits = (v + rows - 1) / rows;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float dec = g->dec;
     // lane m of every slot keeps the best of its rows for activation row m
     // (scalars rather than an ArgPart: a struct captured by the lambda below
     // is kept in scratch memory by the compiler)
     float b_key = -INFINITY, b_val = -INFINITY, b_lm = -INFINITY, b_ls = 0.0f;
     int b_idx = INT_MAX;
-    // Grammar mask word of a tile (tiles are 32 rows, 32-aligned) for the
-    // activation row this lane serves in the epilogue; all ones without a mask.
-    // Loaded with the tile's weights, so it adds no latency to the epilogue.
-    static_assert(GemvTile<R, KS>::kRowsPerTile == 32, "one mask word per tile");
-    const int mrow = min(min((int)(threadIdx.x & 15), MT - 1), m_rt - 1);
-    auto load_mask = [&](int tile) -> uint32_t {
+    // Grammar mask word (32 rows) of a unit for the activation row this lane
+    // serves in the epilogue; all ones without a mask.  Loaded with the
+    // unit's weights, so it adds no latency to the epilogue.
+    const int mrow = min(min(lane & 15, MT - 1), m_rt - 1);
+    auto load_mask = [&](int unit) -> uint32_t {
         if (mask == nullptr) return ~0u;
-        return tile < mask_words ? mask[(size_t)mrow * mask_words + tile] : 0u;
+        const int word = (unit * rows) >> 5;
+        return word < mask_words ? mask[(size_t)mrow * mask_words + word] : 0u;
     };
     uint32_t mword = ~0u;
     auto epi = [&](int row, int mm, float s) {
@@ -196,7 +239,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
         if (row == 0) st_dev(&row0[mm], logit);
         // grammar mask: a disallowed row is scored as -inf (mword holds this
-        // lane's mask word of the current 32-row tile)
+        // lane's mask word of the current unit)
         if (!((mword >> (row & 31)) & 1u)) key = -INFINITY;
         if constexpr (LP) {
             if (key != -INFINITY) lse_merge(b_lm, b_ls, key, 1.0f);   // exp(-inf) adds nothing
@@ -207,63 +250,100 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
             b_idx = row;
         }
     };
+    const int G = gridDim.x, b0 = blockIdx.x;
+    if (threadIdx.x == 0) s_q = 0;
     if constexpr (MT == 1 && CPL > 0) {
-        // one activation row: it lives in registers; each tile's loads are
-        // issued at the top of its iteration and other resident wavefronts
-        // cover the latency
-        XRegs<CPL> xr;
-        load_xregs<KS, CPL>(xr, x);
-        for (int t = t_begin; t < ntiles; t += t_step) {
-            TileRegs<MT, R, KS, CPL> cur;
-            gemv_tile_load(cur, codes, scales, v, k, t * rows);
-            mword = load_mask(t);
-            gemv_tile_compute_x1(cur, xr, v, t * rows, red, epi);
+        // one activation row: it lives in registers; the next unit's loads
+        // are in flight while this one is computed
+        int q = wave, u = b0 + G * q;
+        TileRegs<MT, R, 1, CPL> cur;
+        uint32_t mcur = ~0u;
+        if (u < nunits) {
+            gemv_tile_load<MT, R, 1, CPL, true>(cur, codes, scales, v, k, u * rows);
+            mcur = load_mask(u);
         }
-    } else if constexpr (CPL > 0) {
-        TileRegs<MT, R, KS, CPL> cur;
-        gemv_tile_load(cur, codes, scales, v, k, t_begin * rows);
-        uint32_t mcur = load_mask(t_begin);
-        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        XRegs<CPL> xr;
+        load_xregs<1, CPL>(xr, x);
         __syncthreads();
-        for (int t = t_begin; t < ntiles; t += t_step) {
-            TileRegs<MT, R, KS, CPL> nxt;
+        int qn = lm_draw<NW>(&s_q, lane);
+        while (u < nunits) {
+            const int un = b0 + G * qn;
+            TileRegs<MT, R, 1, CPL> nxt;
             uint32_t mnxt = mcur;
-            if (t + t_step < ntiles) {
-                gemv_tile_load(nxt, codes, scales, v, k, (t + t_step) * rows);
-                mnxt = load_mask(t + t_step);
+            if (un < nunits) {
+                gemv_tile_load<MT, R, 1, CPL, true>(nxt, codes, scales, v, k, un * rows);
+                mnxt = load_mask(un);
             } else {
                 nxt = cur;
             }
+            qn = lm_draw<NW>(&s_q, lane);
             mword = mcur;
-            gemv_tile_compute(cur, xs, v, k, t * rows, red, epi);
+            gemv_tile_compute_x1<R, 1, CPL, true>(cur, xr, v, u * rows, nullptr, epi);
             cur = nxt;
             mcur = mnxt;
+            u = un;
+        }
+    } else if constexpr (CPL > 0) {
+        // the next unit's loads are in flight while this one is computed
+        int q = wave, u = b0 + G * q;
+        TileRegs<MT, R, 1, CPL> cur;
+        uint32_t mcur = ~0u;
+        if (u < nunits) {
+            gemv_tile_load<MT, R, 1, CPL, true>(cur, codes, scales, v, k, u * rows);
+            mcur = load_mask(u);
+        }
+        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __syncthreads();
+        int qn = lm_draw<NW>(&s_q, lane);
+        while (u < nunits) {
+            const int un = b0 + G * qn;
+            TileRegs<MT, R, 1, CPL> nxt;
+            uint32_t mnxt = mcur;
+            if (un < nunits) {
+                gemv_tile_load<MT, R, 1, CPL, true>(nxt, codes, scales, v, k, un * rows);
+                mnxt = load_mask(un);
+            } else {
+                nxt = cur;
+            }
+            qn = lm_draw<NW>(&s_q, lane);
+            mword = mcur;
+            gemv_tile_compute<MT, R, 1, CPL, true>(cur, xs, v, k, u * rows, nullptr, epi);
+            cur = nxt;
+            mcur = mnxt;
+            u = un;
         }
     } else {
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        for (int t = t_begin; t < ntiles; t += t_step) {
-            mword = load_mask(t);
-            gemv_tile_loop<MT, R, KS>(xs, codes, scales, v, k, t * rows, red, epi);
+        int q = wave, qn = lm_draw<NW>(&s_q, lane);
+        for (int u = b0 + G * q; u < nunits; u = b0 + G * q) {
+            mword = load_mask(u);
+            q = qn;
+            qn = lm_draw<NW>(&s_q, lane);
+            gemv_tile_loop<MT, R, 1, (R >= 4 ? 1 : 4 / R), true>(xs, codes, scales, v, k, u * rows, nullptr, epi);
         }
     }
 
-    // workgroup combine: 16 slots x MT candidates -> MT partials
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane >> 4, t = lane & 15;
-    if (t < MT) cand[wave * 4 + slot][t] = ArgPart{b_key, b_val, b_idx, b_lm, b_ls, {0, 0, 0}};
+    // workgroup combine: the four slots of a wavefront by shuffles, then the
+    // NW wavefronts in LDS -> MT partials
+    {
+        ArgPart c{b_key, b_val, b_idx, b_lm, b_ls, {0, 0, 0}};
+        argpart_shfl_combine<LP>(c, 16);
+        argpart_shfl_combine<LP>(c, 32);
+        if (lane < MT) wbest[wave][lane] = c;
+    }
     __syncthreads();
-    if (threadIdx.x < MT) {
-        const int mm = threadIdx.x;
-        ArgPart b = cand[0][mm];
-        for (int s = 1; s < 16; ++s) argpart_combine<LP>(b, cand[s][mm]);
-        ArgPart *dst = parts + (size_t)blockIdx.x * MT + mm;
+    if (wave == 0) {
+        const ArgPart b = combine_waves<MT, NW, LP>(wbest, lane);
+        if (lane < MT) {
+        ArgPart *dst = parts + (size_t)blockIdx.x * MT + lane;
         st_dev(&dst->key, b.key);
         st_dev(&dst->val, b.val);
         st_dev(&dst->idx, b.idx);
         if constexpr (LP) {
             st_dev(&dst->lm, b.lm);
             st_dev(&dst->ls, b.ls);
+        }
         }
     }
     wait_mem();   // partials and row-0 logits have reached device scope
@@ -272,37 +352,24 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
     __syncthreads();
     if (!s_last) return;
 
-    // last workgroup: combine every tile's partials
+    // last workgroup: combine every workgroup's partials (one per thread:
+    // gridDim.x * MT <= 64 * NW)
     const int nparts = gridDim.x;
     ArgPart b[MT];
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
-    // U partials per thread per round: all their loads are issued before any
-    // is compared, so a round costs one memory latency, not U of them
-    constexpr int U = 16 / MT;
-    for (int p0 = threadIdx.x; p0 < nparts; p0 += blockDim.x * U) {
-        ArgPart c[U][MT];
+    for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + u * (int)blockDim.x;
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm) {
-                if (p < nparts) {
-                    const ArgPart *src = parts + (size_t)p * MT + mm;
-                    c[u][mm].key = ld_dev(&src->key);
-                    c[u][mm].val = ld_dev(&src->val);
-                    c[u][mm].idx = ld_dev(&src->idx);
-                    c[u][mm].lm = LP ? ld_dev(&src->lm) : -INFINITY;
-                    c[u][mm].ls = LP ? ld_dev(&src->ls) : 0.0f;
-                } else {
-                    c[u][mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
-                }
-            }
+        for (int mm = 0; mm < MT; ++mm) {
+            const ArgPart *src = parts + (size_t)p * MT + mm;
+            ArgPart c;
+            c.key = ld_dev(&src->key);
+            c.val = ld_dev(&src->val);
+            c.idx = ld_dev(&src->idx);
+            c.lm = LP ? ld_dev(&src->lm) : -INFINITY;
+            c.ls = LP ? ld_dev(&src->ls) : 0.0f;
+            argpart_combine<LP>(b[mm], c);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm) argpart_combine<LP>(b[mm], c[u][mm]);
     }
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm)
@@ -313,24 +380,25 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint16_t *__restrict__ x, 
         for (int mm = 0; mm < MT; ++mm) wbest[wave][mm] = b[mm];
     }
     __syncthreads();
-    if (threadIdx.x < m_rt) {
-        const int mm = threadIdx.x;
-        ArgPart f = wbest[0][mm];
-        for (int w = 1; w < 4; ++w) argpart_combine<LP>(f, wbest[w][mm]);
-        // nothing above -inf: the scan keeps its initial index 0
-        float wkey = f.key;
-        if (!(f.key > -INFINITY)) {
-            const float l0 = ld_dev(&row0[mm]);
-            out_idx[mm] = 0;
-            out_max[mm] = l0;
-            wkey = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(l0)) : l0;
-        } else {
-            out_idx[mm] = f.idx;
-            out_max[mm] = f.val;
+    if (wave == 0) {
+        const ArgPart f = combine_waves<MT, NW, LP>(wbest, lane);
+        if (lane < m_rt) {
+            const int mm = lane;
+            // nothing above -inf: the scan keeps its initial index 0
+            float wkey = f.key;
+            if (!(f.key > -INFINITY)) {
+                const float l0 = ld_dev(&row0[mm]);
+                out_idx[mm] = 0;
+                out_max[mm] = l0;
+                wkey = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(l0)) : l0;
+            } else {
+                out_idx[mm] = f.idx;
+                out_max[mm] = f.val;
+            }
+            // no mass (nothing allowed, or only -inf keys): not measured
+            if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
+            s_sel[mm] = f.key > -INFINITY ? f.idx : 0;
         }
-        // no mass (nothing allowed, or only -inf keys): not measured
-        if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
-        s_sel[mm] = f.key > -INFINITY ? f.idx : 0;
     }
     if (emb.table != nullptr) {
         __syncthreads();
@@ -414,28 +482,27 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
     return check_launch("w4a16_gemv");
 }
 
-// Grid of the persistent LM-head kernel: as many workgroups as are resident
-// at once (a second round of workgroups would leave the chip half idle in
-// its tail), never more than there are tiles.
-template <class K>
-static int lm_grid(K kernel, size_t lds, int ntiles) {
-    const int cap = num_cus() * blocks_per_cu(reinterpret_cast<const void *>(kernel), 256, lds);
-    return ntiles < cap ? ntiles : cap;
-}
-
+// Grid of the persistent LM-head kernel: every workgroup that is resident at
+// once (normally one per CU), never more than the workspace has partials for.
 template <int MT, int CPL, bool BK, bool LP>
 static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
                              char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words,
                              const EmbedOut &emb) {
-    auto kern = k_lmhead<MT, 2, 1, CPL, BK, LP>;
+    constexpr int NW = lm_waves<MT, CPL>();
+    auto kern = k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW>;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
-    const int ntiles = (v + 31) / 32;
-    hipLaunchKernelGGL(kern, dim3(lm_grid(kern, lds, ntiles)), dim3(256), lds, s, h, m, w->codes, w->scales, w->global,
-                       v, w->k, ws, oi, om, olp, mask, mask_words, emb);
+    const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kern), 64 * NW, lds);
+    if (per_cu < 1) {
+        fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: a %d-thread workgroup does not fit on a CU", 64 * NW);
+        return;
+    }
+    const int cap = num_cus() * per_cu, nparts = (v + 15) / 16;
+    hipLaunchKernelGGL(kern, dim3(cap < nparts ? cap : nparts), dim3(64 * NW), lds, s, h, m, w->codes, w->scales,
+                       w->global, v, w->k, ws, oi, om, olp, mask, mask_words, emb);
 }
 
-// The LM head keeps KS = 1 and R = 2 (32-row tiles); there are at most
-// ceil(V / 32) partials.  A fixed chunk count when K = 2048.
+// The LM head keeps KS = 1 and R = 2 (8-row wavefront units); there are at
+// most ceil(V / 16) partials.  A fixed chunk count when K = 2048.
 template <int MT>
 static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
                            float *olp, const uint32_t *mask, int mask_words, const EmbedOut &emb, bool bk,

@@ -101,25 +101,29 @@ __device__ __forceinline__ void chunk_fma(const uint4 cw, uint32_t sw, const uin
     }
 }
 
-// Computes the tile's dot products; calls epi(row, m, value) once per
-// (row < n, m < MT) with the fp32 sum (before the global scale), from lane
-// m of the slot in the K-segment-0 wavefront.  red: LDS scratch of
-// 16 * R * MT floats (used when KS > 1).  If PRELOADED, the first tile's
-// loads were issued by gemv_tile_load into `pre` before x was staged.
+// Tiles: a workgroup tile is 16 * R / KS rows (four wavefronts of four
+// 16-lane slots, R rows per slot, K split over KS wavefronts).  With WT (a
+// wavefront tile, KS = 1) the tile is the calling wavefront's own 4 * R rows
+// starting at row0, so wavefronts can take tiles independently.
+// The tile functions compute the dot products and call epi(row, m, value)
+// once per (row < n, m < MT) with the fp32 sum (before the global scale),
+// from lane m of the slot in the K-segment-0 wavefront.  red: LDS scratch
+// of 16 * R * MT floats (used when KS > 1).
 template <int MT, int R, int KS, int CPL>
 struct TileRegs {
     uint4 c[R][CPL > 0 ? CPL : 1];
     uint32_t s[R][CPL > 0 ? CPL : 1];
 };
 
-template <int MT, int R, int KS, int CPL>
+template <int MT, int R, int KS, int CPL, bool WT = false>
 __device__ __forceinline__ void gemv_tile_load(TileRegs<MT, R, KS, CPL> &t, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, int n, int k, int row0) {
     static_assert(CPL > 0, "preloading needs a fixed chunk count");
+    static_assert(!WT || KS == 1, "a wavefront tile has no K split");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane >> 4, tl = lane & 15;
     const int ks = (KS == 1) ? 0 : (wave % KS);
-    const int rg = wave / KS;
+    const int rg = WT ? 0 : wave / KS;
     const int rbase = row0 + (rg * 4 + slot) * R;
     const int c_lo = ks * 16 * CPL;
     // rows past n load row n - 1 instead (no branch around the loads); their
@@ -142,12 +146,12 @@ __device__ __forceinline__ void gemv_tile_load(TileRegs<MT, R, KS, CPL> &t, cons
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MT, int R, int KS, int CPL, class Epi>
+template <int MT, int R, int KS, int CPL, bool WT = false, class Epi>
 __device__ __forceinline__ void gemv_tile_finish(float (&acc)[R][MT], int n, int row0, float *red, Epi &&epi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane >> 4, t = lane & 15;
     const int ks = (KS == 1) ? 0 : (wave % KS);
-    const int rg = wave / KS;
+    const int rg = WT ? 0 : wave / KS;
     const int rbase = row0 + (rg * 4 + slot) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -191,7 +195,7 @@ __device__ __forceinline__ void gemv_tile_finish(float (&acc)[R][MT], int n, int
 }
 
 // Full tile with fixed chunk count: loads already issued into `t`.
-template <int MT, int R, int KS, int CPL, class Epi>
+template <int MT, int R, int KS, int CPL, bool WT = false, class Epi>
 __device__ __forceinline__ void gemv_tile_compute(const TileRegs<MT, R, KS, CPL> &t, const uint4 *xs, int n, int k,
                                                   int row0, float *red, Epi &&epi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -208,7 +212,7 @@ __device__ __forceinline__ void gemv_tile_compute(const TileRegs<MT, R, KS, CPL>
     for (int j = 0; j < CPL; ++j)
 #pragma unroll
         for (int r = 0; r < R; ++r) chunk_fma<MT>(t.c[r][j], t.s[r][j], xs, C, c_lo + tl + 16 * j, acc[r]);
-    gemv_tile_finish<MT, R, KS, CPL>(acc, n, row0, red, epi);
+    gemv_tile_finish<MT, R, KS, CPL, WT>(acc, n, row0, red, epi);
 }
 
 // Single activation row with a fixed chunk count: a lane always works on the
@@ -263,7 +267,7 @@ __device__ __forceinline__ float chunk_dot_xreg(const uint4 cw, uint32_t sw, con
     return __builtin_fmaf(b1, sf1, acc);
 }
 
-template <int R, int KS, int CPL, class Epi>
+template <int R, int KS, int CPL, bool WT = false, class Epi>
 __device__ __forceinline__ void gemv_tile_compute_x1(const TileRegs<1, R, KS, CPL> &t, const XRegs<CPL> &xr, int n,
                                                      int row0, float *red, Epi &&epi) {
     float acc[R][1];
@@ -273,7 +277,7 @@ __device__ __forceinline__ void gemv_tile_compute_x1(const TileRegs<1, R, KS, CP
     for (int j = 0; j < CPL; ++j)
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r][0] = chunk_dot_xreg(t.c[r][j], t.s[r][j], xr.w[j], acc[r][0]);
-    gemv_tile_finish<1, R, KS, CPL>(acc, n, row0, red, epi);
+    gemv_tile_finish<1, R, KS, CPL, WT>(acc, n, row0, red, epi);
 }
 
 // One stage of the pipelined loop: chunks c0, c0 + 16, ... of the slot's R
@@ -331,14 +335,14 @@ __device__ __forceinline__ void pipe_rows(const uint4 *xs, const uint8_t *const 
 // Generic shape (any K % 32 == 0): loop over the lane's chunks.  U > 0:
 // pipelined stages of U chunks where every lane owns the same number of
 // chunks; U = 0: one chunk at a time (the fewest registers).
-template <int MT, int R, int KS, int U = (R >= 4 ? 1 : 4 / R), class Epi>
+template <int MT, int R, int KS, int U = (R >= 4 ? 1 : 4 / R), bool WT = false, class Epi>
 __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, int n, int k, int row0, float *red,
                                                Epi &&epi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = lane >> 4, tl = lane & 15;
     const int ks = (KS == 1) ? 0 : (wave % KS);
-    const int rg = wave / KS;
+    const int rg = WT ? 0 : wave / KS;
     const int C = k >> 5;
     const int cs = (C + KS - 1) / KS;
     const int c_lo = ks * cs;
@@ -374,7 +378,7 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
             for (int r = 0; r < R; ++r) chunk_fma<MT>(cw[r], sw[r], xs, C, c, acc[r]);
         }
     }
-    gemv_tile_finish<MT, R, KS, 0>(acc, n, row0, red, epi);
+    gemv_tile_finish<MT, R, KS, 0, WT>(acc, n, row0, red, epi);
 }
 
 // ---------------------------------------------------------------- host ----
