@@ -134,9 +134,25 @@ __device__ __forceinline__ void argpart_shfl_combine(ArgPart &b, int off) {
     argpart_combine<LP>(b, o);
 }
 
+// Argmax as one unsigned 64-bit word whose order is that of beats(): the
+// key's bits made monotone in the upper half (-0 taken as +0, so equal keys
+// compare equal), the complemented index in the lower half (a lower index
+// wins a tie).  Keys here are never NaN (NaN never beats the initial -inf).
+__device__ __forceinline__ unsigned long long pack_best(float key, int idx) {
+    const unsigned int kb = __float_as_uint(key == 0.0f ? 0.0f : key);
+    const unsigned int ok = (kb & 0x80000000u) ? ~kb : (kb | 0x80000000u);
+    return ((unsigned long long)ok << 32) | (unsigned long long)(~(unsigned int)idx);
+}
+__device__ __forceinline__ float unpack_best_key(unsigned long long p) {
+    const unsigned int ok = (unsigned int)(p >> 32);
+    return __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
+}
+__device__ __forceinline__ int unpack_best_idx(unsigned long long p) { return (int)~(unsigned int)p; }
+
 // Workspace layout of lmhead_gemv_argmax.
 constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
 constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
+constexpr int kLmBest = 128;      // uint64[8]: packed best (key, index) per row (zero between calls)
 constexpr int kLmParts = 256;     // ArgPart[grid][MT]
 
 // Optional gather of the selected tokens' embedding rows by the last
@@ -209,10 +225,10 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     uint4 *xs = smem;
     __shared__ ArgPart wbest[NW][MT];
     __shared__ int s_last, s_q;
-    __shared__ int s_sel[MT];
     unsigned int *ticket = reinterpret_cast<unsigned int *>(ws + kLmTicket);
     float *row0 = reinterpret_cast<float *>(ws + kLmRow0);
     ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
+    unsigned long long *best = reinterpret_cast<unsigned long long *>(ws + kLmBest);
 
     constexpr int rows = 4 * R;
     static_assert(32 % rows == 0, "a unit lies inside one 32-row mask word");
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     }
 
     // workgroup combine: the four slots of a wavefront by shuffles, then the
-    // NW wavefronts in LDS -> MT partials
+    // NW wavefronts in LDS -> MT candidates
     {
         ArgPart c{b_key, b_val, b_idx, b_lm, b_ls, {0, 0, 0}};
         argpart_shfl_combine<LP>(c, 16);
@@ -336,82 +352,110 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     if (wave == 0) {
         const ArgPart b = combine_waves<MT, NW, LP>(wbest, lane);
         if (lane < MT) {
-        ArgPart *dst = parts + (size_t)blockIdx.x * MT + lane;
-        st_dev(&dst->key, b.key);
-        st_dev(&dst->val, b.val);
-        st_dev(&dst->idx, b.idx);
-        if constexpr (LP) {
-            st_dev(&dst->lm, b.lm);
-            st_dev(&dst->ls, b.ls);
-        }
+            // the argmax as one 64-bit atomic max per activation row (the
+            // fp32 logit of a bf16 key, or the sign of a zero one, is looked
+            // up afterwards in the partial of the workgroup that owns the
+            // winning row); the log-sum-exp state as a partial
+            ArgPart *dst = parts + (size_t)blockIdx.x * MT + lane;
+            st_dev(&dst->val, b.val);
+            if constexpr (LP) {
+                st_dev(&dst->lm, b.lm);
+                st_dev(&dst->ls, b.ls);
+            }
+            __hip_atomic_fetch_max(&best[lane], pack_best(b.key, b.idx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    wait_mem();   // partials and row-0 logits have reached device scope
+    wait_mem();   // partials, maxima and row-0 logits have reached device scope
     __syncthreads();
     if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
     __syncthreads();
     if (!s_last) return;
 
-    // last workgroup: combine every workgroup's partials (one per thread:
-    // gridDim.x * MT <= 64 * NW)
-    const int nparts = gridDim.x;
-    ArgPart b[MT];
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm) b[mm] = ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
-    for (int p = threadIdx.x; p < nparts; p += blockDim.x) {
+    // last workgroup: its first wavefront reads the maxima and merges the
+    // log-sum-exp partials
+    if (wave != 0) return;
+    ArgPart f{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
+    if constexpr (LP) {
+        float lm[MT], ls[MT];
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) {
-            const ArgPart *src = parts + (size_t)p * MT + mm;
-            ArgPart c;
-            c.key = ld_dev(&src->key);
-            c.val = ld_dev(&src->val);
-            c.idx = ld_dev(&src->idx);
-            c.lm = LP ? ld_dev(&src->lm) : -INFINITY;
-            c.ls = LP ? ld_dev(&src->ls) : 0.0f;
-            argpart_combine<LP>(b[mm], c);
+            lm[mm] = -INFINITY;
+            ls[mm] = 0.0f;
         }
-    }
+        // UB partials per lane per round, all loads issued before any merge
+        constexpr int UB = MT <= 2 ? 4 : MT == 4 ? 2 : 1;
+        for (int p0 = lane; p0 < (int)gridDim.x; p0 += 64 * UB) {
+            float plm[UB][MT], pls[UB][MT];
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
+            for (int j = 0; j < UB; ++j) {
+                const int p = p0 + 64 * j;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) argpart_shfl_combine<LP>(b[mm], off);
-    if (lane == 0) {
-#pragma unroll
-        for (int mm = 0; mm < MT; ++mm) wbest[wave][mm] = b[mm];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const ArgPart f = combine_waves<MT, NW, LP>(wbest, lane);
-        if (lane < m_rt) {
-            const int mm = lane;
-            // nothing above -inf: the scan keeps its initial index 0
-            float wkey = f.key;
-            if (!(f.key > -INFINITY)) {
-                const float l0 = ld_dev(&row0[mm]);
-                out_idx[mm] = 0;
-                out_max[mm] = l0;
-                wkey = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(l0)) : l0;
-            } else {
-                out_idx[mm] = f.idx;
-                out_max[mm] = f.val;
+                for (int mm = 0; mm < MT; ++mm) {
+                    const ArgPart *src = parts + (size_t)(p < (int)gridDim.x ? p : 0) * MT + mm;
+                    plm[j][mm] = ld_dev(&src->lm);
+                    pls[j][mm] = ld_dev(&src->ls);
+                    if (p >= (int)gridDim.x) {
+                        plm[j][mm] = -INFINITY;
+                        pls[j][mm] = 0.0f;
+                    }
+                }
             }
-            // no mass (nothing allowed, or only -inf keys): not measured
-            if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
-            s_sel[mm] = f.key > -INFINITY ? f.idx : 0;
+#pragma unroll
+            for (int j = 0; j < UB; ++j)
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) lse_merge(lm[mm], ls[mm], plm[j][mm], pls[j][mm]);
         }
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                lse_merge(lm[mm], ls[mm], __shfl_xor(lm[mm], off, 64), __shfl_xor(ls[mm], off, 64));
+            if (mm == lane) {
+                f.lm = lm[mm];
+                f.ls = ls[mm];
+            }
+        }
+    }
+    if (lane < MT) {
+        const unsigned long long pk = ld_dev(&best[lane]);
+        st_dev(&best[lane], 0ull);   // ready for the next call
+        f.key = unpack_best_key(pk);
+        f.idx = unpack_best_idx(pk);
+        f.val = f.key;
+        if (f.key > -INFINITY && (BF16KEY || f.key == 0.0f)) {
+            const int owner = (f.idx / rows) % (int)gridDim.x;
+            f.val = ld_dev(&parts[(size_t)owner * MT + lane].val);
+        }
+    }
+    if (lane < m_rt) {
+        const int mm = lane;
+        // nothing above -inf: the scan keeps its initial index 0
+        float wkey = f.key;
+        if (!(f.key > -INFINITY)) {
+            const float l0 = ld_dev(&row0[mm]);
+            out_idx[mm] = 0;
+            out_max[mm] = l0;
+            wkey = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(l0)) : l0;
+        } else {
+            out_idx[mm] = f.idx;
+            out_max[mm] = f.val;
+        }
+        // no mass (nothing allowed, or only -inf keys): not measured
+        if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
     }
     if (emb.table != nullptr) {
-        __syncthreads();
+        // the selected token of row mm is lane mm's
+        const int sel = lane < m_rt && f.key > -INFINITY ? f.idx : 0;
         for (int mm = 0; mm < m_rt; ++mm) {
-            const int id = s_sel[mm];
+            const int id = __shfl(sel, mm, 64);
             const bool in = id >= 0 && id < emb.vocab;
             const uint4 *src = emb.table + (size_t)(in ? id : 0) * emb.units;
             uint4 *dst = emb.out + (size_t)mm * emb.stride_units;
-            for (int u = threadIdx.x; u < emb.units; u += blockDim.x) dst[u] = in ? src[u] : make_uint4(0, 0, 0, 0);
-            if (threadIdx.x == 0 && emb.id_log != nullptr) emb.id_log[mm] = id;
+            for (int u = lane; u < emb.units; u += 64) dst[u] = in ? src[u] : make_uint4(0, 0, 0, 0);
+            if (lane == 0 && emb.id_log != nullptr) emb.id_log[mm] = id;
         }
     }
-    if (threadIdx.x == 0) st_dev(ticket, 0u);   // ready for the next call
+    if (lane == 0) st_dev(ticket, 0u);   // ready for the next call
 }
 
 // ------------------------------------------------------------ dispatch ----
