@@ -183,9 +183,10 @@ int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, vo
  *   workspace device scratch of at least
  *            lmhead_gemv_argmax_workspace_bytes(m, V) bytes (V = the number
  *            of rows scored), 256-byte aligned.  It holds a ticket counter
- *            that must be zero before the first call (zero-fill the buffer
- *            once); each call returns it to zero.  A workspace serves one
- *            call at a time: calls that overlap on one workspace race.
+ *            and per-row packed maxima that must be zero before the first
+ *            call (zero-fill the buffer once); each call returns them to
+ *            zero.  A workspace serves one call at a time: calls that
+ *            overlap on one workspace race.
  * Rows with equal codes and scales produce bit-identical logits.  One launch.
  */
 size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows);
