@@ -10,8 +10,8 @@
 // (hardware E2M1 -> fp32 convert, times the E4M3 block scale, packed to
 // bf16 -- exact, since e2m1 * e4m3 has at most 6 significant bits).  The
 // next step's global loads are issued before the current step's MFMAs.
-// LDS chunks are XOR-swizzled (lds_off) to spread the 16 rows of an operand
-// load and the rows of a staging store over the banks.  The global scale is
+// LDS chunks are XOR-swizzled (lds_off) to spread the rows of an operand
+// load and of a staging store over the banks.  The global scale is
 // applied in the epilogue.
 #include "common.hpp"
 
@@ -21,9 +21,10 @@ constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLdsRow = kBK * 2;   // bytes per LDS row (64 bf16 of one K step)
 
 // Byte offset of 16-byte chunk c (8 bf16) of tile row r in LDS.  The chunk is
-// stored at position c ^ ((r / 2) % 8), so that the 16 rows one MFMA operand
-// load reads at a fixed chunk land in different bank groups.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsRow + 16 * (c ^ ((r >> 1) & 7)); }
+// stored at position c ^ (r % 8): each 8 consecutive rows of one operand
+// read at a fixed chunk, and the 4 rows of one staging store, hit 8
+// different 16-byte bank groups of a 128-byte bank row.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsRow + 16 * (c ^ (r & 7)); }
 
 // Two E2M1 codes (byte SEL of word) times sf, packed as two bf16 (exact).
 template <int SEL>
