@@ -33,6 +33,16 @@ constexpr int kMoeHeader = 16384;   // route header bytes at the start of the wo
 #endif
 constexpr int kPairU = NVFP4_PAIR_U;   // chunks per pipeline stage of the gate|up row pair
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
+constexpr int kSpinLimit = 1 << 22;    // polls of the fused down pass's wait (seconds)
+// Hand-off words of the fused launch (zero between calls), each counter on
+// its own 128-byte line: per expert column u a count of its finished gate/up
+// workgroups (word 32 u), a count of finished columns (word 32 * 128), then
+// one go flag per down workgroup, kGoStride words apart.
+constexpr int kColStride = 32, kTopWord = 32 * 128, kSyncWords = 32 * 129, kGoStride = 16;
+#ifndef NVFP4_MOE_FUSED
+#define NVFP4_MOE_FUSED 1
+#endif
+constexpr bool kMoeFused = NVFP4_MOE_FUSED;
 constexpr size_t kMoeMaxLds = 160 * 1024 - 4096;   // dynamic LDS of one workgroup, static LDS aside
 
 // One distinct expert of a call: the tokens that chose it (ascending) and,
@@ -243,6 +253,28 @@ __device__ __forceinline__ void stage_rows(uint4 *xs, const uint16_t *__restrict
     }
 }
 
+// stage_rows for rows another workgroup of the same launch wrote: 16-byte
+// buffer loads with the device-coherent cache policy (sc1), over a source of
+// src_rows rows.
+constexpr int kBufWord3 = 0x00020000;   // buffer resource word 3 for raw byte buffers (gfx9 family)
+constexpr int kCoherent = 16;           // sc1: device-scope coherent load
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+__device__ __forceinline__ void stage_rows_dev(uint4 *xs, const uint16_t *__restrict__ src, size_t src_rows,
+                                               const int *rows, int cnt, int mt, int k) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, (int)(src_rows * k * 2), kBufWord3);
+    const int C = k >> 5, upr = k >> 3;
+    for (int p = threadIdx.x; p < mt * upr; p += blockDim.x) {
+        int mm = p / upr, w = p - mm * upr;
+        int c = w >> 2, q = w & 3;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (mm < cnt) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (rows[mm] * k + 8 * w) * 2, 0, kCoherent);
+            v = make_uint4(t.x, t.y, t.z, t.w);
+        }
+        xs[(mm * 4 + q) * C + c] = v;
+    }
+}
+
 // gate/up body for MT >= cnt token rows.
 template <int MT, int CPL>
 __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const int *tok, const int *prs, int cnt,
@@ -255,7 +287,7 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
         if (mm >= cnt) return;
         const float up = v * udec;
         const float a = gl / (1.0f + expf(-gl)) * up;
-        act[(size_t)prs[mm] * I + row] = (uint16_t)f32_to_bf16_bits(a);
+        st_dev(&act[(size_t)prs[mm] * I + row], (uint16_t)f32_to_bf16_bits(a));   // read across workgroups
     };
     // Preloading both tiles is kept to MT <= 2 (the common case: most experts
     // serve one or two tokens), so that the 8-token branch does not set the
@@ -304,23 +336,26 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
 }
 
 // Routing + gate/up: every workgroup computes the routing in LDS (cheap,
-// and it saves a launch), takes the distinct expert blockIdx.y, and
-// workgroup (0, 0) publishes ids, weights and the route for the down pass.
-template <int CPL>
-__global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
-                                                    int m, int E, int topk, nvfp4_moe_weights e,
-                                                    int32_t *__restrict__ ids, float *__restrict__ wts,
-                                                    MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
-                                                    MoeShared sh) {
-    extern __shared__ uint4 smem[];
+// and it saves a launch), takes the distinct expert u and the row tile bx
+// (of gx), and workgroup (0, 0) publishes ids and weights -- and, for a
+// separate down launch, the route.  Activations, and the shared expert's
+// activations and gate, are stored device-scope: in the fused launch the
+// down workgroups read them in the same launch, once the workgroup has
+// counted itself in the hand-off words `done` (FUSED).
+template <int CPL, bool FUSED>
+__device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx, const uint16_t *__restrict__ x,
+                                             const float *__restrict__ logits, int m, int E, int topk,
+                                             const nvfp4_moe_weights &e, int32_t *__restrict__ ids,
+                                             float *__restrict__ wts, MoeRoute *__restrict__ route,
+                                             uint16_t *__restrict__ act, const MoeShared &sh, unsigned int *done,
+                                             int n_down) {
     RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // reused for the activations afterwards
     __shared__ int tok[8], prs[8];
     __shared__ int s_ex, s_cnt, s_nd;
-    const int u = blockIdx.y;
     // shared expert: the workgroups of the first expert column form 16 of its
     // activations per token each (loads issued before the routing, stored after)
     const int I = e.inter, H = e.hidden;
-    const int si = blockIdx.x * kMoeRows + (threadIdx.x & 15), st = threadIdx.x >> 4;
+    const int si = bx * kMoeRows + (threadIdx.x & 15), st = threadIdx.x >> 4;
     const bool s_act = sh.on && u == 0 && st < m && si < I;
     float sgv = 0.0f, suv = 0.0f;
     if (s_act) {
@@ -328,9 +363,9 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
         suv = sh.su[(size_t)st * I + si];
     }
     moe_route_lds(logits, m, E, topk, L);
-    if (s_act) sh.sact[(size_t)st * I + si] = (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv);
+    if (s_act) st_dev(&sh.sact[(size_t)st * I + si], (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv));
     // shared_expert_gate: the last workgroup of the first column, one wavefront per token
-    if (sh.on && u == 0 && blockIdx.x == gridDim.x - 1) {
+    if (sh.on && u == 0 && bx == gx - 1) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         for (int t = wave; t < m; t += 4) {
             float z = 0.0f;
@@ -338,14 +373,16 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
                 for (int h = lane; h < H; h += 64)
                     z = __builtin_fmaf(bf16_bits_to_f32(sh.gate_w[h]), bf16_bits_to_f32(x[(size_t)t * H + h]), z);
             z = wave_sum(z);
-            if (lane == 0) sh.sgate[t] = sh.gate_w != nullptr ? 1.0f / (1.0f + expf(-z)) : 1.0f;
+            if (lane == 0) st_dev(&sh.sgate[t], sh.gate_w != nullptr ? 1.0f / (1.0f + expf(-z)) : 1.0f);
         }
     }
-    if (blockIdx.x == 0 && u == 0) {
+    if (bx == 0 && u == 0) {
         for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
             ids[p] = L.sel_i[p / topk][p % topk];
             wts[p] = L.sel_w[p / topk][p % topk];
         }
+    }
+    if (!FUSED && bx == 0 && u == 0) {
         for (int q = threadIdx.x; q < L.n_distinct; q += blockDim.x) {
             route->ex[q] = L.ex[q];
             route->ex_id[q] = L.ex[q].expert;
@@ -385,12 +422,45 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
     const uint8_t *gc = e.gate_codes + (size_t)ex * (wsz / 2), *gs = e.gate_scales + (size_t)ex * (wsz / 16);
     const uint8_t *uc = e.up_codes + (size_t)ex * (wsz / 2), *us = e.up_scales + (size_t)ex * (wsz / 16);
     const float gdec = e.gate_global[ex].dec, udec = e.up_global[ex].dec;
-    const int row0 = blockIdx.x * kMoeRows;
+    const int row0 = bx * kMoeRows;
     const int mt = round_up_mt(cnt);
     if (mt == 1) gate_up_body<1, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     else if (mt == 2) gate_up_body<2, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     else if (mt == 4) gate_up_body<4, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     else gate_up_body<8, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    if constexpr (FUSED) {
+        // count this workgroup in its column; the one that completes a column
+        // counts the column, and the one that completes the last column
+        // releases every down workgroup through its own go flag
+        __shared__ int s_release;
+        wait_mem();   // this workgroup's activations have reached device scope
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int rel = 0;
+            if (atomicAdd(&done[kColStride * u], 1u) == (unsigned int)(gx - 1)) {
+                st_dev(&done[kColStride * u], 0u);
+                if (atomicAdd(&done[kTopWord], 1u) == (unsigned int)(s_nd - 1)) {
+                    st_dev(&done[kTopWord], 0u);
+                    rel = 1;
+                }
+            }
+            s_release = rel;
+        }
+        __syncthreads();
+        if (s_release)
+            for (int i = threadIdx.x; i < n_down; i += blockDim.x) st_dev(&done[kSyncWords + kGoStride * i], 1u);
+    }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+                                                    int m, int E, int topk, nvfp4_moe_weights e,
+                                                    int32_t *__restrict__ ids, float *__restrict__ wts,
+                                                    MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
+                                                    MoeShared sh) {
+    extern __shared__ uint4 smem[];
+    gate_up_role<CPL, false>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts, route, act,
+                             sh, nullptr, 0);
 }
 
 template <int MT, int CPL>
@@ -466,34 +536,74 @@ constexpr int kDownBatch = 4;   // items per slot in flight
 constexpr int kDownMaxExperts = 129;   // routed (<= 128) + the shared one
 constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the shared expert
 
-template <int CPL>
-__global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
-                                                      const float *__restrict__ wts, const MoeRoute *__restrict__ route,
-                                                      const uint16_t *__restrict__ act, float *__restrict__ y,
-                                                      MoeShared sh) {
-    extern __shared__ uint4 smem[];
+// The row-owner down pass of workgroup bx.  Separate launch: the plan comes
+// from the route the gate/up launch published.  FUSED (one launch with the
+// gate/up workgroups, which come first in dispatch order): the workgroup
+// computes the routing itself, builds the plan in LDS, issues its weight
+// loads, then waits for its go flag (set once every gate/up workgroup of
+// the routed experts has finished) and reads the activations with
+// device-coherent loads.  The wait is bounded: past kSpinLimit polls the
+// workgroup writes NaN rows instead of waiting for ever.
+template <int CPL, bool FUSED>
+__device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
+                                               const MoeRoute *__restrict__ route, const float *__restrict__ logits,
+                                               int E, int gx, const uint16_t *__restrict__ act, float *__restrict__ y,
+                                               const MoeShared &sh, unsigned int *done) {
     __shared__ int s_ex[kDownMaxExperts], s_pb[kDownMaxExperts + 1];
     __shared__ float s_dec[kDownMaxExperts], s_w[kDownMaxPos];
     __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
     __shared__ float contrib[kDownMaxPos][kDownRows];
+    __shared__ int s_nr, s_p0, s_late;
     const int H = e.hidden, I = e.inter, C = I >> 5;
-    // the plan in LDS, one round of loads; with a shared expert it follows
-    // the routed ones as expert nd (id -1), its m positions after the pairs,
-    // weighted by the shared gate, activation rows from sh.sact
-    const int nr = route->n_distinct, P0 = route->n_pairs;
-    const int nd = nr + (sh.on ? 1 : 0), P = P0 + (sh.on ? m : 0);
-    for (int i = threadIdx.x; i <= nr; i += blockDim.x) {
-        s_pb[i] = route->pb[i];
-        if (i < nr) {
-            s_ex[i] = route->ex_id[i];
-            s_dec[i] = route->ddec[i];
+    // the plan in LDS; with a shared expert it follows the routed ones as
+    // expert nd (id -1), its m positions after the pairs, weighted by the
+    // shared gate, activation rows from sh.sact
+    if constexpr (FUSED) {
+        RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // the activation image overwrites it later
+        moe_route_lds(logits, m, E, topk, L);
+        const int nr = L.n_distinct;
+        for (int q = threadIdx.x; q < nr; q += blockDim.x) {
+            s_ex[q] = L.ex[q].expert;
+            s_dec[q] = e.down_global[L.ex[q].expert].dec;
         }
+        if (threadIdx.x == 0) {
+            int pb = 0;
+            for (int q = 0; q < nr; ++q) {
+                const MoeExpert &me = L.ex[q];
+                s_pb[q] = pb;
+                for (int c = 0; c < me.cnt; ++c, ++pb) {
+                    s_tok[pb] = me.tok[c];
+                    s_pair[pb] = me.pair[c];
+                    s_w[pb] = L.sel_w[me.tok[c]][me.pair[c] - me.tok[c] * topk];
+                }
+            }
+            s_pb[nr] = pb;
+            s_nr = nr;
+            s_p0 = pb;
+        }
+        __syncthreads();
+    } else {
+        const int nr = route->n_distinct, P0 = route->n_pairs;
+        for (int i = threadIdx.x; i <= nr; i += blockDim.x) {
+            s_pb[i] = route->pb[i];
+            if (i < nr) {
+                s_ex[i] = route->ex_id[i];
+                s_dec[i] = route->ddec[i];
+            }
+        }
+        for (int i = threadIdx.x; i < P0; i += blockDim.x) {
+            s_tok[i] = route->pos_tok[i];
+            s_pair[i] = route->pos_pair[i];
+            s_w[i] = route->pos_w[i];
+        }
+        if (threadIdx.x == 0) {
+            s_nr = nr;
+            s_p0 = P0;
+        }
+        __syncthreads();
     }
-    for (int i = threadIdx.x; i < P0; i += blockDim.x) {
-        s_tok[i] = route->pos_tok[i];
-        s_pair[i] = route->pos_pair[i];
-        s_w[i] = route->pos_w[i];
-    }
+    const int nr = s_nr, P0 = s_p0;
+    const int nd = nr + (sh.on ? 1 : 0), P = P0 + (sh.on ? m : 0);
     if (sh.on) {
         if (threadIdx.x == 0) {
             s_ex[nr] = -1;
@@ -503,13 +613,13 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
         if (threadIdx.x < m) {
             s_tok[P0 + threadIdx.x] = threadIdx.x;
             s_pair[P0 + threadIdx.x] = threadIdx.x;   // row of sh.sact
-            s_w[P0 + threadIdx.x] = sh.sgate[threadIdx.x];
+            if (!FUSED) s_w[P0 + threadIdx.x] = sh.sgate[threadIdx.x];   // FUSED: read after the wait
         }
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tl = lane & 15;
     const int sl = wave * 4 + (lane >> 4);
-    const int r0 = blockIdx.x * kDownRows;
+    const int r0 = bx * kDownRows;
     const int nitems = nd * kDownRows;
     const size_t wsz = (size_t)H * I;
     for (int b0 = 0; b0 < nitems; b0 += 16 * kDownBatch) {
@@ -536,8 +646,32 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
         }
         __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any arithmetic
         if (b0 == 0) {
-            stage_rows(smem, act, s_pair, P0, P0, I);   // row pos of the image = pair position pos
-            if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
+            if constexpr (FUSED) {
+                if (threadIdx.x == 0) {
+                    unsigned int *go = done + kSyncWords + kGoStride * bx;
+                    int it = 0;
+                    while (ld_dev(go) == 0u && it < kSpinLimit) {
+                        __builtin_amdgcn_s_sleep(2);
+                        ++it;
+                    }
+                    s_late = it >= kSpinLimit;
+                    st_dev(go, 0u);   // ready for the next call
+                }
+                __syncthreads();
+                if (s_late) {
+                    for (int i = threadIdx.x; i < m * kDownRows; i += blockDim.x) {
+                        const int row = r0 + i % kDownRows;
+                        if (row < H) y[(size_t)(i / kDownRows) * H + row] = __builtin_nanf("");
+                    }
+                    return;
+                }
+                if (sh.on && threadIdx.x < m) s_w[P0 + threadIdx.x] = ld_dev(&sh.sgate[threadIdx.x]);
+                stage_rows_dev(smem, act, (size_t)m * topk, s_pair, P0, P0, I);
+                if (sh.on) stage_rows_dev(smem + (size_t)P0 * 4 * C, sh.sact, (size_t)m, s_pair + P0, m, m, I);
+            } else {
+                stage_rows(smem, act, s_pair, P0, P0, I);   // row pos of the image = pair position pos
+                if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
+            }
             __syncthreads();
         }
 #pragma unroll
@@ -583,6 +717,34 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
 }
 
 template <int CPL>
+__global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
+                                                      const float *__restrict__ wts, const MoeRoute *__restrict__ route,
+                                                      const uint16_t *__restrict__ act, float *__restrict__ y,
+                                                      MoeShared sh) {
+    extern __shared__ uint4 smem[];
+    down_rows_role<CPL, false>(smem, blockIdx.x, e, m, topk, route, nullptr, 0, 0, act, y, sh, nullptr);
+}
+
+// Gate/up and the row-owner down pass in one launch: workgroups [0, g1) are
+// the gate/up tiles (gx per expert column), the rest own kDownRows output
+// rows each.  The down workgroups come after every gate/up workgroup in
+// dispatch order, so the ones they wait for are already running.
+template <int CPLG, int CPLD>
+__global__ __launch_bounds__(256) void k_moe_fused(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+                                                  int m, int E, int topk, nvfp4_moe_weights e,
+                                                  int32_t *__restrict__ ids, float *__restrict__ wts,
+                                                  uint16_t *__restrict__ act, float *__restrict__ y, MoeShared sh,
+                                                  unsigned int *__restrict__ counters, int gx, int g1) {
+    extern __shared__ uint4 smem[];
+    const int b = blockIdx.x;
+    if (b < g1)
+        gate_up_role<CPLG, true>(smem, b % gx, b / gx, gx, x, logits, m, E, topk, e, ids, wts, nullptr, act, sh,
+                                 counters, (int)gridDim.x - g1);
+    else
+        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters);
+}
+
+template <int CPL>
 static int launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weights &e, int m, int topk,
                             const float *wts, const MoeRoute *route, const uint16_t *act, float *y,
                             const MoeShared &sh) {
@@ -593,13 +755,14 @@ static int launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_w
 }
 
 struct MoeLayout {
-    size_t tickets, act, dbuf, total;
+    size_t tickets, sync, act, dbuf, total;
 };
 static MoeLayout moe_layout(int m, int topk, int H, int I) {
     MoeLayout L;
     const size_t pairs = (size_t)m * topk;
     L.tickets = kMoeHeader;
-    L.act = L.tickets + (((size_t)(H + kMoeRows - 1) / kMoeRows * 4 + 255) & ~(size_t)255);
+    L.sync = L.tickets + (((size_t)(H + kMoeRows - 1) / kMoeRows * 4 + 255) & ~(size_t)255);
+    L.act = L.sync + (((size_t)kSyncWords * 4 + (size_t)(H + kDownRows - 1) / kDownRows * kGoStride * 4 + 255) & ~(size_t)255);
     L.dbuf = L.act + ((pairs * I * 2 + 255) & ~(size_t)255);
     L.total = L.dbuf + pairs * H * 4;
     return L;
@@ -621,6 +784,43 @@ static int launch_down(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weight
     if (rc) return rc;
     hipLaunchKernelGGL(k_moe_down<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, dbuf, tickets, y);
     return check_launch("moe_w4a16_gemv(down)");
+}
+
+constexpr int kNotResident = 1;   // launch_fused: the grid does not fit at once (nothing launched)
+
+template <int CPLG, int CPLD>
+static int launch_fused_t(int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
+                          int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act, float *y,
+                          const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+    const void *kern = reinterpret_cast<const void *>(k_moe_fused<CPLG, CPLD>);
+    const int rc = allow_lds(kern, lds, "moe_w4a16_gemv");
+    if (rc) return rc;
+    // the down workgroups only overlap the gate/up pass when every workgroup
+    // of the launch is resident at once
+    if (grid > num_cus() * blocks_per_cu(kern, 256, lds)) return kNotResident;
+    hipLaunchKernelGGL((k_moe_fused<CPLG, CPLD>), dim3(grid), dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, act,
+                       y, sh, counters, gx, g1);
+    return check_launch("moe_w4a16_gemv");
+}
+template <int CPLG>
+static int launch_fused_g(int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m,
+                          int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
+                          float *y, const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+    switch (cpld) {
+        case 1: return launch_fused_t<CPLG, 1>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        case 2: return launch_fused_t<CPLG, 2>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        default: return launch_fused_t<CPLG, 4>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+    }
+}
+static int launch_fused(int cplg, int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits,
+                        int m, int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
+                        float *y, const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+    switch (cplg) {
+        case 1: return launch_fused_g<1>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        case 2: return launch_fused_g<2>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        case 4: return launch_fused_g<4>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        default: return launch_fused_g<0>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+    }
 }
 
 static int cpl_for(int k) {
@@ -679,6 +879,19 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const nvfp4_moe_weights ev = *e;
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kMoeRows - 1) / kMoeRows, maxd);
     const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
+    const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
+    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows
+    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : (size_t)kLdsBytes - 16384;
+    const bool row_owner = pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0;
+    if (row_owner && kMoeFused) {
+        // one launch: gate/up workgroups, then the row-owner down workgroups
+        const int gx = (int)g1.x, ng1 = gx * maxd, ng3 = (H + kDownRows - 1) / kDownRows;
+        const size_t lds = std::max(lds1, pos * I * 2);
+        const int frc = launch_fused(cpl_for(H), cpl_for(I), ng1 + ng3, lds, s, x_bf16, router_logits, m, E, top_k,
+                                     ev, topk_ids, topk_w, act, y, sh, reinterpret_cast<unsigned int *>(ws + L.sync),
+                                     gx, ng1);
+        if (frc != kNotResident) return frc;
+    }
     int rc;
     switch (cpl_for(H)) {
         case 1: rc = launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
@@ -687,10 +900,7 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
         default: rc = launch_gate_up<0>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
     }
     if (rc) return rc;
-    const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
-    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows
-    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : (size_t)kLdsBytes - 16384;
-    if (pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0) {
+    if (row_owner) {
         const dim3 g3((H + kDownRows - 1) / kDownRows);
         const size_t lds3 = pos * I * 2;
         switch (cpl_for(I)) {
