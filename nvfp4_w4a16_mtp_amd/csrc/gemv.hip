@@ -169,9 +169,15 @@ struct EmbedOut {
 // Wavefronts per LM-head workgroup: one workgroup per CU holding as many
 // wavefronts as the kernel's registers leave resident (3 per SIMD up to 170
 // VGPRs, 4 up to 128 for the one-row generic loop, 2 up to 256, 1 beyond).
+#ifndef NVFP4_LM_NW1
+#define NVFP4_LM_NW1 8
+#endif
+#ifndef NVFP4_LM_NW1G
+#define NVFP4_LM_NW1G 16
+#endif
 template <int MT, int CPL>
 constexpr int lm_waves() {
-    return MT == 1 && CPL == 0 ? 16 : MT <= 2 ? 12 : MT == 4 ? 8 : 4;
+    return MT == 1 && CPL == 0 ? NVFP4_LM_NW1G : MT == 1 ? NVFP4_LM_NW1 : MT <= 2 ? 12 : MT == 4 ? 8 : 4;
 }
 
 // Rows per slot of an LM-head unit: one activation row takes 4-row units
