@@ -502,6 +502,13 @@ static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t
     hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, grp, k, bf16);
 }
 
+// Tile target of a GEMV launch: at least this many workgroups per CU (a
+// sweep of 2, 4, 6, 8 and 12 put the q|k|v grouped GEMV at 5.8, 5.3, 4.9,
+// 4.9 and 4.9 us: one tile per workgroup, so more of them keep more loads
+// in flight while the launch ramps up).
+#ifndef NVFP4_GEMV_TPC
+#define NVFP4_GEMV_TPC 6
+#endif
 // One launch over `count` weights with a common K (their tiles concatenated);
 // the tile shape is chosen for the total row count.
 template <int MT>
@@ -510,7 +517,7 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
     const int k = w[0]->k;
     int total_n = 0;
     for (int i = 0; i < count; ++i) total_n += w[i]->n;
-    const TileChoice tc = canonical(choose_tile(total_n, k, MT, 2 * num_cus(), 0));
+    const TileChoice tc = canonical(choose_tile(total_n, k, MT, NVFP4_GEMV_TPC * num_cus(), 0));
     const int rows = 16 * tc.R / tc.KS;
     GemvGroups grp{};
     grp.count = count;

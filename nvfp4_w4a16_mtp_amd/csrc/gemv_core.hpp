@@ -407,6 +407,11 @@ inline TileChoice choose_tile(int n, int k, int mt, int min_tiles, size_t extra_
     for (const auto &o : order) {
         TileChoice c{o[0], o[1], 0};
         if (c.KS > 1 && gemv_lds_bytes(mt, k, c) + extra_lds > (size_t)kLdsBytes) break;
+        // a K split only with a fixed chunk count (the generic loop pipelines
+        // its loads only without a split)
+        if (c.KS > 1 && !(k % (512 * c.KS) == 0 && (k / (512 * c.KS) == 1 || k / (512 * c.KS) == 2 ||
+                                                    k / (512 * c.KS) == 4)))
+            continue;
         pick = c;
         const int rows = 16 * c.R / c.KS;
         if ((n + rows - 1) / rows >= min_tiles) {
