@@ -179,6 +179,34 @@ __device__ __forceinline__ void route_token(const float *__restrict__ lg, int E,
 
 template <int PER>
 __device__ __forceinline__ void moe_route_per(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
+    if (m == 1) {
+        // one token: its top_k experts are the distinct ones; wavefront 0
+        // selects them and ranks them by id (no masks, atomics or
+        // compaction rounds), in the same order as the general path below
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            float my_v;
+            int my_i;
+            route_token<PER>(logits, E, topk, lane, my_v, my_i);
+            const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+            const float ex = lane < topk ? expf(my_v - vmax) : 0.0f;
+            const float den = wave_sum(ex);
+            int rank = 0;
+            for (int j = 0; j < topk; ++j) rank += __builtin_amdgcn_readlane(my_i, j) < my_i;
+            if (lane < topk) {
+                L.sel_i[0][lane] = my_i;
+                L.sel_w[0][lane] = ex / den;
+                MoeExpert &me = L.ex[rank];
+                me.expert = my_i;
+                me.cnt = 1;
+                me.tok[0] = 0;
+                me.pair[0] = lane;
+            }
+            if (lane == 0) L.n_distinct = topk;
+        }
+        __syncthreads();
+        return;
+    }
     for (int e = threadIdx.x; e < E; e += blockDim.x) L.tokmask[e] = 0;
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
