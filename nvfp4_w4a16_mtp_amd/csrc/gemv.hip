@@ -191,6 +191,27 @@ constexpr int lm_rows_per_slot() {
     return MT == 1 && NVFP4_LM_R1 ? 1 : 2;
 }
 
+// Wavefronts per workgroup of the MFMA units (M >= 2, K % 128 == 0), and
+// whether those units are used.
+#ifndef NVFP4_LM_MF_WAVES
+#define NVFP4_LM_MF_WAVES 8
+#endif
+#ifndef NVFP4_LM_MFMA
+#define NVFP4_LM_MFMA 1
+#endif
+constexpr int kLmMfWaves = NVFP4_LM_MF_WAVES;
+#ifndef NVFP4_LM_MF_DEPTH
+#define NVFP4_LM_MF_DEPTH 8
+#endif
+constexpr int kLmMfDepth = NVFP4_LM_MF_DEPTH;   // 128-k steps of code loads in flight per lane
+constexpr bool kLmMfma = NVFP4_LM_MFMA;
+// Fewest activation rows served by the MFMA units.  Their cost per unit does
+// not depend on M (16 rows of which M are used, and an fp32 multiply per
+// dequantized weight that the dot2 units fold into one per 16), while the
+// dot2 units' grows with M: at K = 2048 the MFMA units measure 63-65 us for
+// any M, the dot2 units 41, 55 and 103 us at M = 2, 4 and 8.
+constexpr int kLmMfMinRows = 8;
+
 // Next position in a workgroup's unit sequence: wavefronts draw from an LDS
 // counter (positions 0 .. NW-1 are the wavefronts' first units).
 template <int NW>
@@ -200,17 +221,21 @@ __device__ __forceinline__ int lm_draw(int *q, int lane) {
     return NW + __builtin_amdgcn_readfirstlane(g);
 }
 
-// Combines per-wavefront candidates wb[0..NW)[m] inside one wavefront:
-// lane w * MT + m takes entry (w, m), xor shuffles fold the w bits, and lane
-// m < MT ends with the combination for activation row m.
+// Combines per-wavefront candidates wb[0..NW)[m] inside one wavefront: lane
+// l takes the entries (w, m = l % MT) for w = l / MT, l / MT + 64 / MT, ...,
+// xor shuffles fold the wavefront bits, and lane m < MT ends with the
+// combination for activation row m.
 template <int MT, int NW, bool LP>
 __device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], int lane) {
-    constexpr int NWP = NW <= 4 ? 4 : NW <= 8 ? 8 : 16;
-    static_assert(NWP * MT <= 64 && (MT & (MT - 1)) == 0, "one wavefront holds every (wave, row) entry");
-    const int w = lane / MT, mm = lane % MT;
-    ArgPart c = w < NW ? wb[w][mm] : ArgPart{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
+    static_assert((MT & (MT - 1)) == 0 && MT <= 64, "MT divides the wavefront");
+    constexpr int LW = 64 / MT;                              // wavefronts one pass of the lanes covers
+    constexpr int NWP = NW <= 1 ? 1 : NW <= 2 ? 2 : NW <= 4 ? 4 : NW <= 8 ? 8 : NW <= 16 ? 16 : 32;
+    constexpr int SPAN = NWP < LW ? NWP : LW;                // lane groups holding entries
+    const int w0 = lane / MT, mm = lane % MT;
+    ArgPart c{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
+    for (int w = w0; w < NW; w += LW) argpart_combine<LP>(c, wb[w][mm]);
 #pragma unroll
-    for (int off = NWP * MT / 2; off >= MT; off >>= 1) argpart_shfl_combine<LP>(c, off);
+    for (int off = SPAN * MT / 2; off >= MT; off >>= 1) argpart_shfl_combine<LP>(c, off);
     return c;
 }
 
@@ -221,7 +246,7 @@ __device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], in
 // whichever wavefront is free next (an LDS counter), so wavefronts that the
 // CU's arbitration serves less take fewer units and all of them end
 // together.  The activations are loaded once per workgroup.
-template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW>
+template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW, bool MF = false, bool MASKED = true>
 __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                    int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
@@ -236,8 +261,9 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
     unsigned long long *best = reinterpret_cast<unsigned long long *>(ws + kLmBest);
 
-    constexpr int rows = 4 * R;
+    constexpr int rows = MF ? 16 : 4 * R;
     static_assert(32 % rows == 0, "a unit lies inside one 32-row mask word");
+    static_assert(!MF || MT >= 2, "the MFMA units serve two or more activation rows");
     const int nunits = (v + rows - 1) / rows;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float dec = g->dec;
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     // unit's weights, so it adds no latency to the epilogue.
     const int mrow = min(min(lane & 15, MT - 1), m_rt - 1);
     auto load_mask = [&](int unit) -> uint32_t {
-        if (mask == nullptr) return ~0u;
+        if (!MASKED) return ~0u;   // no mask: no load (an optional load would make the compiler drain every load)
         const int word = (unit * rows) >> 5;
         return word < mask_words ? mask[(size_t)mrow * mask_words + word] : 0u;
     };
@@ -274,7 +300,99 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     };
     const int G = gridDim.x, b0 = blockIdx.x;
     if (threadIdx.x == 0) s_q = 0;
-    if constexpr (MT == 1 && CPL > 0) {
+    // MFMA units: lane (n, q) keeps the best of its rows for activation rows
+    // 4 q + r, r = 0..3 (the scalars above serve the other paths)
+    float mk[4], mv[4], mlm[4], mls[4];
+    int mi[4];
+    uint32_t mw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mk[r] = -INFINITY;
+        mv[r] = -INFINITY;
+        mlm[r] = -INFINITY;
+        mls[r] = 0.0f;
+        mi[r] = INT_MAX;
+        mw[r] = ~0u;
+    }
+    if constexpr (MF) {
+        const int q = lane >> 4;
+        auto epi_mf = [&](int row, int r, float s) {
+            const int mm = 4 * q + r;
+            const float logit = s * dec;
+            float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
+            if (row == 0) st_dev(&row0[mm], logit);
+            if (!((mw[r] >> (row & 31)) & 1u)) key = -INFINITY;
+            if constexpr (LP) {
+                if (key != -INFINITY) lse_merge(mlm[r], mls[r], key, 1.0f);
+            }
+            if (beats(key, row, mk[r], mi[r])) {
+                mk[r] = key;
+                mv[r] = logit;
+                mi[r] = row;
+            }
+        };
+        stage_x_mf(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __syncthreads();
+        // the code loads run kLmMfDepth steps ahead as one stream across the
+        // wavefront's units (the launch keeps the step count a multiple of
+        // the depth); past its last unit the stream reads unit 0, unused
+        constexpr int D = kLmMfDepth;
+        const int li = lane & 15, cpr = k >> 3, S = k >> 7;
+        int u = b0 + G * wave;
+        int un = b0 + G * lm_draw<NW>(&s_q, lane);
+        MfRow cur = mf_row(codes, scales, v, k, (u < nunits ? u : 0) * rows, li, q);
+        MfRow nxt = mf_row(codes, scales, v, k, (un < nunits ? un : 0) * rows, li, q);
+        const uint4 *xa[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xa[b] = mf_xrow(xs, cpr, MT, li, q, b);
+        uint4 cw[D];
+        uint32_t sw[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            cw[d] = ld_stream16(cur.cp + 64 * (size_t)d);
+            sw[d] = ld_stream2(cur.sp + 8 * (size_t)d);
+            __builtin_amdgcn_sched_barrier(0);   // same issue order as the loop's reloads
+        }
+        while (u < nunits) {
+            if constexpr (MASKED) {
+                const int word = (u * rows) >> 5;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int mm = min(min(4 * q + r, MT - 1), m_rt - 1);
+                    mw[r] = word < mask_words ? mask[(size_t)mm * mask_words + word] : 0u;
+                }
+            }
+            f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s0 = 0; s0 < S; s0 += D) {
+                // this round reloads steps s0 + D .. s0 + 2 D - 1: of this
+                // unit, or in the last round steps 0 .. D - 1 of the next
+                const bool last = s0 + D >= S;
+                const uint8_t *lc = last ? nxt.cp : cur.cp + 64 * (size_t)(s0 + D);
+                const uint8_t *ls = last ? nxt.sp : cur.sp + 8 * (size_t)(s0 + D);
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    uint4 a[4], bw[4];
+                    mf_xload(xa, s0 + d, a);
+                    mf_dequant(cw[d], sw[d], bw);
+                    cw[d] = ld_stream16(lc + 64 * d);
+                    sw[d] = ld_stream2(ls + 8 * d);
+                    // the reload stays right after the dequantization: sunk
+                    // to the end of the round, every step of the next round
+                    // would wait for it
+                    __builtin_amdgcn_sched_barrier(0);
+                    mf_mma(a, bw, acc0, acc1);
+                }
+            }
+            const int rowu = u * rows + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * q + r < MT && rowu < v) epi_mf(rowu, r, acc0[r] + acc1[r]);
+            u = un;
+            cur = nxt;
+            un = b0 + G * lm_draw<NW>(&s_q, lane);
+            nxt = mf_row(codes, scales, v, k, (un < nunits ? un : 0) * rows, li, q);
+        }
+    } else if constexpr (MT == 1 && CPL > 0) {
         // one activation row: it lives in registers; the next unit's loads
         // are in flight while this one is computed
         int q = wave, u = b0 + G * q;
@@ -348,7 +466,17 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
 
     // workgroup combine: the four slots of a wavefront by shuffles, then the
     // NW wavefronts in LDS -> MT candidates
-    {
+    if constexpr (MF) {
+        // rows 4 q + r: fold the 16 lanes of group q
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ArgPart c{mk[r], mv[r], mi[r], mlm[r], mls[r], {0, 0, 0}};
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) argpart_shfl_combine<LP>(c, off);
+            const int mm = 4 * (lane >> 4) + r;
+            if ((lane & 15) == 0 && mm < MT) wbest[wave][mm] = c;
+        }
+    } else {
         ArgPart c{b_key, b_val, b_idx, b_lm, b_ls, {0, 0, 0}};
         argpart_shfl_combine<LP>(c, 16);
         argpart_shfl_combine<LP>(c, 32);
@@ -541,12 +669,13 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
 
 // Grid of the persistent LM-head kernel: every workgroup that is resident at
 // once (normally one per CU), never more than the workspace has partials for.
-template <int MT, int CPL, bool BK, bool LP>
+template <int MT, int CPL, bool BK, bool LP, bool MF = false>
 static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
                              char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words,
                              const EmbedOut &emb) {
-    constexpr int NW = lm_waves<MT, CPL>();
-    auto kern = k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW>;
+    constexpr int NW = MF ? kLmMfWaves : lm_waves<MT, CPL>();
+    auto kern = mask != nullptr ? k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW, MF, true>
+                                : k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW, MF, false>;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
     const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kern), 64 * NW, lds);
     if (per_cu < 1) {
@@ -568,7 +697,15 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
     ok();   // clears the message that a refused LDS request would leave
-    if (tc.CPL == 4) {
+    if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
+        if constexpr (MT >= kLmMfMinRows) {
+            const size_t lmf = (size_t)MT * w->k * 2;
+            if (bk) lp ? launch_lm_kernel<MT, 0, true, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                       : launch_lm_kernel<MT, 0, true, false, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
+            else lp ? launch_lm_kernel<MT, 0, false, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
+                    : launch_lm_kernel<MT, 0, false, false, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
+        }
+    } else if (tc.CPL == 4) {
         if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
                    : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
         else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)

@@ -381,6 +381,91 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
     gemv_tile_finish<MT, R, KS, 0, WT>(acc, n, row0, red, epi);
 }
 
+// ------------------------------------------------------------ MFMA path ----
+// For M >= 2 activation rows a unit of 16 weight rows is one wavefront's
+// v_mfma_f32_16x16x32_bf16 tile: B = the 16 rows dequantized exactly to bf16,
+// A = the activation rows, padded to 16 with zeros.  Lane (n = l % 16,
+// q = l / 16) covers, in 128-k step s, the k = 128 s + 32 q .. + 31 of row n:
+// one 16-byte code chunk and its two scale bytes.  Inside a step the MFMA k
+// order is chosen so that block b takes k = 128 s + 32 q + 8 b .. + 7 from
+// every lane group q; each block still sums 32 products of the row, and the
+// activations are read from LDS in the same order.  The result C[m][n]
+// leaves lane (n, q) as rows m = 4 q + r, r = 0..3.
+
+// Activation image of the MFMA path: row m is K / 8 chunks of 16 bytes,
+// chunk c stored at c ^ (m % 8), so that the rows a lane group reads at one
+// chunk hit different bank groups.  K % 128 == 0.
+__device__ __forceinline__ void stage_x_mf(uint4 *xs, const uint4 *__restrict__ x, int m_rt, int mt, int k) {
+    const int cpr = k >> 3;
+    for (int p = threadIdx.x; p < mt * cpr; p += blockDim.x) {
+        const int m = p / cpr, c = p - m * cpr;
+        xs[m * cpr + (c ^ (m & 7))] = m < m_rt ? x[p] : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Two E2M1 codes (byte SEL of word) times sf as two bf16 (exact: e2m1 times
+// an E4M3 scale has at most 6 significant bits).
+template <int SEL>
+__device__ __forceinline__ uint32_t mf_dq2(uint32_t word, float sf) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+    const uint32_t lo = __float_as_uint(f.x * sf), hi = __float_as_uint(f.y * sf);
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+// One 128-k step in two halves.  mf_dequant: the lane's code chunk and
+// scale bytes as the four bf16x8 B blocks; mf_mma: the activation rows
+// against them (lanes n >= MT read row n % MT and zero it), four MFMAs into
+// two accumulators (blocks 0, 2 and 1, 3).  Split so that the registers of
+// the chunk can be reloaded between the halves.
+__device__ __forceinline__ void mf_dequant(uint4 cw, uint32_t sw, uint4 (&bw)[4]) {
+    float sf0, sf1;
+    e4m3x2_to_f32(sw, sf0, sf1);
+    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float sf = b < 2 ? sf0 : sf1;
+        bw[b] = make_uint4(mf_dq2<0>(w[b], sf), mf_dq2<1>(w[b], sf), mf_dq2<2>(w[b], sf), mf_dq2<3>(w[b], sf));
+    }
+}
+
+// xa[b]: block b of this lane's activation row in LDS (mf_xrow); lanes
+// n >= MT read row n % MT, whose products land in output rows >= MT that are
+// never read.  Read apart from the MFMAs so that the four LDS reads are in
+// flight together.
+__device__ __forceinline__ void mf_xload(const uint4 *const (&xa)[4], int s, uint4 (&a)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) a[b] = xa[b][16 * s];
+}
+
+__device__ __forceinline__ void mf_mma(const uint4 (&a)[4], const uint4 (&bw)[4], f32x4 &acc0, f32x4 &acc1) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f32x4 &acc = (b & 1) ? acc1 : acc0;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[b]), __builtin_bit_cast(bf16x8, bw[b]),
+                                                    acc, 0, 0, 0);
+    }
+}
+
+// Chunk 16 s + 4 q + b of lane (n, q)'s activation row sits at
+// mf_xrow(..., b)[16 s]: the swizzle c ^ (m % 8) only touches the low three
+// bits of c, so it is folded into one base per block.
+__device__ __forceinline__ const uint4 *mf_xrow(const uint4 *xs, int cpr, int mt, int li, int q, int b) {
+    const int xr = li & (mt - 1);
+    return xs + xr * cpr + ((4 * q + b) ^ (xr & 7));
+}
+
+// Code and scale pointers of lane (n, q) for a 16-row unit at row0 (rows
+// past n read row n - 1, never passed on): step s at + 64 s and + 8 s.
+struct MfRow {
+    const uint8_t *cp, *sp;
+};
+__device__ __forceinline__ MfRow mf_row(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int n,
+                                        int k, int row0, int li, int q) {
+    const int row = min(row0 + li, n - 1);
+    return MfRow{codes + (size_t)row * (size_t)(k >> 1) + 16 * q, scales + (size_t)row * (size_t)(k >> 4) + 2 * q};
+}
+
 // ---------------------------------------------------------------- host ----
 struct TileChoice {
     int R, KS, CPL;   // CPL 0: generic loop

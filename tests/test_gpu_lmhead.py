@@ -63,6 +63,16 @@ def test_random_unplanted(orc, m):
     _check_certified(orc, h, codes, scales, glob[0])
 
 
+@pytest.mark.parametrize("m,v,k", [(5, 3001, 1024), (7, 1000, 3072), (8, 17, 2048), (6, 4096, 7168)])
+def test_random_unplanted_eight_row_units(orc, m, v, k):
+    """Five to eight rows with K a multiple of 1024 (16-row MFMA units):
+    ragged vocabularies, rows padded to eight."""
+    w = synth.weight_bf16(60 + m, v, k)
+    h = synth.acts_bf16(60 + m, m, k)
+    codes, scales, glob = orc.quantize(w)
+    _check_certified(orc, h, codes, scales, glob[0])
+
+
 @pytest.mark.parametrize("vocab", [32768, 151936])
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_config_planted_near_ties(orc, vocab, m):
