@@ -3,21 +3,25 @@
 // NVFP4 weights dequantized exactly to bf16, bf16 matrix products, fp32
 // accumulation, activations never quantized.  y[m][n] = sum_k x[m][k] W^[n][k].
 //
-// gfx950 design: a 128 x 128 output tile per workgroup (4 wavefronts, each
-// 64 x 64 = 4 x 4 blocks of v_mfma_f32_16x16x32_bf16), K in steps of 64.
-// Per step the workgroup stages the 128 x 64 activation tile and the
-// 128 x 64 weight tile in LDS; the weight tile is dequantized on the way in
-// (hardware E2M1 -> fp32 convert, times the E4M3 block scale, packed to
-// bf16 -- exact, since e2m1 * e4m3 has at most 6 significant bits).  The
-// next step's global loads are issued before the current step's MFMAs.
-// LDS chunks are XOR-swizzled (lds_off) to spread the rows of an operand
-// load and of a staging store over the banks.  The global scale is
-// applied in the epilogue.
+// gfx950 design: a 128- or 256-row by 128-column output tile per workgroup
+// (4 or 8 wavefronts, each 64 x 64 = 4 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16), K in steps of 64.  Per step the workgroup
+// stages the activation tile and the 128 x 64 weight tile in LDS; the
+// weight tile is dequantized on the way in (hardware E2M1 -> fp32 convert,
+// times the E4M3 block scale, packed to bf16 -- exact, since e2m1 * e4m3 has
+// at most 6 significant bits).  The next step's global loads are issued
+// before the current step's MFMAs.  LDS chunks are XOR-swizzled (lds_off)
+// to spread the rows of an operand load and of a staging store over the
+// banks.  The global scale is applied in the epilogue.
+//
+// The dequantization runs on the same SIMDs as the MFMAs and the two hardly
+// overlap (timed: 4 MFMAs and 32 fp32 multiplies per wavefront cost close to
+// the sum of either alone), so its share is what the tile height sets.
 #include "common.hpp"
 
 namespace nvfp4 {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBN = 128, kBK = 64;
 constexpr int kLdsRow = kBK * 2;   // bytes per LDS row (64 bf16 of one K step)
 
 // Byte offset of 16-byte chunk c (8 bf16) of tile row r in LDS.  The chunk is
@@ -35,32 +39,44 @@ __device__ __forceinline__ uint32_t dq2(uint32_t word, float sf) {
     return __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // upper halves: exact bf16
 }
 
-template <bool BF16OUT>
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
-                                             const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                             int M, int N, int K, void *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[kBM * kLdsRow];
+// BM x 128 output tile per workgroup: BM / 64 x 2 wavefronts of 64 x 64.
+// The weight tile is dequantized once per workgroup, so a taller tile
+// spends fewer dequantization instructions per MFMA (a BM = 256 tile half as
+// many as BM = 128); each of the 2 BM threads stages one half row of the
+// activation tile and 8192 / (2 BM) weights.  Tall tiles raise the wave
+// priority over their MFMA phase, so that the CU's other workgroup stages
+// in the gaps (measured +1-5% at 8192 rows; it slowed the 128-row tile).
+template <int BM, bool BF16OUT>
+__global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 4 : 3))) void k_gemm(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
+                                                int M, int N, int K, void *__restrict__ y) {
+    constexpr int NT = 2 * BM;          // threads
+    constexpr int BPR = NT / kBN;       // weight staging parts per tile row: 2 or 4
+    constexpr int CPT = 64 / BPR / 8;   // code dwords (8 codes each) per thread: 4 or 2
+    static_assert(BPR == 2 || BPR == 4, "BM is 128 or 256");
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsRow];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBN * kLdsRow];
 
     const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kBN;
 
-    // staging role: row th/2 of both tiles, half th%2 (32 k) of the K step
+    // staging roles: activation row th / 2, half th % 2 (32 k) of the K step;
+    // weight row th / BPR, part th % BPR (64 / BPR k)
     const int srow = th >> 1, shalf = th & 1;
-    const int xm = m0 + srow, wnr = n0 + srow;
+    const int brow = th / BPR, bpart = th % BPR;
+    const int xm = m0 + srow, wnr = n0 + brow;
     const bool xval = xm < M, wval = wnr < N;
     const uint16_t *xrow = x + (size_t)(xval ? xm : 0) * K;
     const uint8_t *crow = codes + (size_t)(wval ? wnr : 0) * (K >> 1);
     const uint8_t *srow_p = scales + (size_t)(wval ? wnr : 0) * (K >> 4);
 
     uint4 xr[4];
-    uint4 cr;
+    uint32_t cr[CPT];
     uint32_t sr;
     auto load_step = [&](int k0) {
         const int kk = k0 + 32 * shalf;
-        const bool kin = kk < K;
-        if (xval && kin) {
+        if (xval && kk < K) {
             const uint4 *p = reinterpret_cast<const uint4 *>(xrow + kk);
             xr[0] = p[0];
             xr[1] = p[1];
@@ -69,11 +85,24 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
         } else {
             xr[0] = xr[1] = xr[2] = xr[3] = make_uint4(0, 0, 0, 0);
         }
-        if (wval && kin) {
-            cr = *reinterpret_cast<const uint4 *>(crow + (kk >> 1));
-            sr = *reinterpret_cast<const uint16_t *>(srow_p + (kk >> 4));
+        const int kb = k0 + (64 / BPR) * bpart;
+        if (wval && kb < K) {
+            if constexpr (CPT == 4) {
+                const uint4 c = *reinterpret_cast<const uint4 *>(crow + (kb >> 1));
+                cr[0] = c.x;
+                cr[1] = c.y;
+                cr[2] = c.z;
+                cr[3] = c.w;
+                sr = *reinterpret_cast<const uint16_t *>(srow_p + (kb >> 4));
+            } else {
+                const uint2 c = *reinterpret_cast<const uint2 *>(crow + (kb >> 1));
+                cr[0] = c.x;
+                cr[1] = c.y;
+                sr = srow_p[kb >> 4];
+            }
         } else {
-            cr = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int d = 0; d < CPT; ++d) cr[d] = 0;
             sr = 0;
         }
     };
@@ -92,17 +121,16 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
             for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4 *>(lds_a + lds_off(srow, 4 * shalf + q)) = xr[q];
             typedef __attribute__((ext_vector_type(2))) float f32x2;
             const f32x2 sfv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sr, false);   // E4M3 block scales, exact
-            const float sf0 = sfv.x, sf1 = sfv.y;
-            const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const float sf = d < 2 ? sf0 : sf1;
-                *reinterpret_cast<uint4 *>(lds_b + lds_off(srow, 4 * shalf + d)) =
-                    make_uint4(dq2<0>(cw[d], sf), dq2<1>(cw[d], sf), dq2<2>(cw[d], sf), dq2<3>(cw[d], sf));
+            for (int d = 0; d < CPT; ++d) {
+                const float sf = (CPT == 4 && d >= 2) ? sfv.y : sfv.x;   // 16 codes per scale
+                *reinterpret_cast<uint4 *>(lds_b + lds_off(brow, CPT * bpart + d)) =
+                    make_uint4(dq2<0>(cr[d], sf), dq2<1>(cr[d], sf), dq2<2>(cr[d], sf), dq2<3>(cr[d], sf));
             }
         }
         __syncthreads();
         if (k0 + kBK < K) load_step(k0 + kBK);
+        if constexpr (BM == 256) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 af[4], bfr[4];
@@ -117,6 +145,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
+        if constexpr (BM == 256) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
 
@@ -140,6 +169,26 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ x, co
         }
 }
 
+// Tile choice by rounds of resident workgroups: a 256-row round (2 per CU)
+// takes about kTallRound times a 128-row round (3 per CU) -- measured at
+// 8192 x 17408 x 5120, where both fill the chip: 919 against 815 TFLOP/s,
+// 2 x 256 / 919 over 3 x 128 / 815.  A partly filled last round costs a
+// full one, so e.g. 1024 x 17408 (544 tall tiles, 2 rounds) keeps the
+// 128-row tile (1088 tiles, 2 rounds).
+#ifndef NVFP4_GEMM_TALL_ROUND
+#define NVFP4_GEMM_TALL_ROUND 1.18
+#endif
+constexpr double kTallRound = NVFP4_GEMM_TALL_ROUND;
+
+template <int BM>
+static void launch_gemm(const uint16_t *x, int m, const nvfp4_weight *w, void *y, bool bf16, hipStream_t s) {
+    dim3 grid((w->n + kBN - 1) / kBN, (m + BM - 1) / BM);
+    if (bf16)
+        hipLaunchKernelGGL((k_gemm<BM, true>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n, w->k, y);
+    else
+        hipLaunchKernelGGL((k_gemm<BM, false>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n, w->k, y);
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -155,13 +204,17 @@ extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_we
         return fail(NVFP4_ERR_ARG, "w4a16_gemm_m128: unknown y_dtype %d", y_dtype);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: x not 16-byte aligned");
     if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: y not 4-byte aligned");
-    if ((w->n + kBN - 1) / kBN > 2147483647 || (m + kBM - 1) / kBM > 65535)
+    if ((w->n + kBN - 1) / kBN > 2147483647 || (m + 127) / 128 > 65535)
         return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemm_m128: grid too large");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    dim3 grid((w->n + kBN - 1) / kBN, (m + kBM - 1) / kBM);
-    if (y_dtype == NVFP4_OUT_BF16)
-        hipLaunchKernelGGL(k_gemm<true>, grid, dim3(256), 0, s, x_bf16, w->codes, w->scales, w->global, m, w->n, w->k, y);
+    const long cols = (w->n + kBN - 1) / kBN;
+    const long slots_s = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<128, false>), 256, 0);
+    const long slots_t = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<256, false>), 512, 0);
+    const long rounds_s = (cols * ((m + 127) / 128) + slots_s - 1) / slots_s;
+    const long rounds_t = (cols * ((m + 255) / 256) + slots_t - 1) / slots_t;
+    if (kTallRound * rounds_t < rounds_s)
+        launch_gemm<256>(x_bf16, m, w, y, y_dtype == NVFP4_OUT_BF16, s);
     else
-        hipLaunchKernelGGL(k_gemm<false>, grid, dim3(256), 0, s, x_bf16, w->codes, w->scales, w->global, m, w->n, w->k, y);
+        launch_gemm<128>(x_bf16, m, w, y, y_dtype == NVFP4_OUT_BF16, s);
     return check_launch("w4a16_gemm_m128");
 }

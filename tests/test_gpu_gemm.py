@@ -17,8 +17,10 @@ def _w(codes, scales, g_dec):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (128, 128, 64), (200, 384, 512), (77, 130, 96), (300, 512, 2048),
-                                   (512, 128, 64), (600, 200, 96), (1000, 384, 2048)])
+                                   (512, 128, 64), (600, 200, 96), (1000, 384, 2048),
+                                   (300, 32728, 96), (257, 65536, 64)])
 def test_exact_family_bit_exact(orc, m, n, k):
+    """The last two shapes have 512 or more 256-row tiles: 256-row workgroups."""
     import nvfp4_w4a16_mtp_amd as nv
     x, codes, scales, g = synth.exact_family(200 + m, m, n, k)
     y = nv.w4a16_gemm_m128(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
@@ -26,7 +28,7 @@ def test_exact_family_bit_exact(orc, m, n, k):
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,n,k", [(128, 2048, 4096), (257, 512, 2048), (777, 640, 1024)])
+@pytest.mark.parametrize("m,n,k", [(128, 2048, 4096), (257, 512, 2048), (777, 640, 1024), (513, 22000, 1024)])
 def test_random_full(orc, m, n, k):
     import nvfp4_w4a16_mtp_amd as nv
     w = synth.weight_bf16(300 + n, n, k)
