@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--m", type=int, default=1, help="decode rows per step (1..8)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="only time the prefill GEMM at every prompt-chunk shape (one JSON line)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
     return p.parse_args()
@@ -72,6 +74,10 @@ def main():
         return
     import nvfp4_w4a16_mtp_amd as nv
     nv.lib()
+    if a.gemm_only:
+        s = torch.cuda.Stream()
+        print(json.dumps({"prefill_gemm": gemm_rows(nv, torch, torch.device("cuda:0"), s, GEMM_SHAPES)}), flush=True)
+        return
     M = a.m
     assert 1 <= M <= 8
     dev = torch.device("cuda:0")
@@ -354,13 +360,27 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
     nvfp4_lay = nvfp4_bytes(E, H) + 3 * nvfp4_bytes(I, H)
     out["moe_layer_router_shared"] = {"ms": round(ms, 5), "extra_weight_bytes": nvfp4_lay}
     del lay
-    # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120) at M = 1024
-    gen = torch.Generator(device=hl.device)
+    # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120)
+    out.update(gemm_rows(nv, torch, hl.device, s, (("fc", 2048, 4096, 1024), ("gate_up", 17408, 5120, 1024),
+                                                   ("gate_up", 17408, 5120, 8192))))
+    return out
+
+
+# prefill GEMM shapes: (name, N, K, M) -- prompt chunks of 128, 1024 and 8192
+# rows through the fc, k/v and the dense-head FFN projections
+GEMM_SHAPES = tuple((name, n, k, m) for name, n, k in (("fc", 2048, 4096), ("kv", 512, 2048), ("gate_up", 17408, 5120),
+                                                      ("down", 5120, 17408)) for m in (128, 1024, 8192))
+
+
+def gemm_rows(nv, torch, dev, s, shapes):
+    """Back-to-back launch time of w4a16_gemm_m128 (bf16 output) per shape."""
+    out = {}
+    gen = torch.Generator(device=dev)
     gen.manual_seed(1)
-    for name, n, k, m in (("fc", 2048, 4096, 1024), ("gate_up", 17408, 5120, 1024), ("gate_up", 17408, 5120, 8192)):
-        w = nv.nvfp4_quantize((torch.randn((n, k), generator=gen, device=hl.device) * 0.02).to(torch.bfloat16))
-        x = torch.randn((m, k), generator=gen, device=hl.device).to(torch.bfloat16)
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=hl.device)
+    for name, n, k, m in shapes:
+        w = nv.nvfp4_quantize((torch.randn((n, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16))
+        x = torch.randn((m, k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ms = _time(torch, lambda i: nv.w4a16_gemm_m128(x, w, out=y), 10, s)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         out[f"gemm_{name}_m{m}"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}

@@ -158,13 +158,23 @@ int w4a16_gemv_grouped(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
  * `w4a16_gemm_m128_dispatch` of [prefill.rs] in its lossless form (NVFP4 ->
  * bf16 dequantization, bf16 matrix products, fp32 accumulation; activations
  * are never quantized).  y[m][n] = sum_k x[m][k] * W^[n][k].
- *   x_bf16  [m][w->k] bf16, 16-byte aligned; m >= 1 (any m; work is tiled in
- *           128-row blocks, a ragged last block is masked).
- *   y       [m][w->n] fp32 or bf16 (y_dtype), 4-byte aligned.
- * Any n >= 0; rows and columns outside the 128 x 128 tiles are masked.
+ *   x_bf16     [m][w->k] bf16, 16-byte aligned; m >= 1 (any m; work is tiled
+ *              in 128- or 256-row blocks, a ragged last block is masked).
+ *   y          [m][w->n] fp32 or bf16 (y_dtype), 4-byte aligned.
+ *   workspace  NULL, or 16-byte aligned device scratch of at least
+ *              w4a16_gemm_m128_workspace_bytes(m, w->n, w->k) bytes.  When
+ *              the output tiles are too few to fill the device, K is cut
+ *              into slices whose fp32 partial sums go to the workspace and
+ *              are added in slice order by a second kernel (the same order
+ *              on every call).  NULL: one pass over K.  Nothing needs to be
+ *              initialised; calls that overlap on one workspace race.
+ * Any n >= 0; rows and columns outside the tiles are masked.  Errors:
+ * NVFP4_ERR_WORKSPACE for a non-NULL workspace below the size needed, and
+ * those of w4a16_gemv.
  */
+size_t w4a16_gemm_m128_workspace_bytes(int32_t m, int32_t n, int32_t k);
 int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
-                    int32_t y_dtype, void *stream);
+                    int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * lmhead_gemv_argmax -- LM-head GEMV over the first V vocabulary rows fused

@@ -59,7 +59,9 @@ def lib():
         L.nvfp4_quantize.argtypes = [P, i32, i32, P, P, P, P]
         L.w4a16_gemv.argtypes = [P, i32, WP, P, i32, P]
         L.w4a16_gemv_grouped.argtypes = [P, i32, ctypes.POINTER(WP), ctypes.POINTER(P), i32, i32, P]
-        L.w4a16_gemm_m128.argtypes = [P, i32, WP, P, i32, P]
+        L.w4a16_gemm_m128_workspace_bytes.argtypes = [i32, i32, i32]
+        L.w4a16_gemm_m128_workspace_bytes.restype = sz
+        L.w4a16_gemm_m128.argtypes = [P, i32, WP, P, i32, P, sz, P]
         L.lmhead_gemv_argmax_workspace_bytes.argtypes = [i32, i32]
         L.lmhead_gemv_argmax_workspace_bytes.restype = sz
         L.lmhead_gemv_argmax.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P]
@@ -223,15 +225,34 @@ def w4a16_gemv_grouped(x: torch.Tensor, ws, out_dtype=torch.float32, outs=None):
     return outs
 
 
-def w4a16_gemm_m128(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: torch.Tensor | None = None):
+def gemm_workspace(m: int, n: int, k: int, device) -> torch.Tensor | None:
+    """Workspace for w4a16_gemm_m128 at m x n x k on `device` (None when the
+    call needs none: its output tiles fill the device)."""
+    with torch.cuda.device(device):
+        nbytes = lib().w4a16_gemm_m128_workspace_bytes(m, n, k)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def w4a16_gemm_m128(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, split_k: bool = True):
+    """y = x @ W^T.  Short prompt chunks split K over a workspace (allocated
+    here when none is given); split_k=False runs one pass over K."""
     x = _as_bf16(x)
     _dev(x, "x")
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    if split_k and workspace is None:
+        workspace = gemm_workspace(m, w.n, w.k, x.device)
+    if not split_k:
+        workspace = None
+    if workspace is not None:
+        _dev(workspace, "workspace")
     d = w.desc()
-    _check(lib().w4a16_gemm_m128(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype), _stream(x)),
-           "w4a16_gemm_m128")
+    _check(lib().w4a16_gemm_m128(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype),
+                                 _ptr(workspace) if workspace is not None else None,
+                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                 _stream(x)), "w4a16_gemm_m128")
     return out
 
 

@@ -14,6 +14,11 @@
 // to spread the rows of an operand load and of a staging store over the
 // banks.  The global scale is applied in the epilogue.
 //
+// Prompt chunks too short to fill the chip with output tiles (a few hundred
+// rows) split K over up to 16 workgroups per tile, which write fp32 partial
+// planes to the caller's workspace; a second kernel sums them in slice order
+// and applies the global scale.
+//
 // The dequantization runs on the same SIMDs as the MFMAs and the two hardly
 // overlap (timed: 4 MFMAs and 32 fp32 multiplies per wavefront cost close to
 // the sum of either alone), so its share is what the tile height sets.
@@ -46,10 +51,15 @@ __device__ __forceinline__ uint32_t dq2(uint32_t word, float sf) {
 // activation tile and 8192 / (2 BM) weights.  Tall tiles raise the wave
 // priority over their MFMA phase, so that the CU's other workgroup stages
 // in the gaps (measured +1-5% at 8192 rows; it slowed the 128-row tile).
-template <int BM, bool BF16OUT>
-__global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 4 : 3))) void k_gemm(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
-                                                const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
-                                                int M, int N, int K, void *__restrict__ y) {
+// K split: slice z = blockIdx.z of gridDim.z takes the K steps
+// [z S / Z, (z + 1) S / Z) of the S = ceil(K / 64) and, with PART, writes
+// its fp32 sums without the global scale to plane z of `part` (row-major
+// [M][N] planes, `plane` floats apart) for k_gemm_reduce.
+template <int BM, bool BF16OUT, bool PART>
+__global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 4 : 3))) void k_gemm(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+    const nvfp4_global *__restrict__ g, int M, int N, int K, void *__restrict__ y, float *__restrict__ part,
+    size_t plane) {
     constexpr int NT = 2 * BM;          // threads
     constexpr int BPR = NT / kBN;       // weight staging parts per tile row: 2 or 4
     constexpr int CPT = 64 / BPR / 8;   // code dwords (8 codes each) per thread: 4 or 2
@@ -113,8 +123,10 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    load_step(0);
-    for (int k0 = 0; k0 < K; k0 += kBK) {
+    const int steps = (K + kBK - 1) / kBK, nz = gridDim.z, z = blockIdx.z;
+    const int kb0 = (int)((long)z * steps / nz) * kBK, kb1 = min(K, (int)((long)(z + 1) * steps / nz) * kBK);
+    if (kb0 < kb1) load_step(kb0);
+    for (int k0 = kb0; k0 < kb1; k0 += kBK) {
         // stage: activations as they are, weights dequantized
         {
 #pragma unroll
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
             }
         }
         __syncthreads();
-        if (k0 + kBK < K) load_step(k0 + kBK);
+        if (k0 + kBK < kb1) load_step(k0 + kBK);
         if constexpr (BM == 256) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -149,7 +161,8 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
         __syncthreads();
     }
 
-    const float dec = g->dec;
+    const float dec = PART ? 1.0f : g->dec;
+    float *pz = PART ? part + (size_t)z * plane : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -160,13 +173,46 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
                 const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
                 if (m < M && n < N) {
                     const float o = acc[i][j][r] * dec;
-                    if constexpr (BF16OUT)
+                    if constexpr (PART)
+                        pz[(size_t)m * N + n] = o;
+                    else if constexpr (BF16OUT)
                         reinterpret_cast<uint16_t *>(y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(o);
                     else
                         reinterpret_cast<float *>(y)[(size_t)m * N + n] = o;
                 }
             }
         }
+}
+
+// Sum of the K-slice partials of each output in slice order (the same
+// order on every call), times the global scale, as fp32 or bf16.  Planes are
+// padded to a multiple of 4 floats, so the float4 reads of a last group stay
+// inside the plane.
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ part, size_t plane, int nz,
+                                                     size_t count, const nvfp4_global *__restrict__ g,
+                                                     void *__restrict__ y) {
+    const float dec = g->dec;
+    const size_t stride = (size_t)gridDim.x * 256 * 4;
+    for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; e < count; e += stride) {
+        float4 a = *reinterpret_cast<const float4 *>(part + e);
+        for (int z = 1; z < nz; ++z) {
+            const float4 b = *reinterpret_cast<const float4 *>(part + (size_t)z * plane + e);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        const float v[4] = {a.x * dec, a.y * dec, a.z * dec, a.w * dec};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (e + c >= count) break;
+            if constexpr (BF16OUT)
+                reinterpret_cast<uint16_t *>(y)[e + c] = (uint16_t)f32_to_bf16_bits(v[c]);
+            else
+                reinterpret_cast<float *>(y)[e + c] = v[c];
+        }
+    }
 }
 
 // Tile choice by rounds of resident workgroups: a 256-row round (2 per CU)
@@ -179,22 +225,65 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
 #define NVFP4_GEMM_TALL_ROUND 1.18
 #endif
 constexpr double kTallRound = NVFP4_GEMM_TALL_ROUND;
+constexpr int kMaxSplit = 16;       // K slices at most
+constexpr int kMinSliceSteps = 4;   // 64-k steps per slice at least
 
-template <int BM>
-static void launch_gemm(const uint16_t *x, int m, const nvfp4_weight *w, void *y, bool bf16, hipStream_t s) {
-    dim3 grid((w->n + kBN - 1) / kBN, (m + BM - 1) / BM);
+struct GemmPlan {
+    int bm;       // 128 or 256
+    int split;    // K slices (128-row tiles only)
+    size_t plane; // floats per partial plane (split > 1)
+};
+
+// 256-row tiles where they take fewer rounds; else 128-row tiles, with K cut
+// into slices when the tiles fill less than one round of resident
+// workgroups (prompt chunks of a few hundred rows): then up to kMaxSplit
+// slices bring the grid to about one round.
+static GemmPlan gemm_plan(int m, int n, int k) {
+    const long cols = (n + kBN - 1) / kBN;
+    const long slots_s = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<128, false, false>), 256, 0);
+    const long slots_t = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<256, false, false>), 512, 0);
+    const long tiles_s = cols * ((m + 127) / 128), tiles_t = cols * ((m + 255) / 256);
+    const long rounds_s = (tiles_s + slots_s - 1) / slots_s, rounds_t = (tiles_t + slots_t - 1) / slots_t;
+    GemmPlan p{128, 1, 0};
+    if (kTallRound * rounds_t < rounds_s) {
+        p.bm = 256;
+        return p;
+    }
+    const long steps = (k + kBK - 1) / kBK;
+    long split = slots_s / (tiles_s > 0 ? tiles_s : 1);
+    split = split < kMaxSplit ? split : kMaxSplit;
+    split = split < steps / kMinSliceSteps ? split : steps / kMinSliceSteps;
+    if (split >= 2) {
+        p.split = (int)split;
+        p.plane = ((size_t)m * n + 3) & ~(size_t)3;
+    }
+    return p;
+}
+
+template <int BM, bool PART>
+static void launch_gemm(const uint16_t *x, int m, const nvfp4_weight *w, void *y, bool bf16, float *part, size_t plane,
+                        int split, hipStream_t s) {
+    dim3 grid((w->n + kBN - 1) / kBN, (m + BM - 1) / BM, split);
     if (bf16)
-        hipLaunchKernelGGL((k_gemm<BM, true>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n, w->k, y);
+        hipLaunchKernelGGL((k_gemm<BM, true, PART>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m,
+                           w->n, w->k, y, part, plane);
     else
-        hipLaunchKernelGGL((k_gemm<BM, false>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n, w->k, y);
+        hipLaunchKernelGGL((k_gemm<BM, false, PART>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global,
+                           m, w->n, w->k, y, part, plane);
 }
 
 }  // namespace nvfp4
 
 using namespace nvfp4;
 
+extern "C" size_t w4a16_gemm_m128_workspace_bytes(int32_t m, int32_t n, int32_t k) {
+    if (m < 1 || n < 1 || k < 32) return 0;
+    const GemmPlan p = gemm_plan(m, n, k);
+    return p.split > 1 ? (size_t)p.split * p.plane * sizeof(float) : 0;
+}
+
 extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,
-                               void *stream) {
+                               void *workspace, size_t ws_bytes, void *stream) {
     int rc = validate_weight(w, "w4a16_gemm_m128");
     if (rc) return rc;
     if (w->n == 0 && m >= 1) return ok();   // empty output: nothing to read or write
@@ -207,14 +296,33 @@ extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_we
     if ((w->n + kBN - 1) / kBN > 2147483647 || (m + 127) / 128 > 65535)
         return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemm_m128: grid too large");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const long cols = (w->n + kBN - 1) / kBN;
-    const long slots_s = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<128, false>), 256, 0);
-    const long slots_t = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<256, false>), 512, 0);
-    const long rounds_s = (cols * ((m + 127) / 128) + slots_s - 1) / slots_s;
-    const long rounds_t = (cols * ((m + 255) / 256) + slots_t - 1) / slots_t;
-    if (kTallRound * rounds_t < rounds_s)
-        launch_gemm<256>(x_bf16, m, w, y, y_dtype == NVFP4_OUT_BF16, s);
+    const bool bf16 = y_dtype == NVFP4_OUT_BF16;
+    GemmPlan p = gemm_plan(m, w->n, w->k);
+    if (p.split > 1 && workspace == nullptr) p.split = 1;   // no workspace: one pass over K
+    if (p.split > 1) {
+        const size_t need = (size_t)p.split * p.plane * sizeof(float);
+        if (ws_bytes < need)
+            return fail(NVFP4_ERR_WORKSPACE, "w4a16_gemm_m128: workspace of %zu bytes, %zu needed", ws_bytes, need);
+        if (!aligned(workspace, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: workspace not 16-byte aligned");
+        float *part = reinterpret_cast<float *>(workspace);
+        launch_gemm<128, true>(x_bf16, m, w, y, bf16, part, p.plane, p.split, s);
+        rc = check_launch("w4a16_gemm_m128");
+        if (rc) return rc;
+        const size_t count = (size_t)m * w->n;
+        const size_t groups = (count + 3) / 4;
+        const size_t want = (groups + 255) / 256, cap = (size_t)num_cus() * 8;
+        const unsigned blocks = (unsigned)(want < cap ? want : cap);
+        if (bf16)
+            hipLaunchKernelGGL(k_gemm_reduce<true>, dim3(blocks), dim3(256), 0, s, part, p.plane, p.split, count,
+                               w->global, y);
+        else
+            hipLaunchKernelGGL(k_gemm_reduce<false>, dim3(blocks), dim3(256), 0, s, part, p.plane, p.split, count,
+                               w->global, y);
+        return check_launch("w4a16_gemm_m128");
+    }
+    if (p.bm == 256)
+        launch_gemm<256, false>(x_bf16, m, w, y, bf16, nullptr, 0, 1, s);
     else
-        launch_gemm<128>(x_bf16, m, w, y, y_dtype == NVFP4_OUT_BF16, s);
+        launch_gemm<128, false>(x_bf16, m, w, y, bf16, nullptr, 0, 1, s);
     return check_launch("w4a16_gemm_m128");
 }

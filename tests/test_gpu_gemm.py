@@ -38,6 +38,29 @@ def test_random_full(orc, m, n, k):
     assert_close(y, orc.gemv(x, codes, scales, glob[0]), f"gemm {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(200, 384, 512), (64, 640, 4096), (130, 256, 96 * 64)])
+def test_split_k_equals_one_pass(orc, m, n, k):
+    """Short chunks cut K into slices summed from a workspace; on the exact
+    family both that and one pass over K equal the oracle bit for bit."""
+    import nvfp4_w4a16_mtp_amd as nv
+    assert nv.gemm_workspace(m, n, k, torch.device("cuda")) is not None   # the split path is taken
+    x, codes, scales, g = synth.exact_family(210 + m, m, n, k)
+    wd = _w(codes, scales, g)
+    ys = nv.w4a16_gemm_m128(dev_bf16(x), wd).cpu().numpy()
+    y1 = nv.w4a16_gemm_m128(dev_bf16(x), wd, split_k=False).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(ys.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), ref.view(np.uint32))
+
+
+def test_split_k_workspace_too_small():
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(5, 128, 512, 1024)
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError, match="workspace"):
+        nv.w4a16_gemm_m128(dev_bf16(x), _w(codes, scales, g), workspace=ws)
+
+
 def test_gemm_m1_equals_gemv(orc):
     import nvfp4_w4a16_mtp_amd as nv
     x, codes, scales, g = synth.exact_family(9, 8, 512, 1024)
