@@ -2,15 +2,17 @@
 // new.rs (`MtpHead::new`) resolves as `nvfp4_global_absmax` and
 // `quantize_bf16_to_nvfp4` and runs once per weight matrix at load time.
 //
-// Pass 1 streams the bf16 tensor once (16-byte loads), keeps the largest
-// |w| as an integer (non-negative bf16 magnitudes order like unsigned
-// integers) and folds it into the global struct with one atomic max per
-// workgroup (at most two workgroups per CU, each striding over the
-// tensor).  Pass 2 streams it again: one thread encodes 32 consecutive
-// elements of a row (two 16-element blocks) from four 16-byte loads into one
-// 16-byte code store and one 2-byte scale store.  Every fp32 operation is a
-// single correctly rounded IEEE operation (no contraction, division is the
-// correctly rounded one), so the result is bit-identical to the definition.
+// Pass 1 streams the bf16 tensor once (16-byte loads, four in flight per
+// thread), keeps the largest |w| as an integer (non-negative bf16
+// magnitudes order like unsigned integers) and folds it into the global
+// struct with one atomic max per workgroup (at most four workgroups per CU,
+// each striding over the tensor).  Pass 2 streams it again: one thread
+// encodes 32 consecutive elements of a row (two 16-element blocks) from four
+// 16-byte loads into one 16-byte code store and one 2-byte scale store.
+// Every fp32 operation is a single correctly rounded IEEE operation (no
+// contraction, division is the correctly rounded one), and the E2M1
+// rounding is the hardware convert, which equals the threshold rounding on
+// every finite input, so the result is bit-identical to the definition.
 #include "common.hpp"
 
 #pragma clang fp contract(off)
@@ -28,15 +30,31 @@ __global__ void k_quant_clear(nvfp4_global *g) {
     }
 }
 
+#ifndef NVFP4_ABSMAX_LOADS
+#define NVFP4_ABSMAX_LOADS 4
+#endif
+constexpr int kAbsmaxLoads = NVFP4_ABSMAX_LOADS;
+
 __global__ __launch_bounds__(256) void k_quant_absmax(const uint4 *__restrict__ w, int64_t nvec,
                                                      nvfp4_global *g) {
     uint32_t mx = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-        uint4 v = w[i];
-        uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
-        mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
-        mx = max(mx, max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16)));
+    // kAbsmaxLoads loads in flight per thread; an index past the end re-reads
+    // the round's first vector (harmless for a maximum) instead of branching
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += kAbsmaxLoads * stride) {
+        uint4 v[kAbsmaxLoads];
+#pragma unroll
+        for (int u = 0; u < kAbsmaxLoads; ++u) {
+            const int64_t j = i + u * stride;
+            v[u] = w[j < nvec ? j : i];
+        }
+#pragma unroll
+        for (int u = 0; u < kAbsmaxLoads; ++u) {
+            const uint32_t a = v[u].x & 0x7FFF7FFFu, b = v[u].y & 0x7FFF7FFFu, c = v[u].z & 0x7FFF7FFFu,
+                           d = v[u].w & 0x7FFF7FFFu;
+            mx = max(mx, max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16)));
+            mx = max(mx, max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16)));
+        }
     }
     // wave max, workgroup max, then one atomic per workgroup on the fp32 bit
     // pattern of amax (atomics on one word serialize: keep them few)
@@ -66,14 +84,18 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float s) {
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// Nearest E2M1 code to v by its rounding thresholds (ties to the even code,
-// saturation at 6); the sign bit is the sign of v.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-    float a = fabsf(v);
-    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
+// Nearest E2M1 codes to two fp32 values, written as byte SEL of `into` (low
+// nibble = a): v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest
+// with ties to the even code, saturates at 6 and keeps the sign bit of a
+// zero result.  Compared on the GPU for every non-NaN fp32 bit pattern
+// (and both operand positions) with the threshold form
+//   |v| > 0.25, >= 0.75, > 1.25, >= 1.75, > 2.5, >= 3.5, > 5  (count = magnitude code)
+// plus the sign bit of v: no difference.  NaN inputs differ; they arise only
+// from an infinite input times a zero factor, which encode_block handles
+// apart.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t into, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(into, a, b, 1.0f, SEL);
 }
 
 __device__ __forceinline__ void global_scales(const nvfp4_global *g, float &enc, float &dec) {
@@ -105,13 +127,34 @@ __device__ __forceinline__ uint32_t encode_block(const uint32_t (&p)[8], float e
         inv = enc / sf;
         if (inv > 3.402823466e38f) inv = 3.402823466e38f;
     }
-    uint32_t out[2] = {0u, 0u};
+    float v[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float v0 = bf16_bits_to_f32(p[i] & 0xFFFFu) * inv;
-        float v1 = bf16_bits_to_f32(p[i] >> 16) * inv;
-        uint32_t byte = e2m1_code(v0) | (e2m1_code(v1) << 4);
-        out[i >> 2] |= byte << (8 * (i & 3));
+        v[2 * i] = bf16_bits_to_f32(p[i] & 0xFFFFu) * inv;
+        v[2 * i + 1] = bf16_bits_to_f32(p[i] >> 16) * inv;
+    }
+    uint32_t out[2];
+    if (inv == 0.0f) {
+        // every product is a zero, or NaN for an infinite input (outside the
+        // quantizer's domain): the code is the sign nibble alone, as the
+        // threshold rounding gives it, NaN included
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t o = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o |= ((__float_as_uint(v[8 * h + i]) >> 28) & 8u) << (4 * i);
+            out[h] = o;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t o = 0u;
+            o = e2m1_pair<0>(o, v[8 * h + 0], v[8 * h + 1]);
+            o = e2m1_pair<1>(o, v[8 * h + 2], v[8 * h + 3]);
+            o = e2m1_pair<2>(o, v[8 * h + 4], v[8 * h + 5]);
+            o = e2m1_pair<3>(o, v[8 * h + 6], v[8 * h + 7]);
+            out[h] = o;
+        }
     }
     lo = out[0];
     hi = out[1];
@@ -142,6 +185,11 @@ __global__ __launch_bounds__(256) void k_quant_encode(const uint4 *__restrict__ 
     }
 }
 
+#ifndef NVFP4_ABSMAX_PER_CU
+#define NVFP4_ABSMAX_PER_CU 4
+#endif
+constexpr int kAbsmaxPerCu = NVFP4_ABSMAX_PER_CU;
+
 static int grid_for(int64_t items, int per_cu) {
     int64_t blocks = (items + 255) / 256;
     int64_t cap = (int64_t)num_cus() * per_cu;
@@ -166,7 +214,7 @@ extern "C" int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint
     int rc = check_launch("nvfp4_quantize(clear)");
     if (rc) return rc;
     const int64_t nvec = count / 8;
-    hipLaunchKernelGGL(k_quant_absmax, dim3(grid_for(nvec, 2)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_quant_absmax, dim3(grid_for(nvec, kAbsmaxPerCu)), dim3(256), 0, s,
                        reinterpret_cast<const uint4 *>(w_bf16), nvec, global);
     rc = check_launch("nvfp4_quantize(absmax)");
     if (rc) return rc;
