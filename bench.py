@@ -343,7 +343,10 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
     wts = torch.empty((M, TOPK), dtype=torch.float32, device=hl.device)
     ms = _time_graph(torch, lambda i: nv.moe_w4a16_gemv(xm, router, TOPK, copies[i % NCOPIES]["moe"], workspace=ws, out=ymo,
                                                         topk_ids=ids, topk_w=wts), reps, s)
-    out["moe"] = {"ms": round(ms, 5)}
+    nd = len(set(ids.cpu().numpy().ravel().tolist()))   # distinct routed experts
+    mb = nd * 3 * nvfp4_bytes(I, H) + M * H * 2 + M * E * 4 + M * H * 4 + 2 * M * TOPK * 4
+    out["moe"] = {"ms": round(ms, 5), "gbs": round(mb / ms / 1e6, 1), "frac": round(mb / ms / 1e6 / HBM_PEAK_GBS, 4),
+                  "distinct_experts": nd}
     # the complete MoE layer: NVFP4 router + routed experts + gated shared expert
     gen2 = torch.Generator(device=hl.device)
     gen2.manual_seed(2)
@@ -358,8 +361,19 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
                                                          *lay[i % NCOPIES][1:], shared_gate_w=sgw, workspace=lws,
                                                          out=ymo, topk_ids=ids, topk_w=wts, router_logits=rl), reps, s)
     nvfp4_lay = nvfp4_bytes(E, H) + 3 * nvfp4_bytes(I, H)
-    out["moe_layer_router_shared"] = {"ms": round(ms, 5), "extra_weight_bytes": nvfp4_lay}
+    lb = mb + nvfp4_lay + M * E * 4
+    out["moe_layer_router_shared"] = {"ms": round(ms, 5), "extra_weight_bytes": nvfp4_lay,
+                                      "gbs": round(lb / ms / 1e6, 1), "frac": round(lb / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del lay
+    # quantizer on the largest matrix (the LM head): clear, absmax and encode
+    # launches back to back; bytes = 2 reads of the bf16 tensor + the NVFP4 write
+    wq = (torch.randn((VOCAB, H), generator=gen2, device=hl.device) * 0.02).to(torch.bfloat16)
+    qo = nv.nvfp4_quantize(wq)
+    ms = _time(torch, lambda i: nv.nvfp4_quantize(wq, out=qo), 10, s)
+    qb = 2 * VOCAB * H * 2 + nvfp4_bytes(VOCAB, H)
+    out["quantize_151936x2048"] = {"ms": round(ms, 4), "gbs": round(qb / ms / 1e6, 1),
+                                   "frac": round(qb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del wq, qo
     # prefill GEMM: fc (2048 x 4096) and the dense-FFN gate/up (17408 x 5120)
     out.update(gemm_rows(nv, torch, hl.device, s, (("fc", 2048, 4096, 1024), ("gate_up", 17408, 5120, 1024),
                                                    ("gate_up", 17408, 5120, 8192))))

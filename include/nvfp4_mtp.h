@@ -127,7 +127,12 @@ int nvfp4_quantize(const uint16_t *w_bf16, int32_t n, int32_t k, uint8_t *codes,
  *   y       [m][w->n], fp32 (y_dtype NVFP4_OUT_F32) or bf16 rounded to
  *           nearest-even from the fp32 sum (NVFP4_OUT_BF16); 4-byte aligned.
  * fp32 accumulation; one pass over codes and scales; one launch.  The
- * activations are staged in LDS: round_up_pow2(m) * k * 2 <= 155648.
+ * activations are staged in LDS: when round_up_pow2(m) * k * 2 exceeds
+ * 155648 bytes the rows go in groups of the most that fit, one pass and
+ * one launch per group (k * 2 <= 155648 is required).  Large weights
+ * (enough 4-, 8- or 16-row units for every wavefront of the device) run on
+ * the persistent streaming grid of lmhead_gemv_argmax with plain outputs;
+ * either way each output is one fp32 sum.
  */
 int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y,
                int32_t y_dtype, void *stream);

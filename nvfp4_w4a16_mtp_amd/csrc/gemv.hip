@@ -35,6 +35,13 @@ struct GemvGroups {
     int count;
 };
 
+#ifndef NVFP4_GEMV_PIPE
+#define NVFP4_GEMV_PIPE 4
+#endif
+// Chunks per lane per pipelined stage of the generic loop (R rows share it).
+template <int R>
+constexpr int gemv_pipe() { return R >= NVFP4_GEMV_PIPE ? 1 : NVFP4_GEMV_PIPE / R; }
+
 template <int MT, int R, int KS, int CPL>
 __global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
                                              int bf16out) {
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, in
     } else {
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        gemv_tile_loop<MT, R, KS>(xs, codes, scales, n, k, row0, red, epi);
+        gemv_tile_loop<MT, R, KS, gemv_pipe<R>()>(xs, codes, scales, n, k, row0, red, epi);
     }
 }
 
@@ -246,12 +253,18 @@ __device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], in
 // whichever wavefront is free next (an LDS counter), so wavefronts that the
 // CU's arbitration serves less take fewer units and all of them end
 // together.  The activations are loaded once per workgroup.
-template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW, bool MF = false, bool MASKED = true>
+//
+// GOUT: the same streaming loop as a plain GEMV -- every unit's sums, times
+// the global scale, go to gy[m][row] (fp32, or bf16 with gy_bf16) and there
+// is no argmax, mask or workspace.  Large decode GEMVs use it for the
+// persistent grid, the LDS unit queue and the next unit's loads in flight.
+template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW, bool MF = false, bool MASKED = true, bool GOUT = false>
 __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                    int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
                                                    float *__restrict__ out_max, float *__restrict__ out_lp,
-                                                   const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb) {
+                                                   const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb,
+                                                   void *__restrict__ gy, int gy_bf16) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     __shared__ ArgPart wbest[NW][MT];
@@ -282,7 +295,19 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         return word < mask_words ? mask[(size_t)mrow * mask_words + word] : 0u;
     };
     uint32_t mword = ~0u;
+    auto gout = [&](int row, int mm, float s) {
+        if (mm >= m_rt) return;
+        const float o = s * dec;
+        if (gy_bf16)
+            reinterpret_cast<uint16_t *>(gy)[(size_t)mm * v + row] = (uint16_t)f32_to_bf16_bits(o);
+        else
+            reinterpret_cast<float *>(gy)[(size_t)mm * v + row] = o;
+    };
     auto epi = [&](int row, int mm, float s) {
+        if constexpr (GOUT) {
+            gout(row, mm, s);
+            return;
+        }
         const float logit = s * dec;
         float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
         if (row == 0) st_dev(&row0[mm], logit);
@@ -318,6 +343,10 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         const int q = lane >> 4;
         auto epi_mf = [&](int row, int r, float s) {
             const int mm = 4 * q + r;
+            if constexpr (GOUT) {
+                gout(row, mm, s);
+                return;
+            }
             const float logit = s * dec;
             float key = BF16KEY ? bf16_bits_to_f32(f32_to_bf16_bits(logit)) : logit;
             if (row == 0) st_dev(&row0[mm], logit);
@@ -463,6 +492,8 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             gemv_tile_loop<MT, R, 1, (R >= 4 ? 1 : 4 / R), true>(xs, codes, scales, v, k, u * rows, nullptr, epi);
         }
     }
+
+    if constexpr (GOUT) return;   // plain GEMV: every output is written
 
     // workgroup combine: the four slots of a wavefront by shuffles, then the
     // NW wavefronts in LDS -> MT candidates
@@ -639,10 +670,22 @@ static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t
 #endif
 // One launch over `count` weights with a common K (their tiles concatenated);
 // the tile shape is chosen for the total row count.
+#ifndef NVFP4_GEMV_PERSIST
+#define NVFP4_GEMV_PERSIST 1
+#endif
+constexpr bool kGemvPersist = NVFP4_GEMV_PERSIST;
+template <int MT>
+static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16);
+
 template <int MT>
 static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
                          hipStream_t s) {
     const int k = w[0]->k;
+    if (count == 1 && kGemvPersist) {
+        ok();   // clears the message that a refused LDS request would leave
+        if (launch_gemv_persist<MT>(s, x, m, w[0], y[0], bf16)) return check_launch("w4a16_gemv");
+        if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
+    }
     int total_n = 0;
     for (int i = 0; i < count; ++i) total_n += w[i]->n;
     const TileChoice tc = canonical(choose_tile(total_n, k, MT, NVFP4_GEMV_TPC * num_cus(), 0));
@@ -684,7 +727,49 @@ static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m
     }
     const int cap = num_cus() * per_cu, nparts = (v + 15) / 16;
     hipLaunchKernelGGL(kern, dim3(cap < nparts ? cap : nparts), dim3(64 * NW), lds, s, h, m, w->codes, w->scales,
-                       w->global, v, w->k, ws, oi, om, olp, mask, mask_words, emb);
+                       w->global, v, w->k, ws, oi, om, olp, mask, mask_words, emb, nullptr, 0);
+}
+
+// Persistent streaming GEMV (the LM-head loop with plain outputs) for one
+// weight.  One and two rows: when there are kPersistUnits or more units per
+// wavefront of the chip (with about one per wavefront the per-tile grid is as
+// fast).  Five to eight rows: the MFMA units whenever K allows them, as long
+// as every fourth wavefront gets a unit -- dot2 units cost twice as much at
+// eight rows.  Four rows keep the per-tile grid, which measured faster.
+// Returns false (nothing launched) when the persistent grid is not used.
+#ifndef NVFP4_GEMV_PERSIST_UNITS
+#define NVFP4_GEMV_PERSIST_UNITS 2
+#endif
+constexpr int kPersistUnits = NVFP4_GEMV_PERSIST_UNITS;
+
+template <int MT, int CPL, bool MF>
+static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y,
+                                  int bf16) {
+    constexpr int NW = MF ? kLmMfWaves : lm_waves<MT, CPL>();
+    constexpr int rows = MF ? 16 : 4 * lm_rows_per_slot<MT>();
+    auto kern = k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, false, false, NW, MF, false, true>;
+    const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kern), 64 * NW, lds);
+    const long units = (w->n + rows - 1) / rows, waves = (long)num_cus() * per_cu * NW;
+    if (per_cu < 1 || (MF ? 4 * units < waves : units < kPersistUnits * waves)) return false;
+    if (allow_lds(reinterpret_cast<const void *>(kern), lds, "w4a16_gemv")) return false;
+    hipLaunchKernelGGL(kern, dim3(num_cus() * per_cu), dim3(64 * NW), lds, s, x, m, w->codes, w->scales, w->global,
+                       w->n, w->k, nullptr, nullptr, nullptr, nullptr, nullptr, 0, EmbedOut{}, y, bf16);
+    return true;
+}
+
+template <int MT>
+static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16) {
+    const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
+    const size_t lds = gemv_lds_bytes(MT, w->k, tc);
+    if (lds > kMaxLds) return false;
+    if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
+        if constexpr (MT >= kLmMfMinRows) return launch_gemv_persist_k<MT, 0, true>((size_t)MT * w->k * 2, s, x, m, w, y, bf16);
+    }
+    if constexpr (MT == 4 || MT > 8) return false;
+    if constexpr (MT == 1) {
+        if (tc.CPL == 4) return launch_gemv_persist_k<MT, 4, false>(lds, s, x, m, w, y, bf16);
+    }
+    return launch_gemv_persist_k<MT, 0, false>(lds, s, x, m, w, y, bf16);
 }
 
 // The LM head keeps KS = 1 and R = 2 (8-row wavefront units); there are at
@@ -744,17 +829,31 @@ static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
     if (total_n == 0) return ok();   // empty outputs: nothing to read or write
     if (!x_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL x", who);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "%s: x not 16-byte aligned", who);
-    const int mt = round_up_mt(m);
-    if ((size_t)mt * w[0]->k * 2 > kMaxLds)
-        return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w[0]->k);
+    const int k = w[0]->k;
+    if ((size_t)k * 2 > kMaxLds)
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: one activation row of k=%d exceeds the LDS", who, k);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int bf16 = y_dtype == NVFP4_OUT_BF16;
-    switch (mt) {
-        case 1: return launch_gemv_m<1>(x_bf16, m, w, y, count, bf16, s);
-        case 2: return launch_gemv_m<2>(x_bf16, m, w, y, count, bf16, s);
-        case 4: return launch_gemv_m<4>(x_bf16, m, w, y, count, bf16, s);
-        default: return launch_gemv_m<8>(x_bf16, m, w, y, count, bf16, s);
+    // activation rows are staged in LDS: rows that do not fit at once go in
+    // groups of the most that do (each group streams the weights again)
+    int grp = round_up_mt(m);
+    while ((size_t)grp * k * 2 > kMaxLds) grp >>= 1;
+    for (int r0 = 0; r0 < m; r0 += grp) {
+        const int mg = m - r0 < grp ? m - r0 : grp;
+        void *yg[kMaxGroups];
+        for (int i = 0; i < count; ++i)
+            yg[i] = w[i]->n > 0 ? static_cast<char *>(y[i]) + (size_t)r0 * w[i]->n * (bf16 ? 2 : 4) : nullptr;
+        const uint16_t *xg = x_bf16 + (size_t)r0 * k;
+        int rc;
+        switch (round_up_mt(mg)) {
+            case 1: rc = launch_gemv_m<1>(xg, mg, w, yg, count, bf16, s); break;
+            case 2: rc = launch_gemv_m<2>(xg, mg, w, yg, count, bf16, s); break;
+            case 4: rc = launch_gemv_m<4>(xg, mg, w, yg, count, bf16, s); break;
+            default: rc = launch_gemv_m<8>(xg, mg, w, yg, count, bf16, s); break;
+        }
+        if (rc) return rc;
     }
+    return NVFP4_OK;
 }
 
 extern "C" int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,

@@ -91,3 +91,33 @@ def test_no_write_outside_output(orc):
     b = buf.cpu().numpy()
     assert (b[:64] == 12345.0).all() and (b[364:] == 12345.0).all()
     assert np.array_equal(y.cpu().numpy(), orc.gemv(x, codes, scales, g))
+
+
+# Weights with enough units for the persistent streaming grid on a 256-CU
+# MI355X (two units per wavefront at one or two rows; the MFMA units at five
+# to eight rows), ragged row counts; the exact family makes every output bit
+# exact in any summation order.
+@pytest.mark.parametrize("m,n,k", [(1, 16387, 2048), (1, 32771, 512), (2, 49155, 256), (8, 8195, 1024),
+                                   (6, 20000, 2048)])
+def test_persistent_grid_bit_exact(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(150 + m, m, n, k)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", [(5, 300, 10240), (8, 301, 17408), (3, 77, 40960)])
+def test_rows_beyond_the_lds_go_in_groups(orc, m, n, k):
+    """round_up(m) rows of K do not fit the LDS image: the rows go in groups
+    (5 -> 4 + 1, 8 -> 4 + 4, 3 -> 1 + 1 + 1); the bf16 output is the
+    rounding of the fp32 one, and odd n puts bf16 groups at 2-byte offsets."""
+    import nvfp4_w4a16_mtp_amd as nv
+    w = synth.weight_bf16(160 + m, n, k)
+    x = synth.acts_bf16(161 + m, m, k)
+    codes, scales, glob = orc.quantize(w)
+    wd = _w(codes, scales, glob[0])
+    y32 = nv.w4a16_gemv(dev_bf16(x), wd).cpu().numpy()
+    assert_close(y32, orc.gemv(x, codes, scales, glob[0]), f"m={m} k={k}")
+    yb = nv.w4a16_gemv(dev_bf16(x), wd, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(yb, bf16_round_f64(y32).astype(np.float32))
