@@ -212,12 +212,16 @@ constexpr int kLmMfWaves = NVFP4_LM_MF_WAVES;
 #endif
 constexpr int kLmMfDepth = NVFP4_LM_MF_DEPTH;   // 128-k steps of code loads in flight per lane
 constexpr bool kLmMfma = NVFP4_LM_MFMA;
+constexpr int kMfStageBytes = 3072;   // per wavefront: one code pair (2 KiB) and one scale round (1 KiB)
 // Fewest activation rows served by the MFMA units.  Their cost per unit does
 // not depend on M (16 rows of which M are used, and an fp32 multiply per
 // dequantized weight that the dot2 units fold into one per 16), while the
-// dot2 units' grows with M: at K = 2048 the MFMA units measure 63-65 us for
-// any M, the dot2 units 41, 55 and 103 us at M = 2, 4 and 8.
-constexpr int kLmMfMinRows = 8;
+// dot2 units' grows with M: at K = 2048 the LM head with MFMA units measures
+// 45-47 us at M = 4..8, with dot2 units 37.5, 55 and 103 us at M = 2, 4, 8.
+#ifndef NVFP4_LM_MF_MIN_ROWS
+#define NVFP4_LM_MF_MIN_ROWS 4
+#endif
+constexpr int kLmMfMinRows = NVFP4_LM_MF_MIN_ROWS;
 
 // Next position in a workgroup's unit sequence: wavefronts draw from an LDS
 // counter (positions 0 .. NW-1 are the wavefronts' first units).
@@ -362,25 +366,33 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         };
         stage_x_mf(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        // the code loads run kLmMfDepth steps ahead as one stream across the
-        // wavefront's units (the launch keeps the step count a multiple of
-        // the depth); past its last unit the stream reads unit 0, unused
+        // the code loads run kLmMfDepth steps ahead (and the scale loads one
+        // round of kLmMfDepth steps) as one stream across the wavefront's
+        // units (the launch keeps the step count a multiple of the depth);
+        // past its last unit the stream reads unit 0, unused
         constexpr int D = kLmMfDepth;
+        static_assert(D == 8, "a round of 8 steps is one scale line");
         const int li = lane & 15, cpr = k >> 3, S = k >> 7;
+        uint4 *cst = smem + (size_t)MT * cpr + (size_t)wave * (kMfStageBytes / 16);   // code pair, 2 KiB
+        const uint16_t *sst = reinterpret_cast<const uint16_t *>(cst + 128);            // scale round, 1 KiB
         int u = b0 + G * wave;
         int un = b0 + G * lm_draw<NW>(&s_q, lane);
-        MfRow cur = mf_row(codes, scales, v, k, (u < nunits ? u : 0) * rows, li, q);
-        MfRow nxt = mf_row(codes, scales, v, k, (un < nunits ? un : 0) * rows, li, q);
+        MfLines cur = mf_lines(codes, scales, v, k, (u < nunits ? u : 0) * rows, lane);
+        MfLines nxt = mf_lines(codes, scales, v, k, (un < nunits ? un : 0) * rows, lane);
         const uint4 *xa[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) xa[b] = mf_xrow(xs, cpr, MT, li, q, b);
+        const int ws0 = mf_code_wslot(lane, 0), ws1 = mf_code_wslot(lane, 1);
+        const int rs0 = mf_code_rslot(li, q, 0), rs1 = mf_code_rslot(li, q, 1);
+        // issue order as in the loop (scales, then the code pairs), so that
+        // each wait there only covers what it needs
+        uint4 sv = ld_stream16(cur.sp);
+        __builtin_amdgcn_sched_barrier(0);
         uint4 cw[D];
-        uint32_t sw[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            cw[d] = ld_stream16(cur.cp + 64 * (size_t)d);
-            sw[d] = ld_stream2(cur.sp + 8 * (size_t)d);
-            __builtin_amdgcn_sched_barrier(0);   // same issue order as the loop's reloads
+            cw[d] = ld_stream16((d & 1 ? cur.cb : cur.ca) + 128 * (d >> 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
         while (u < nunits) {
             if constexpr (MASKED) {
@@ -393,23 +405,32 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             }
             f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
             for (int s0 = 0; s0 < S; s0 += D) {
-                // this round reloads steps s0 + D .. s0 + 2 D - 1: of this
-                // unit, or in the last round steps 0 .. D - 1 of the next
+                // this round reloads steps s0 + D .. s0 + 2 D - 1 and the next
+                // round's scales: of this unit, or in the last round steps
+                // 0 .. D - 1 of the next
                 const bool last = s0 + D >= S;
-                const uint8_t *lc = last ? nxt.cp : cur.cp + 64 * (size_t)(s0 + D);
+                const uint8_t *la = last ? nxt.ca : cur.ca + 64 * (size_t)(s0 + D);
+                const uint8_t *lb = last ? nxt.cb : cur.cb + 64 * (size_t)(s0 + D);
                 const uint8_t *ls = last ? nxt.sp : cur.sp + 8 * (size_t)(s0 + D);
+                cst[128 + lane] = sv;   // the round's scales to LDS (row r at byte 64 r)
+                sv = ld_stream16(ls);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    uint4 a[4], bw[4];
-                    mf_xload(xa, s0 + d, a);
-                    mf_dequant(cw[d], sw[d], bw);
-                    cw[d] = ld_stream16(lc + 64 * d);
-                    sw[d] = ld_stream2(ls + 8 * d);
-                    // the reload stays right after the dequantization: sunk
-                    // to the end of the round, every step of the next round
-                    // would wait for it
-                    __builtin_amdgcn_sched_barrier(0);
-                    mf_mma(a, bw, acc0, acc1);
+                for (int d = 0; d < D; d += 2) {
+                    cst[ws0] = cw[d];         // the pair's lines to LDS
+                    cst[ws1] = cw[d + 1];
+                    cw[d] = ld_stream16(la + 128 * (d >> 1));
+                    cw[d + 1] = ld_stream16(lb + 128 * (d >> 1));
+                    __builtin_amdgcn_sched_barrier(0);   // reloads issued here, D steps ahead
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        uint4 a[4], bw[4];
+                        mf_xload(xa, s0 + d + h, a);
+                        const uint4 c = cst[h ? rs1 : rs0];
+                        const uint32_t sw = sst[32 * li + 4 * (d + h) + q];
+                        mf_dequant(c, sw, bw);
+                        mf_mma(a, bw, acc0, acc1);
+                    }
                 }
             }
             const int rowu = u * rows + li;
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             u = un;
             cur = nxt;
             un = b0 + G * lm_draw<NW>(&s_q, lane);
-            nxt = mf_row(codes, scales, v, k, (un < nunits ? un : 0) * rows, li, q);
+            nxt = mf_lines(codes, scales, v, k, (un < nunits ? un : 0) * rows, lane);
         }
     } else if constexpr (MT == 1 && CPL > 0) {
         // one activation row: it lives in registers; the next unit's loads
@@ -733,10 +754,10 @@ static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m
 // Persistent streaming GEMV (the LM-head loop with plain outputs) for one
 // weight.  One and two rows: when there are kPersistUnits or more units per
 // wavefront of the chip (with about one per wavefront the per-tile grid is as
-// fast).  Five to eight rows: the MFMA units whenever K allows them, as long
-// as every fourth wavefront gets a unit -- dot2 units cost twice as much at
-// eight rows.  Four rows keep the per-tile grid, which measured faster.
-// Returns false (nothing launched) when the persistent grid is not used.
+// fast).  Four to eight rows: the MFMA units whenever K allows them, as long
+// as every fourth wavefront gets a unit (at 151936 x 2048: 35.8 and 37.9 us
+// at M = 4 and 8, against 50.5 and 127 us on the per-tile grid).  Returns
+// false (nothing launched) when the persistent grid is not used.
 #ifndef NVFP4_GEMV_PERSIST_UNITS
 #define NVFP4_GEMV_PERSIST_UNITS 2
 #endif
@@ -763,13 +784,18 @@ static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const n
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     if (lds > kMaxLds) return false;
     if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
-        if constexpr (MT >= kLmMfMinRows) return launch_gemv_persist_k<MT, 0, true>((size_t)MT * w->k * 2, s, x, m, w, y, bf16);
+        if constexpr (MT >= kLmMfMinRows)
+            return launch_gemv_persist_k<MT, 0, true>((size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes, s, x,
+                                                      m, w, y, bf16);
     }
-    if constexpr (MT == 4 || MT > 8) return false;
-    if constexpr (MT == 1) {
-        if (tc.CPL == 4) return launch_gemv_persist_k<MT, 4, false>(lds, s, x, m, w, y, bf16);
+    if constexpr (MT >= kLmMfMinRows) {
+        return false;   // K does not allow the MFMA units: the per-tile grid
+    } else {
+        if constexpr (MT == 1) {
+            if (tc.CPL == 4) return launch_gemv_persist_k<MT, 4, false>(lds, s, x, m, w, y, bf16);
+        }
+        return launch_gemv_persist_k<MT, 0, false>(lds, s, x, m, w, y, bf16);
     }
-    return launch_gemv_persist_k<MT, 0, false>(lds, s, x, m, w, y, bf16);
 }
 
 // The LM head keeps KS = 1 and R = 2 (8-row wavefront units); there are at
@@ -784,7 +810,7 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
     ok();   // clears the message that a refused LDS request would leave
     if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
         if constexpr (MT >= kLmMfMinRows) {
-            const size_t lmf = (size_t)MT * w->k * 2;
+            const size_t lmf = (size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes;
             if (bk) lp ? launch_lm_kernel<MT, 0, true, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
                        : launch_lm_kernel<MT, 0, true, false, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
             else lp ? launch_lm_kernel<MT, 0, false, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)

@@ -455,15 +455,36 @@ __device__ __forceinline__ const uint4 *mf_xrow(const uint4 *xs, int cpr, int mt
     return xs + xr * cpr + ((4 * q + b) ^ (xr & 7));
 }
 
-// Code and scale pointers of lane (n, q) for a 16-row unit at row0 (rows
-// past n read row n - 1, never passed on): step s at + 64 s and + 8 s.
-struct MfRow {
-    const uint8_t *cp, *sp;
+// Loads of a 16-row unit that fill whole 128-byte lines (one instruction
+// touching 16 rows x 64 bytes, the MFMA layout, costs about twice the time
+// of one touching 8 rows x 128 bytes).  Codes: step pair p (256 k) of rows
+// 0-7 is one instruction (lane l: row l / 8, bytes 128 p + 16 (l % 8)), of
+// rows 8-15 the next; scales: 8 steps (1024 k, 64 bytes a row) of all 16
+// rows are one instruction (lane l: row l / 4, bytes 16 (l % 4)).  Rows past
+// n read row n - 1, never passed on.
+struct MfLines {
+    const uint8_t *ca, *cb, *sp;
 };
-__device__ __forceinline__ MfRow mf_row(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int n,
-                                        int k, int row0, int li, int q) {
-    const int row = min(row0 + li, n - 1);
-    return MfRow{codes + (size_t)row * (size_t)(k >> 1) + 16 * q, scales + (size_t)row * (size_t)(k >> 4) + 2 * q};
+__device__ __forceinline__ MfLines mf_lines(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                            int n, int k, int row0, int lane) {
+    const int ra = min(row0 + (lane >> 3), n - 1), rb = min(row0 + 8 + (lane >> 3), n - 1);
+    const int rs = min(row0 + (lane >> 2), n - 1);
+    return MfLines{codes + (size_t)ra * (size_t)(k >> 1) + 16 * (lane & 7),
+                   codes + (size_t)rb * (size_t)(k >> 1) + 16 * (lane & 7),
+                   scales + (size_t)rs * (size_t)(k >> 4) + 16 * (lane & 3)};
+}
+
+// The lines go through a per-wavefront LDS area to the MFMA layout: code
+// slot (8 r + (i ^ (r % 8))) holds 16-byte segment i of row r of the pair
+// (the swizzle keeps the 16 rows one layout read touches on different
+// banks); the scale area holds row r's 64 bytes at 64 r.
+__device__ __forceinline__ int mf_code_wslot(int lane, int half) {   // lane's store, rows 8 half + lane / 8
+    const int r = 8 * half + (lane >> 3), i = lane & 7;
+    return 8 * r + (i ^ (r & 7));
+}
+__device__ __forceinline__ int mf_code_rslot(int li, int q, int h) {   // step h of the pair, lane (n = li, q)
+    const int i = 4 * h + q;
+    return 8 * li + (i ^ (li & 7));
 }
 
 // ---------------------------------------------------------------- host ----
