@@ -71,30 +71,30 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kBN;
 
-    // staging roles: activation row th / 2, half th % 2 (32 k) of the K step;
-    // weight row th / BPR, part th % BPR (64 / BPR k)
-    const int srow = th >> 1, shalf = th & 1;
+    // staging roles: activation rows th / 8 + (NT / 8) q, q = 0..3, chunk th % 8
+    // (8 bf16) of the K step -- each load instruction of a wavefront covers
+    // 8 rows x 128 bytes, whole lines; weight row th / BPR, part th % BPR
+    // (64 / BPR k)
+    const int xrow0 = th >> 3, xch = th & 7;
     const int brow = th / BPR, bpart = th % BPR;
-    const int xm = m0 + srow, wnr = n0 + brow;
-    const bool xval = xm < M, wval = wnr < N;
-    const uint16_t *xrow = x + (size_t)(xval ? xm : 0) * K;
+    const int wnr = n0 + brow;
+    const bool wval = wnr < N;
     const uint8_t *crow = codes + (size_t)(wval ? wnr : 0) * (K >> 1);
     const uint8_t *srow_p = scales + (size_t)(wval ? wnr : 0) * (K >> 4);
 
+    // rows m0 + xrow0 + (NT / 8) q exist for q < xq
+    const int xleft = M - m0 - xrow0;
+    const int xq = xleft <= 0 ? 0 : (xleft + NT / 8 - 1) / (NT / 8);
+    const uint16_t *xb = x + (size_t)(m0 + (xq > 0 ? xrow0 : 0)) * K + 8 * xch;
+    const int xstep = (NT / 8) * K;   // < 2^31: K < 2^24
     uint4 xr[4];
     uint32_t cr[CPT];
     uint32_t sr;
     auto load_step = [&](int k0) {
-        const int kk = k0 + 32 * shalf;
-        if (xval && kk < K) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(xrow + kk);
-            xr[0] = p[0];
-            xr[1] = p[1];
-            xr[2] = p[2];
-            xr[3] = p[3];
-        } else {
-            xr[0] = xr[1] = xr[2] = xr[3] = make_uint4(0, 0, 0, 0);
-        }
+        const bool kin = k0 + 8 * xch < K;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[q] = (q < xq && kin) ? *reinterpret_cast<const uint4 *>(xb + q * xstep + k0) : make_uint4(0, 0, 0, 0);
         const int kb = k0 + (64 / BPR) * bpart;
         if (wval && kb < K) {
             if constexpr (CPT == 4) {
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
         // stage: activations as they are, weights dequantized
         {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4 *>(lds_a + lds_off(srow, 4 * shalf + q)) = xr[q];
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4 *>(lds_a + lds_off(xrow0 + (NT / 8) * q, xch)) = xr[q];
             typedef __attribute__((ext_vector_type(2))) float f32x2;
             const f32x2 sfv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sr, false);   // E4M3 block scales, exact
 #pragma unroll
