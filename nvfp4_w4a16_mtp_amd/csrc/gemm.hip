@@ -86,7 +86,7 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
     const int xleft = M - m0 - xrow0;
     const int xq = xleft <= 0 ? 0 : (xleft + NT / 8 - 1) / (NT / 8);
     const uint16_t *xb = x + (size_t)(m0 + (xq > 0 ? xrow0 : 0)) * K + 8 * xch;
-    const int xstep = (NT / 8) * K;   // < 2^31: K < 2^24
+    const size_t xstep = (size_t)(NT / 8) * K;
     uint4 xr[4];
     uint32_t cr[CPT];
     uint32_t sr;
