@@ -370,7 +370,46 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
 // activations and gate, are stored device-scope: in the fused launch the
 // down workgroups read them in the same launch, once the workgroup has
 // counted itself in the hand-off words `done` (FUSED).
-template <int CPL, bool FUSED>
+// The routing's outputs: ids and weights, and (route != nullptr) the plan of
+// the two-launch path -- distinct experts, and per pair position (in
+// (expert, token) order) its token, pair and weight.  One workgroup.
+__device__ __forceinline__ void write_route(const RouteLds &L, const nvfp4_moe_weights &e, int m, int topk,
+                                            int32_t *__restrict__ ids, float *__restrict__ wts,
+                                            MoeRoute *__restrict__ route) {
+    for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
+        ids[p] = L.sel_i[p / topk][p % topk];
+        wts[p] = L.sel_w[p / topk][p % topk];
+    }
+    if (route == nullptr) return;
+    // thread q writes distinct expert q and its pairs; its first pair
+    // position is the count of the pairs before it (a serial loop in one
+    // thread took 10 us at 8 tokens)
+    const int nd = L.n_distinct;
+    for (int q = threadIdx.x; q <= nd; q += blockDim.x) {
+        int pb = 0;
+        for (int j = 0; j < q; ++j) pb += L.ex[j].cnt;
+        route->pb[q] = pb;
+        if (q == nd) {
+            route->n_distinct = nd;
+            route->n_pairs = pb;
+            continue;
+        }
+        const MoeExpert &me = L.ex[q];
+        route->ex[q] = me;
+        route->ex_id[q] = me.expert;
+        route->ddec[q] = e.down_global[me.expert].dec;
+        for (int c = 0; c < me.cnt; ++c) {
+            route->pos_tok[pb + c] = me.tok[c];
+            route->pos_pair[pb + c] = me.pair[c];
+            route->pos_w[pb + c] = L.sel_w[me.tok[c]][me.pair[c] - me.tok[c] * topk];
+        }
+    }
+}
+
+// PLANNED: the plan comes from k_moe_route instead of every workgroup's own
+// routing (which, at several tokens, costs a gate/up workgroup about as much
+// as its weights).
+template <int CPL, bool FUSED, bool PLANNED = false>
 __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx, const uint16_t *__restrict__ x,
                                              const float *__restrict__ logits, int m, int E, int topk,
                                              const nvfp4_moe_weights &e, int32_t *__restrict__ ids,
@@ -390,8 +429,6 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
         sgv = sh.sg[(size_t)st * I + si];
         suv = sh.su[(size_t)st * I + si];
     }
-    moe_route_lds(logits, m, E, topk, L);
-    if (s_act) st_dev(&sh.sact[(size_t)st * I + si], (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv));
     // shared_expert_gate: the last workgroup of the first column, one wavefront per token
     if (sh.on && u == 0 && bx == gx - 1) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -404,45 +441,35 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
             if (lane == 0) st_dev(&sh.sgate[t], sh.gate_w != nullptr ? 1.0f / (1.0f + expf(-z)) : 1.0f);
         }
     }
-    if (bx == 0 && u == 0) {
-        for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
-            ids[p] = L.sel_i[p / topk][p % topk];
-            wts[p] = L.sel_w[p / topk][p % topk];
-        }
-    }
-    if (!FUSED && bx == 0 && u == 0) {
-        for (int q = threadIdx.x; q < L.n_distinct; q += blockDim.x) {
-            route->ex[q] = L.ex[q];
-            route->ex_id[q] = L.ex[q].expert;
-            route->ddec[q] = e.down_global[L.ex[q].expert].dec;
-        }
+    if constexpr (PLANNED) {
+        // the routing kernel wrote the plan (and the ids and weights)
         if (threadIdx.x == 0) {
-            route->n_distinct = L.n_distinct;
-            int pb = 0;
-            for (int q = 0; q < L.n_distinct; ++q) {
-                const MoeExpert &me = L.ex[q];
-                route->pb[q] = pb;
-                for (int c = 0; c < me.cnt; ++c, ++pb) {
-                    route->pos_tok[pb] = me.tok[c];
-                    route->pos_pair[pb] = me.pair[c];
-                    route->pos_w[pb] = L.sel_w[me.tok[c]][me.pair[c] - me.tok[c] * topk];
-                }
+            s_nd = route->n_distinct;
+            if (u < s_nd) {
+                s_ex = route->ex[u].expert;
+                s_cnt = route->ex[u].cnt;
             }
-            route->pb[L.n_distinct] = pb;
-            route->n_pairs = pb;
+        }
+        if (threadIdx.x < 8 && u < route->n_distinct) {
+            tok[threadIdx.x] = route->ex[u].tok[threadIdx.x];
+            prs[threadIdx.x] = route->ex[u].pair[threadIdx.x];
+        }
+    } else {
+        moe_route_lds(logits, m, E, topk, L);
+        if (bx == 0 && u == 0) write_route(L, e, m, topk, ids, wts, FUSED ? nullptr : route);
+        if (threadIdx.x == 0) {
+            s_nd = L.n_distinct;
+            if (u < L.n_distinct) {
+                s_ex = L.ex[u].expert;
+                s_cnt = L.ex[u].cnt;
+            }
+        }
+        if (threadIdx.x < 8 && u < L.n_distinct) {
+            tok[threadIdx.x] = L.ex[u].tok[threadIdx.x];
+            prs[threadIdx.x] = L.ex[u].pair[threadIdx.x];
         }
     }
-    if (threadIdx.x == 0) {
-        s_nd = L.n_distinct;
-        if (u < L.n_distinct) {
-            s_ex = L.ex[u].expert;
-            s_cnt = L.ex[u].cnt;
-        }
-    }
-    if (threadIdx.x < 8 && u < L.n_distinct) {
-        tok[threadIdx.x] = L.ex[u].tok[threadIdx.x];
-        prs[threadIdx.x] = L.ex[u].pair[threadIdx.x];
-    }
+    if (s_act) st_dev(&sh.sact[(size_t)st * I + si], (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv));
     __syncthreads();   // the routing scratch is free from here on
     if (u >= s_nd) return;
     const int ex = s_ex, cnt = s_cnt;
@@ -480,16 +507,30 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     }
 }
 
-template <int CPL>
+template <int CPL, bool PLANNED>
 __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                     int m, int E, int topk, nvfp4_moe_weights e,
                                                     int32_t *__restrict__ ids, float *__restrict__ wts,
                                                     MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
                                                     MoeShared sh) {
     extern __shared__ uint4 smem[];
-    gate_up_role<CPL, false>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts, route, act,
-                             sh, nullptr, 0);
+    gate_up_role<CPL, false, PLANNED>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts,
+                                      route, act, sh, nullptr, 0);
 }
+
+// The routing alone (one workgroup), for the planned gate/up launch.
+__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int m, int E, int topk,
+                                                  nvfp4_moe_weights e, int32_t *__restrict__ ids,
+                                                  float *__restrict__ wts, MoeRoute *__restrict__ route) {
+    __shared__ RouteLds L;
+    moe_route_lds(logits, m, E, topk, L);
+    write_route(L, e, m, topk, ids, wts, route);
+}
+
+// Rows per slot of the ticket down pass: 4 (a 64-row tile, about 37 KB of
+// weights per workgroup at inter = 1024; 16-row tiles were launch-bound).
+constexpr int kDownR = 4;
+constexpr int kDownTile = 16 * kDownR;
 
 template <int MT, int CPL>
 __device__ __forceinline__ void down_body(uint4 *xs, const uint16_t *act, const int *prs, int cnt, const uint8_t *dc,
@@ -497,8 +538,10 @@ __device__ __forceinline__ void down_body(uint4 *xs, const uint16_t *act, const 
     auto epi = [&](int row, int mm, float v) {
         if (mm < cnt) st_dev(&dbuf[(size_t)prs[mm] * H + row], v * ddec);
     };
-    if constexpr (CPL > 0) {
-        TileRegs<MT, 1, 1, CPL> t;
+    // preloading is kept to MT <= 2, as in gate/up, so that the rarer wide
+    // experts do not set the register budget of the kernel
+    if constexpr (CPL > 0 && MT <= 2) {
+        TileRegs<MT, kDownR, 1, CPL> t;
         gemv_tile_load(t, dc, ds, H, I, row0);
         stage_rows(xs, act, prs, cnt, MT, I);
         __syncthreads();
@@ -506,7 +549,8 @@ __device__ __forceinline__ void down_body(uint4 *xs, const uint16_t *act, const 
     } else {
         stage_rows(xs, act, prs, cnt, MT, I);
         __syncthreads();
-        gemv_tile_loop<MT, 1, 1, 0>(xs, dc, ds, H, I, row0, nullptr, epi);
+#pragma unroll 1
+        for (int i = 0; i < kDownR; ++i) gemv_tile_loop<MT, 1, 1, 0>(xs, dc, ds, H, I, row0 + 16 * i, nullptr, epi);
     }
 }
 
@@ -527,7 +571,7 @@ __global__ __launch_bounds__(256) void k_moe_down(nvfp4_moe_weights e, int m, in
     const size_t wsz = (size_t)H * I;
     const uint8_t *dc = e.down_codes + (size_t)ex * (wsz / 2), *ds = e.down_scales + (size_t)ex * (wsz / 16);
     const float ddec = e.down_global[ex].dec;
-    const int row0 = blockIdx.x * kMoeRows;
+    const int row0 = blockIdx.x * kDownTile;
     const int mt = round_up_mt(cnt);
     if (mt == 1) down_body<1, CPL>(smem, act, me->pair, cnt, dc, ds, ddec, H, I, row0, dbuf);
     else if (mt == 2) down_body<2, CPL>(smem, act, me->pair, cnt, dc, ds, ddec, H, I, row0, dbuf);
@@ -540,9 +584,8 @@ __global__ __launch_bounds__(256) void k_moe_down(nvfp4_moe_weights e, int m, in
     if (threadIdx.x == 0) s_last = atomicAdd(&tickets[blockIdx.x], 1u) == (unsigned)(nd - 1);
     __syncthreads();
     if (!s_last) return;
-    const int i = threadIdx.x;
-    if (i < m * kMoeRows) {
-        const int t = i / kMoeRows, row = row0 + (i - t * kMoeRows);
+    for (int i = threadIdx.x; i < m * kDownTile; i += blockDim.x) {
+        const int t = i / kDownTile, row = row0 + (i - t * kDownTile);
         if (row < H) {
             float acc = 0.0f;
             for (int j = 0; j < topk; ++j)
@@ -796,13 +839,31 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
     return L;
 }
 
+#ifndef NVFP4_MOE_PLAN_MIN_TOKENS
+#define NVFP4_MOE_PLAN_MIN_TOKENS 3
+#endif
+// Fewest tokens for which the two-launch path routes once, in its own
+// kernel, instead of in every gate/up workgroup.
+constexpr int kMoePlanMinTokens = NVFP4_MOE_PLAN_MIN_TOKENS;
+
 template <int CPL>
 static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
                           uint16_t *act, const MoeShared &sh) {
-    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL>), lds, "moe_w4a16_gemv");
+    if (m >= kMoePlanMinTokens) {
+        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), 0, s, logits, m, E, topk, e, ids, wts, route);
+        const int rc0 = check_launch("moe_w4a16_gemv(route)");
+        if (rc0) return rc0;
+        const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, true>), lds, "moe_w4a16_gemv");
+        if (rc) return rc;
+        hipLaunchKernelGGL((k_moe_gate_up<CPL, true>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route,
+                           act, sh);
+        return check_launch("moe_w4a16_gemv(gate_up)");
+    }
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, false>), lds, "moe_w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL(k_moe_gate_up<CPL>, g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act, sh);
+    hipLaunchKernelGGL((k_moe_gate_up<CPL, false>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route,
+                       act, sh);
     return check_launch("moe_w4a16_gemv(gate_up)");
 }
 template <int CPL>
@@ -905,7 +966,7 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const int E = e->num_experts, H = e->hidden, I = e->inter, mt = round_up_mt(m);
     const int maxd = min(E, m * top_k);
     const nvfp4_moe_weights ev = *e;
-    const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kMoeRows - 1) / kMoeRows, maxd);
+    const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kDownTile - 1) / kDownTile, maxd);
     const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
     const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
     // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows
