@@ -213,6 +213,7 @@ constexpr int kLmMfWaves = NVFP4_LM_MF_WAVES;
 constexpr int kLmMfDepth = NVFP4_LM_MF_DEPTH;   // 128-k steps of code loads in flight per lane
 constexpr bool kLmMfma = NVFP4_LM_MFMA;
 constexpr int kMfStageBytes = 3072;   // per wavefront: one code pair (2 KiB) and one scale round (1 KiB)
+
 // Fewest activation rows served by the MFMA units.  Their cost per unit does
 // not depend on M (16 rows of which M are used, and an fp32 multiply per
 // dequantized weight that the dot2 units fold into one per 16), while the
@@ -222,6 +223,14 @@ constexpr int kMfStageBytes = 3072;   // per wavefront: one code pair (2 KiB) an
 #define NVFP4_LM_MF_MIN_ROWS 4
 #endif
 constexpr int kLmMfMinRows = NVFP4_LM_MF_MIN_ROWS;
+
+// The MFMA units serve MT >= kLmMfMinRows rows when K is a whole number of
+// load rounds and the activation image plus the staging areas fit the LDS
+// (MT = 8: K <= 8192; larger K takes the dot2 units).
+inline bool lm_mf_fits(int mt, int k) {
+    return mt >= kLmMfMinRows && kLmMfma && k % (128 * kLmMfDepth) == 0 &&
+           (size_t)mt * k * 2 + (size_t)kLmMfWaves * kMfStageBytes <= kMaxLds;
+}
 
 // Next position in a workgroup's unit sequence: wavefronts draw from an LDS
 // counter (positions 0 .. NW-1 are the wavefronts' first units).
@@ -783,7 +792,7 @@ static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const n
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     if (lds > kMaxLds) return false;
-    if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
+    if (lm_mf_fits(MT, w->k)) {
         if constexpr (MT >= kLmMfMinRows)
             return launch_gemv_persist_k<MT, 0, true>((size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes, s, x,
                                                       m, w, y, bf16);
@@ -808,7 +817,7 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
     ok();   // clears the message that a refused LDS request would leave
-    if (MT >= kLmMfMinRows && w->k % (128 * kLmMfDepth) == 0 && kLmMfma) {
+    if (lm_mf_fits(MT, w->k)) {
         if constexpr (MT >= kLmMfMinRows) {
             const size_t lmf = (size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes;
             if (bk) lp ? launch_lm_kernel<MT, 0, true, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)

@@ -98,7 +98,7 @@ def test_no_write_outside_output(orc):
 # to eight rows), ragged row counts; the exact family makes every output bit
 # exact in any summation order.
 @pytest.mark.parametrize("m,n,k", [(1, 16387, 2048), (1, 32771, 512), (2, 49155, 256), (8, 8195, 1024),
-                                   (6, 20000, 2048)])
+                                   (6, 20000, 2048), (4, 8195, 1024), (8, 8195, 9216)])
 def test_persistent_grid_bit_exact(orc, m, n, k):
     import nvfp4_w4a16_mtp_amd as nv
     x, codes, scales, g = synth.exact_family(150 + m, m, n, k)

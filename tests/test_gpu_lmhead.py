@@ -63,10 +63,12 @@ def test_random_unplanted(orc, m):
     _check_certified(orc, h, codes, scales, glob[0])
 
 
-@pytest.mark.parametrize("m,v,k", [(5, 3001, 1024), (7, 1000, 3072), (8, 17, 2048), (6, 4096, 7168)])
+@pytest.mark.parametrize("m,v,k", [(5, 3001, 1024), (7, 1000, 3072), (8, 17, 2048), (6, 4096, 7168), (4, 999, 2048),
+                                   (8, 700, 9216)])
 def test_random_unplanted_eight_row_units(orc, m, v, k):
-    """Five to eight rows with K a multiple of 1024 (16-row MFMA units):
-    ragged vocabularies, rows padded to eight."""
+    """Four to eight rows with K a multiple of 1024 (16-row MFMA units):
+    ragged vocabularies, rows padded; at K = 9216 eight rows and the staging
+    areas exceed the LDS and the dot2 units serve them."""
     w = synth.weight_bf16(60 + m, v, k)
     h = synth.acts_bf16(60 + m, m, k)
     codes, scales, glob = orc.quantize(w)
