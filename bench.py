@@ -303,6 +303,13 @@ def _time_graph(torch, fn, reps, stream):
     return e0.elapsed_time(e1) / (3 * reps)
 
 
+def randn_like_rows(torch, m, k, dev):
+    """Seeded N(0, 1) activations [m, k] in bf16."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + m * 7 + k)
+    return torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+
+
 def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
     """Per-row device timings (graph-captured launches over rotating weight
     copies), each with its roofline fraction."""
@@ -365,6 +372,40 @@ def rows_measure(nv, torch, copies, xs, ys, xm, router, hl, M, s):
     out["moe_layer_router_shared"] = {"ms": round(ms, 5), "extra_weight_bytes": nvfp4_lay,
                                       "gbs": round(lb / ms / 1e6, 1), "frac": round(lb / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del lay
+    # the decode rows of the workload at several tokens (M = 4, 8): the q
+    # projection, the LM head and the MoE (rotating weight copies, graph-timed)
+    if M == 1:
+        rows_m = {}
+        for mm in (4, 8):
+            xq = randn_like_rows(torch, mm, 2048, hl.device)
+            yq = torch.empty((mm, 8192), dtype=torch.float32, device=hl.device)
+            ms = _time_graph(torch, lambda i: nv.w4a16_gemv(xq, copies[i % NCOPIES]["q"], out=yq), reps, s)
+            b = nvfp4_bytes(8192, 2048) + mm * 2048 * 2 + mm * 8192 * 4
+            rows_m[f"gemv_q_m{mm}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                       "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            wsm = nv.lmhead_workspace(mm, VOCAB, hl.device)
+            oim = torch.empty(mm, dtype=torch.int32, device=hl.device)
+            omm = torch.empty(mm, dtype=torch.float32, device=hl.device)
+            hm = randn_like_rows(torch, mm, H, hl.device)
+            ms = _time_graph(torch, lambda i: nv.lmhead_gemv_argmax(hm, copies[i % NCOPIES]["lm"], vocab_rows=VOCAB,
+                                                                    workspace=wsm, out_idx=oim, out_max=omm), reps, s)
+            b = nvfp4_bytes(VOCAB, H) + mm * H * 2 + mm * 8
+            rows_m[f"lmhead_v{VOCAB}_m{mm}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                                "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                                "drafts_per_s": round(mm / (ms * 1e-3), 1)}
+            xmm = randn_like_rows(torch, mm, H, hl.device)
+            rm = torch.randn((mm, E), generator=torch.Generator(device=hl.device).manual_seed(10 + mm), device=hl.device)
+            wsq = nv.moe_workspace(mm, TOPK, copies[0]["moe"], hl.device)
+            ymm = torch.empty((mm, H), dtype=torch.float32, device=hl.device)
+            idm = torch.empty((mm, TOPK), dtype=torch.int32, device=hl.device)
+            wtm = torch.empty((mm, TOPK), dtype=torch.float32, device=hl.device)
+            ms = _time_graph(torch, lambda i: nv.moe_w4a16_gemv(xmm, rm, TOPK, copies[i % NCOPIES]["moe"], workspace=wsq,
+                                                                out=ymm, topk_ids=idm, topk_w=wtm), reps, s)
+            ndm = len(set(idm.cpu().numpy().ravel().tolist()))
+            b = ndm * 3 * nvfp4_bytes(I, H) + mm * H * 2 + mm * E * 4 + mm * H * 4 + 2 * mm * TOPK * 4
+            rows_m[f"moe_m{mm}"] = {"ms": round(ms, 5), "gbs": round(b / ms / 1e6, 1),
+                                    "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "distinct_experts": ndm}
+        out["rows_m4_m8"] = rows_m
     # quantizer on the largest matrix (the LM head): clear, absmax and encode
     # launches back to back; bytes = 2 reads of the bf16 tensor + the NVFP4 write
     wq = (torch.randn((VOCAB, H), generator=gen2, device=hl.device) * 0.02).to(torch.bfloat16)
