@@ -111,3 +111,17 @@ def test_errors():
         nv.w4a16_gemv_grouped(x, [w64, w128])                # k differs
     with pytest.raises(nv.NVFP4Error):
         nv.w4a16_gemv_grouped(torch.zeros((9, 64), dtype=torch.bfloat16, device="cuda"), [w64])
+
+
+@pytest.mark.parametrize("m", [5, 8])
+def test_rows_beyond_the_lds_go_in_groups(orc, m):
+    """Two weights at K = 17408: round_up(m) rows of activations exceed the
+    LDS, so the rows go in groups (5 -> 4 + 1, 8 -> 4 + 4); each group's
+    outputs land at its row offset in every output (bit exact on the exact
+    family)."""
+    import nvfp4_w4a16_mtp_amd as nv
+    parts = [synth.exact_family(230 + 5 * i + m, m, n, 17408) for i, n in enumerate((96, 33))]
+    x = parts[0][0]
+    ys = nv.w4a16_gemv_grouped(dev_bf16(x), [_w(c, s, g) for _, c, s, g in parts])
+    for (_, c, s, g), y in zip(parts, ys):
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.gemv(x, c, s, g).view(np.uint32))
