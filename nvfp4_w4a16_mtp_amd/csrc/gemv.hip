@@ -141,6 +141,26 @@ __device__ __forceinline__ void argpart_shfl_combine(ArgPart &b, int off) {
     argpart_combine<LP>(b, o);
 }
 
+// The same combine with the state of the lane OFF places along a 16-lane row
+// (DPP row rotate, a VALU operation: a cross-lane shuffle goes through the
+// LDS unit and its latency chains through every step).  Rotating by 8, 4, 2
+// and 1 leaves every lane of a row with the row's combination; by 8, 4, ...,
+// MT the combination of the row's lanes of one class mod MT.
+template <bool LP, int OFF>
+__device__ __forceinline__ void argpart_row_combine(ArgPart &b) {
+    static_assert(OFF >= 1 && OFF < 16, "a rotation inside a 16-lane row");
+    constexpr int ctrl = 0x120 + OFF;   // row_ror:OFF
+    ArgPart o;
+    o.key = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b.key), ctrl, 0xF, 0xF, false));
+    o.val = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b.val), ctrl, 0xF, 0xF, false));
+    o.idx = __builtin_amdgcn_update_dpp(0, b.idx, ctrl, 0xF, 0xF, false);
+    if constexpr (LP) {
+        o.lm = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b.lm), ctrl, 0xF, 0xF, false));
+        o.ls = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b.ls), ctrl, 0xF, 0xF, false));
+    }
+    argpart_combine<LP>(b, o);
+}
+
 // Argmax as one unsigned 64-bit word whose order is that of beats(): the
 // key's bits made monotone in the upper half (-0 taken as +0, so equal keys
 // compare equal), the complemented index in the lower half (a lower index
@@ -255,7 +275,14 @@ __device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], in
     ArgPart c{-INFINITY, -INFINITY, INT_MAX, -INFINITY, 0.0f, {0, 0, 0}};
     for (int w = w0; w < NW; w += LW) argpart_combine<LP>(c, wb[w][mm]);
 #pragma unroll
-    for (int off = SPAN * MT / 2; off >= MT; off >>= 1) argpart_shfl_combine<LP>(c, off);
+    for (int off = SPAN * MT / 2; off >= 16; off >>= 1) argpart_shfl_combine<LP>(c, off);   // across rows
+    // inside the row: every rotation from 8 down to MT (a rotation covers a
+    // window of lanes, not an aligned block, so none may be skipped even when
+    // the entries fill only part of the row; the other lanes hold -inf)
+    argpart_row_combine<LP, 8>(c);
+    if constexpr (MT <= 4) argpart_row_combine<LP, 4>(c);
+    if constexpr (MT <= 2) argpart_row_combine<LP, 2>(c);
+    if constexpr (MT <= 1) argpart_row_combine<LP, 1>(c);
     return c;
 }
 
@@ -532,8 +559,10 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             ArgPart c{mk[r], mv[r], mi[r], mlm[r], mls[r], {0, 0, 0}};
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) argpart_shfl_combine<LP>(c, off);
+            argpart_row_combine<LP, 8>(c);
+            argpart_row_combine<LP, 4>(c);
+            argpart_row_combine<LP, 2>(c);
+            argpart_row_combine<LP, 1>(c);
             const int mm = 4 * (lane >> 4) + r;
             if ((lane & 15) == 0 && mm < MT) wbest[wave][mm] = c;
         }
