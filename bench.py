@@ -59,8 +59,8 @@ def parse():
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this build runs on a single "
-              "MI355X; the multi-GPU sharding is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: the library's kernels run on a "
+              "single MI355X", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
