@@ -310,13 +310,13 @@ __device__ __forceinline__ void stage_fma(const uint4 (&cw)[U][R], const uint32_
     }
 }
 
-// R rows (code and scale row pointers cp, sp) against the activation image,
-// for a lane that owns chunks tl, tl + 16, ... of C (C % 16 == 0): stages of
-// U chunks, the loads of stage s + 1 in flight while stage s is computed.
+// R rows (code and scale row pointers cp, sp) against the activation image
+// (C chunks a row), for a lane that owns the nc chunks tl, tl + 16, ...:
+// stages of U chunks, the loads of stage s + 1 in flight while stage s is
+// computed.
 template <int MT, int R, int U>
 __device__ __forceinline__ void pipe_rows(const uint4 *xs, const uint8_t *const (&cp)[R], const uint8_t *const (&sp)[R],
-                                          int C, int tl, float (&acc)[R][MT]) {
-    const int nc = C >> 4;
+                                          int C, int tl, int nc, float (&acc)[R][MT]) {
     const int ns = (nc + U - 1) / U;
     uint4 ca[U][R], cb[U][R];
     uint32_t sa[U][R], sb[U][R];
@@ -353,8 +353,9 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
-    if (U > 0 && KS == 1 && (C & 15) == 0) {
-        // every lane owns the same C / 16 chunks: pipelined stages
+    if (U > 0 && ((c_hi - c_lo) & 15) == 0 && c_hi - c_lo == cs) {
+        // every lane owns the same cs / 16 chunks of its K slice: pipelined
+        // stages
         const uint8_t *cp[R], *sp[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -363,7 +364,7 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
             sp[r] = scales + (size_t)row * (size_t)(k >> 4);
         }
         constexpr int UP = U > 0 ? U : 1;
-        pipe_rows<MT, R, UP>(xs, cp, sp, C, tl, acc);
+        pipe_rows<MT, R, UP>(xs, cp, sp, C, c_lo + tl, cs >> 4, acc);
     } else {
         for (int c = c_lo + tl; c < c_hi; c += 16) {
             uint4 cw[R];
@@ -513,11 +514,17 @@ inline TileChoice choose_tile(int n, int k, int mt, int min_tiles, size_t extra_
     for (const auto &o : order) {
         TileChoice c{o[0], o[1], 0};
         if (c.KS > 1 && gemv_lds_bytes(mt, k, c) + extra_lds > (size_t)kLdsBytes) break;
-        // a K split only with a fixed chunk count (the generic loop pipelines
-        // its loads only without a split)
-        if (c.KS > 1 && !(k % (512 * c.KS) == 0 && (k / (512 * c.KS) == 1 || k / (512 * c.KS) == 2 ||
-                                                    k / (512 * c.KS) == 4)))
-            continue;
+        // a K split only where every lane gets the same chunk count (the
+        // fixed counts 1, 2, 4, or the pipelined generic loop).  With one
+        // activation row the generic loop splits only a grid under a third
+        // of min_tiles: there a lane's loads already cover the latency, and
+        // the split's partial-sum exchange costs more than the extra tiles
+        // gain (measured at 17408 x 5120 and 18432 x 7168).
+        if (c.KS > 1 && k % (512 * c.KS) != 0) continue;
+        if (c.KS > 1 && mt == 1) {
+            const int cpl = k / (512 * c.KS);
+            if (cpl != 1 && cpl != 2 && cpl != 4 && (n + 15) / 16 >= min_tiles / 3) continue;
+        }
         pick = c;
         const int rows = 16 * c.R / c.KS;
         if ((n + rows - 1) / rows >= min_tiles) {

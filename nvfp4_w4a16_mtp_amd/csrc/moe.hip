@@ -347,7 +347,7 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
             for (int r = 0; r < 2; ++r)
 #pragma unroll
                 for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
-            pipe_rows<MT, 2, kPairU>(xs, cp, sp, H >> 5, tl, acc);
+            pipe_rows<MT, 2, kPairU>(xs, cp, sp, H >> 5, tl, H >> 9, acc);
 #pragma unroll
             for (int mm = 0; mm < MT; ++mm) {
                 const float g = row16_sum(acc[0][mm]), u = row16_sum(acc[1][mm]);

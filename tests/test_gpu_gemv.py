@@ -107,6 +107,19 @@ def test_persistent_grid_bit_exact(orc, m, n, k):
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
+# Few row tiles and K a multiple of 512 per wavefront slice with a chunk
+# count outside 1, 2, 4 (5, 7, 3, 6, 17 a lane): the K split of the
+# pipelined generic loop, with a partial last stage, ragged row counts.
+@pytest.mark.parametrize("m,n,k", [(1, 333, 5120), (2, 200, 7168), (4, 90, 3072), (1, 100, 12288),
+                                   (1, 1041, 17408), (2, 1040, 5120)])
+def test_k_split_pipelined_bit_exact(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(170 + m, m, n, k)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("m,n,k", [(5, 300, 10240), (8, 301, 17408), (3, 77, 40960)])
 def test_rows_beyond_the_lds_go_in_groups(orc, m, n, k):
     """round_up(m) rows of K do not fit the LDS image: the rows go in groups
