@@ -42,13 +42,13 @@ struct GemvGroups {
 template <int R>
 constexpr int gemv_pipe() { return R >= NVFP4_GEMV_PIPE ? 1 : NVFP4_GEMV_PIPE / R; }
 
-template <int MT, int R, int KS, int CPL>
-__global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
+template <int MT, int R, int KS, int CPL, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
                                              int bf16out) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     float *red = reinterpret_cast<float *>(smem + (MT * k) / 8);
-    constexpr int rows = GemvTile<R, KS>::kRowsPerTile;
+    constexpr int rows = GemvTile<R, KS, NW>::kRowsPerTile;
     // group of this workgroup: selects with constant indices keep the table
     // in scalar registers (a dynamic index would copy it to private memory)
     const int tile = blockIdx.x;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void k_gemv(const uint16_t *__restrict__ x, in
     } else {
         stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
         __syncthreads();
-        gemv_tile_loop<MT, R, KS, gemv_pipe<R>()>(xs, codes, scales, n, k, row0, red, epi);
+        gemv_tile_loop<MT, R, KS, gemv_pipe<R>(), false, (NW > 4)>(xs, codes, scales, n, k, row0, red, epi);
     }
 }
 
@@ -687,7 +687,9 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
 // per lane or 0 for the generic loop).
 #define NVFP4_TILE_SWITCH(FN, MT, tc, ...)                                               \
     do {                                                                                 \
-        if (tc.R == 4 && tc.KS == 1 && tc.CPL == 4) FN<MT, 4, 1, 4>(__VA_ARGS__);        \
+        if (tc.NW == 16 && tc.KS == 4) FN<MT, 1, 4, 0, 16>(__VA_ARGS__);                 \
+        else if (tc.NW == 8 && tc.KS == 2) FN<MT, 1, 2, 0, 8>(__VA_ARGS__);              \
+        else if (tc.R == 4 && tc.KS == 1 && tc.CPL == 4) FN<MT, 4, 1, 4>(__VA_ARGS__);   \
         else if (tc.R == 4 && tc.KS == 1 && tc.CPL == 2) FN<MT, 4, 1, 2>(__VA_ARGS__);   \
         else if (tc.R == 4 && tc.KS == 1) FN<MT, 4, 1, 0>(__VA_ARGS__);                  \
         else if (tc.R == 2 && tc.KS == 1 && tc.CPL == 4) FN<MT, 2, 1, 4>(__VA_ARGS__);   \
@@ -705,6 +707,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
 
 // Reduces a tile choice to the instantiated set above.
 static TileChoice canonical(TileChoice tc) {
+    if (tc.NW != 4) return TileChoice{1, tc.NW == 16 ? 4 : 2, 0, tc.NW == 16 ? 16 : 8};
     if (tc.KS == 1 && tc.R == 4 && tc.CPL != 4 && tc.CPL != 2) tc.CPL = 0;
     if (tc.KS == 1 && tc.R == 2 && tc.CPL != 4) tc.CPL = 0;
     if (tc.KS == 1 && tc.R == 1 && tc.CPL != 4 && tc.CPL != 2) tc.CPL = 0;
@@ -713,11 +716,11 @@ static TileChoice canonical(TileChoice tc) {
     return tc;
 }
 
-template <int MT, int R, int KS, int CPL>
+template <int MT, int R, int KS, int CPL, int NW = 4>
 static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const GemvGroups &grp,
                             int k, int bf16) {
-    if (allow_lds(reinterpret_cast<const void *>(k_gemv<MT, R, KS, CPL>), lds, "w4a16_gemv")) return;
-    hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL>), grid, dim3(256), lds, s, x, m, grp, k, bf16);
+    if (allow_lds(reinterpret_cast<const void *>(k_gemv<MT, R, KS, CPL, NW>), lds, "w4a16_gemv")) return;
+    hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL, NW>), grid, dim3(64 * NW), lds, s, x, m, grp, k, bf16);
 }
 
 // Tile target of a GEMV launch: at least this many workgroups per CU (a
@@ -736,6 +739,23 @@ constexpr bool kGemvPersist = NVFP4_GEMV_PERSIST;
 template <int MT>
 static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16);
 
+// An activation image that leaves LDS for at most three workgroups a CU (a
+// quarter of it or more) caps the per-tile grid at 4 to 12 wavefronts a CU,
+// too few to keep the weight loads in flight: then wide workgroups of
+// 16 rows whose K is split over 2 (two workgroups fit) or 4 (one fits)
+// wavefront groups.
+#ifndef NVFP4_GEMV_WIDE
+#define NVFP4_GEMV_WIDE 1
+#endif
+static TileChoice wide_tile(TileChoice tc, int mt, int k) {
+    if (!NVFP4_GEMV_WIDE || tc.KS != 1 || tc.CPL != 0) return tc;
+    const size_t image = (size_t)mt * k * 2, cu_lds = 160 * 1024;
+    if (4 * image < cu_lds) return tc;
+    const TileChoice w4{1, 4, 0, 16}, w2{1, 2, 0, 8};
+    if (2 * gemv_lds_bytes(mt, k, w2) > cu_lds && gemv_lds_bytes(mt, k, w4) <= kMaxLds) return w4;
+    return gemv_lds_bytes(mt, k, w2) <= kMaxLds ? w2 : tc;
+}
+
 template <int MT>
 static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
                          hipStream_t s) {
@@ -747,8 +767,8 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
     }
     int total_n = 0;
     for (int i = 0; i < count; ++i) total_n += w[i]->n;
-    const TileChoice tc = canonical(choose_tile(total_n, k, MT, NVFP4_GEMV_TPC * num_cus(), 0));
-    const int rows = 16 * tc.R / tc.KS;
+    const TileChoice tc = canonical(wide_tile(choose_tile(total_n, k, MT, NVFP4_GEMV_TPC * num_cus(), 0), MT, k));
+    const int rows = 4 * (tc.NW / tc.KS) * tc.R;
     GemvGroups grp{};
     grp.count = count;
     int tiles = 0;

@@ -14,7 +14,11 @@
 //    = 32 weights per chunk) round-robin;
 //  * with KS > 1 the 4 wavefronts split K into KS segments over the same
 //    rows (for short-and-wide matrices that would otherwise leave CUs idle);
-//  * a workgroup tile is 16 * R / KS rows.
+//  * a workgroup tile is 16 * R / KS rows;
+//  * a wide workgroup (NW = 4 * KS wavefronts) keeps 16 * R rows a tile and
+//    splits their K over KS wavefront groups: for activation images so large
+//    that one workgroup fills a CU's LDS, it puts 4 * KS wavefronts on the
+//    CU instead of 4.
 // When every lane owns exactly CPL chunks of each row (K = 512 * KS * CPL),
 // all R * CPL chunk loads of a tile are issued before any arithmetic, so a
 // wavefront keeps R * CPL * 1 KiB in flight; other shapes take a loop.
@@ -66,9 +70,9 @@ __device__ __forceinline__ void stage_x(uint4 *xs, const uint4 *__restrict__ x, 
     }
 }
 
-template <int R, int KS>
+template <int R, int KS, int NW = 4>
 struct GemvTile {
-    static constexpr int kRowsPerTile = 16 * R / KS;
+    static constexpr int kRowsPerTile = 4 * (NW / KS) * R;
 };
 
 // One chunk of one row: dot products with the MT activation rows, scaled.
@@ -281,8 +285,8 @@ __device__ __forceinline__ void gemv_tile_compute_x1(const TileRegs<1, R, KS, CP
 }
 
 // One stage of the pipelined loop: chunks c0, c0 + 16, ... of the slot's R
-// rows, the first `left` of them (a stage count that is the same in every
-// lane keeps the branch uniform).
+// rows, the first `left` of them (uniform where every lane of the wavefront
+// owns the same chunk count).
 template <int U, int R>
 __device__ __forceinline__ void stage_load(uint4 (&cw)[U][R], uint32_t (&sw)[U][R], const uint8_t *const (&cp)[R],
                                            const uint8_t *const (&sp)[R], int c0, int left) {
@@ -334,8 +338,9 @@ __device__ __forceinline__ void pipe_rows(const uint4 *xs, const uint8_t *const 
 
 // Generic shape (any K % 32 == 0): loop over the lane's chunks.  U > 0:
 // pipelined stages of U chunks where every lane owns the same number of
-// chunks; U = 0: one chunk at a time (the fewest registers).
-template <int MT, int R, int KS, int U = (R >= 4 ? 1 : 4 / R), bool WT = false, class Epi>
+// chunks, or (UNEVEN) in any K split; otherwise one chunk at a time (the
+// fewest registers).
+template <int MT, int R, int KS, int U = (R >= 4 ? 1 : 4 / R), bool WT = false, bool UNEVEN = false, class Epi>
 __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *__restrict__ codes,
                                                const uint8_t *__restrict__ scales, int n, int k, int row0, float *red,
                                                Epi &&epi) {
@@ -353,18 +358,28 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm) acc[r][mm] = 0.0f;
-    if (U > 0 && ((c_hi - c_lo) & 15) == 0 && c_hi - c_lo == cs) {
-        // every lane owns the same cs / 16 chunks of its K slice: pipelined
-        // stages
-        const uint8_t *cp[R], *sp[R];
+    const uint8_t *cp[R], *sp[R];
+    auto row_ptrs = [&]() {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = min(rbase + r, n - 1);   // rows past n: never passed to the epilogue
             cp[r] = codes + (size_t)row * (size_t)(k >> 1);
             sp[r] = scales + (size_t)row * (size_t)(k >> 4);
         }
-        constexpr int UP = U > 0 ? U : 1;
+    };
+    constexpr int UP = U > 0 ? U : 1;
+    if (U > 0 && (cs & 15) == 0 && c_hi - c_lo == cs) {
+        // the same count in every lane, from the kernel arguments alone: a
+        // scalar loop
+        row_ptrs();
         pipe_rows<MT, R, UP>(xs, cp, sp, C, c_lo + tl, cs >> 4, acc);
+    } else if constexpr (U > 0 && KS > 1 && UNEVEN) {
+        // K slices whose counts differ by one between the lanes: still
+        // pipelined (elsewhere the single-chunk loop below keeps the register
+        // count of the common kernels down)
+        const int c0 = c_lo + tl;
+        row_ptrs();
+        pipe_rows<MT, R, UP>(xs, cp, sp, C, c0, c0 < c_hi ? (c_hi - c0 + 15) >> 4 : 0, acc);
     } else {
         for (int c = c_lo + tl; c < c_hi; c += 16) {
             uint4 cw[R];
@@ -491,15 +506,16 @@ __device__ __forceinline__ int mf_code_rslot(int li, int q, int h) {   // step h
 // ---------------------------------------------------------------- host ----
 struct TileChoice {
     int R, KS, CPL;   // CPL 0: generic loop
+    int NW = 4;       // wavefronts a workgroup
 };
 
 constexpr int kLdsBytes = 64 * 1024;   // LDS budget of one workgroup when choosing a K split
 constexpr size_t kMaxLds = 160 * 1024 - 8192;   // largest activation image (LDS per workgroup, static LDS aside)
 
 // LDS bytes of a GEMV workgroup: the activation image plus, with a K split,
-// 16 * R * MT fp32 partial sums.
+// 4 * NW * R * MT fp32 partial sums (one a slot, row and activation row).
 inline size_t gemv_lds_bytes(int mt, int k, TileChoice tc) {
-    return (size_t)mt * k * 2 + (tc.KS > 1 ? (size_t)16 * tc.R * mt * 4 : 0);
+    return (size_t)mt * k * 2 + (tc.KS > 1 ? (size_t)4 * tc.NW * tc.R * mt * 4 : 0);
 }
 
 // Tile shape for an n x k weight and MT activation rows: the largest R

@@ -120,6 +120,20 @@ def test_k_split_pipelined_bit_exact(orc, m, n, k):
     assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
 
 
+# Activation images of a quarter of a CU's LDS or more: wide workgroups
+# (8 or 16 wavefronts, the K of 16 rows split over 2 or 4 wavefront groups),
+# K slices whose chunk counts differ between the lanes (17408 / 32 / 4 = 136
+# chunks over 16 lanes), ragged row counts.
+@pytest.mark.parametrize("m,n,k", [(2, 700, 17408), (4, 333, 17408), (3, 300, 10240), (8, 120, 5120),
+                                   (2, 90, 12288), (4, 17, 9728)])
+def test_wide_workgroups_bit_exact(orc, m, n, k):
+    import nvfp4_w4a16_mtp_amd as nv
+    x, codes, scales, g = synth.exact_family(190 + m, m, n, k)
+    y = nv.w4a16_gemv(dev_bf16(x), _w(codes, scales, g)).cpu().numpy()
+    ref = orc.gemv(x, codes, scales, g)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("m,n,k", [(5, 300, 10240), (8, 301, 17408), (3, 77, 40960)])
 def test_rows_beyond_the_lds_go_in_groups(orc, m, n, k):
     """round_up(m) rows of K do not fit the LDS image: the rows go in groups
