@@ -969,8 +969,11 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kDownTile - 1) / kDownTile, maxd);
     const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
     const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
-    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows
-    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : (size_t)kLdsBytes - 16384;
+    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows.
+    // Without a shared expert it serves one token only: at 2 and 3 tokens
+    // (16 and 23 experts) the ticket pass took 22.3 and 30.6 us against 23.4
+    // and 34.2, and the one-launch path needs the row-owner pass only at one.
+    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : m == 1 ? (size_t)kLdsBytes - 16384 : 0;
     const bool row_owner = pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0;
     if (row_owner && kMoeFused) {
         // one launch: gate/up workgroups, then the row-owner down workgroups

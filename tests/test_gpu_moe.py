@@ -30,7 +30,7 @@ def _run(orc, experts_np, dev_experts, x, r, topk):
     assert_close(y.cpu().numpy(), ry, "moe output")
 
 
-@pytest.mark.parametrize("m,topk", [(1, 1), (3, 4), (3, 8), (5, 8), (8, 8), (8, 16)])
+@pytest.mark.parametrize("m,topk", [(1, 1), (2, 4), (2, 8), (3, 4), (3, 8), (5, 8), (8, 8), (8, 16)])
 def test_small(orc, m, topk):
     ex = synth.moe_quantized_experts(1, 32, 256, 128)
     x = synth.acts_bf16(1 + m, m, 256)

@@ -14,7 +14,7 @@ from tests.test_gpu_moe import _dev_experts
 
 pytestmark = pytest.mark.gpu
 
-H, I, E, TOPK = 2048, 512, 64, 8   # one launch holds every workgroup at m = 1 and 2
+H, I, E, TOPK = 2048, 512, 64, 8   # m = 1: one launch holding every workgroup; m = 2: two launches, the ticket down pass
 
 
 @pytest.fixture(scope="module")
