@@ -730,6 +730,13 @@ static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t
 #ifndef NVFP4_GEMV_TPC
 #define NVFP4_GEMV_TPC 6
 #endif
+// From four activation rows on, 2 per CU: each tile then has more rows and
+// its lanes more arithmetic between loads (q|k|v grouped at M = 4 in 6.9 us
+// against 8.3 at 6 per CU; the single q, fc and 4096 x 2048 GEMVs equal or
+// faster).
+#ifndef NVFP4_GEMV_TPC_M4
+#define NVFP4_GEMV_TPC_M4 2
+#endif
 // One launch over `count` weights with a common K (their tiles concatenated);
 // the tile shape is chosen for the total row count.
 #ifndef NVFP4_GEMV_PERSIST
@@ -767,7 +774,8 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
     }
     int total_n = 0;
     for (int i = 0; i < count; ++i) total_n += w[i]->n;
-    const TileChoice tc = canonical(wide_tile(choose_tile(total_n, k, MT, NVFP4_GEMV_TPC * num_cus(), 0), MT, k));
+    const int tpc = MT >= 4 ? NVFP4_GEMV_TPC_M4 : NVFP4_GEMV_TPC;
+    const TileChoice tc = canonical(wide_tile(choose_tile(total_n, k, MT, tpc * num_cus(), 0), MT, k));
     const int rows = 4 * (tc.NW / tc.KS) * tc.R;
     GemvGroups grp{};
     grp.count = count;
