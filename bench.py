@@ -512,7 +512,7 @@ def cpu_baseline(M, step_bytes, n_distinct):
     sample: whole draft steps of the same shapes on synthetic NVFP4 weights,
     repeated for about 10 s."""
     import oracle
-    from nvfp4_w4a16_mtp_amd import synth
+    from tests import synth
     rng = np.random.default_rng(0)
     W = {name: synth.quantized_domain_weight(rng, n, k) for name, n, k in PROJ}
     lm = synth.quantized_domain_weight(rng, VOCAB, H)

@@ -19,7 +19,8 @@
  *    The caller owns every buffer; the library allocates nothing, keeps no
  *    state between calls and is safe to call from several host threads.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on it and returns; it never synchronizes or reads back.
+ *    enqueues work on it and returns; it never synchronizes or reads back
+ *    (moe_workspace_status, a host query, is the one exception).
  *  - Return value: NVFP4_OK (0) or a negative status.  Arguments are checked
  *    on the host before anything is enqueued; on failure nothing is enqueued
  *    and nvfp4_mtp_last_error() describes the problem.
@@ -91,7 +92,8 @@ enum {
     NVFP4_ERR_ALIGN = -3,       /* a pointer misses its alignment         */
     NVFP4_ERR_WORKSPACE = -4,   /* workspace missing or too small         */
     NVFP4_ERR_UNSUPPORTED = -5, /* shape the kernels do not handle        */
-    NVFP4_ERR_HIP = -6          /* kernel launch failed (message has why) */
+    NVFP4_ERR_HIP = -6,         /* kernel launch failed (message has why) */
+    NVFP4_ERR_DEVICE = -7       /* a kernel reported a failure (workspace status) */
 };
 
 enum { NVFP4_OUT_F32 = 0, NVFP4_OUT_BF16 = 1 };
@@ -348,6 +350,25 @@ int moe_layer_w4a16(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *route
                     const nvfp4_weight *shared_up, const nvfp4_weight *shared_down,
                     const uint16_t *shared_gate_w_bf16, float *y, int32_t *topk_ids, float *topk_w,
                     float *router_logits, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * moe_workspace_status -- reads and clears the sticky status word of a
+ * moe_w4a16_gemv / moe_layer_w4a16 workspace.  In the one-launch path the
+ * down workgroups wait (bounded, about a second) for the gate/up workgroups
+ * of the same launch, released through per-workgroup go words that carry
+ * a per-call tag (a release left over from an earlier call never satisfies
+ * a later wait).  If a wait gives up, or a go word holds a value no call
+ * writes (the workspace was overwritten), that down workgroup writes NaN
+ * rows into y and sets bit 0 (timeout) or bit 1 (overwritten) of this
+ * word; the call itself has already returned NVFP4_OK.
+ *   workspace  the MoE workspace (device), ws_bytes its size.
+ *   status     host uint32: receives the bits (0 after clean calls).
+ * Synchronizes `stream` (not allowed during graph capture:
+ * NVFP4_ERR_UNSUPPORTED).  Returns NVFP4_OK when no bit was set, else
+ * NVFP4_ERR_DEVICE with the reason in nvfp4_mtp_last_error(); an
+ * overwritten workspace must be zero-filled again before its next use.
+ */
+int moe_workspace_status(void *workspace, size_t ws_bytes, uint32_t *status, void *stream);
 
 /* Message of the last failing call on this host thread ("" if none); the
  * pointer stays valid until the next call on the same thread. */

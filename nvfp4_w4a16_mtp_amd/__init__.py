@@ -6,11 +6,18 @@ kernels.  PyTorch supplies device memory and the current stream.  If the
 library is not built the calls raise -- there is no fallback.
 
 Operations (same names as the C ABI):
-  nvfp4_quantize       bf16 W[n, k] -> NVFP4Weight (codes, scales, global)
-  w4a16_gemv           x[m<=8, k] @ W^T
-  w4a16_gemm_m128      x[m, k] @ W^T for prompt-sized m (bf16 MFMA)
-  lmhead_gemv_argmax   argmax over the first V rows of h @ W^T
-  moe_w4a16_gemv       top-k routed NVFP4 expert FFN
+  nvfp4_quantize               bf16 W[n, k] -> NVFP4Weight (codes, scales, global)
+  w4a16_gemv                   x[m<=8, k] @ W^T
+  w4a16_gemv_grouped           the GEMV for several weights sharing x (q|k|v, gate|up)
+  w4a16_gemm_m128              x[m, k] @ W^T for prompt-sized m (bf16 MFMA)
+  lmhead_gemv_argmax           argmax over the first V rows of h @ W^T
+  lmhead_gemv_argmax_logprob   ... plus the top-1 log-probability
+  lmhead_gemv_argmax_masked    ... restricted to a grammar's allowed tokens
+  lmhead_gemv_argmax_embed     ... with the draft tokens' embedding rows gathered
+  embed_from_argmax            embedding rows of device-resident token ids
+  moe_w4a16_gemv               top-k routed NVFP4 expert FFN
+  moe_layer_w4a16              router + routed experts + gated shared expert
+  moe_workspace_status         sticky status of a MoE workspace (host query)
 """
 from __future__ import annotations
 
@@ -76,10 +83,11 @@ def lib():
         L.moe_layer_w4a16_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_layer_w4a16_workspace_bytes.restype = sz
         L.moe_layer_w4a16.argtypes = [P, i32, WP, i32, EP, WP, WP, WP, P, P, P, P, P, P, sz, P]
+        L.moe_workspace_status.argtypes = [P, sz, ctypes.POINTER(u32), P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
-                  "moe_w4a16_gemv", "moe_layer_w4a16"):
+                  "moe_w4a16_gemv", "moe_layer_w4a16", "moe_workspace_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -427,6 +435,17 @@ def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, exp
                                 _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x)),
            "moe_w4a16_gemv")
     return out, topk_ids, topk_w
+
+
+def moe_workspace_status(workspace: torch.Tensor) -> int:
+    """Reads and clears the sticky status word of a MoE workspace
+    (synchronizes the current stream).  Returns 0; raises NVFP4Error when a
+    down pass gave up its wait or found the workspace overwritten."""
+    _dev(workspace, "workspace")
+    st = ctypes.c_uint32(0)
+    _check(lib().moe_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      ctypes.byref(st), _stream(workspace)), "moe_workspace_status")
+    return st.value
 
 
 def moe_layer_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Tensor:

@@ -34,11 +34,26 @@ constexpr int kMoeHeader = 16384;   // route header bytes at the start of the wo
 constexpr int kPairU = NVFP4_PAIR_U;   // chunks per pipeline stage of the gate|up row pair
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
 constexpr int kSpinLimit = 1 << 22;    // polls of the fused down pass's wait (seconds)
-// Hand-off words of the fused launch (zero between calls), each counter on
-// its own 128-byte line: per expert column u a count of its finished gate/up
-// workgroups (word 32 u), a count of finished columns (word 32 * 128), then
-// one go flag per down workgroup, kGoStride words apart.
+// Hand-off words of the fused launch, each counter on its own 128-byte line:
+// per expert column u a count of its finished gate/up workgroups (word
+// 32 u), a count of finished columns (word 32 * 128), both zero between
+// calls; then per down workgroup i, kGoStride words apart, its go word
+// (+0) and its count of calls (+1).  The go word of down workgroup i holds
+// kGoTag times the number of releases it has received and its count the
+// number of calls it has run, so at the start of its call c (count c) the
+// go word is c kGoTag, or (c + 1) kGoTag once this call's release landed;
+// the release adds kGoTag.  A release left over from an earlier call whose
+// wait gave up has landed before the next launch starts (launches on one
+// workspace are serialized) and only brings the word to c kGoTag, which the
+// next call does not accept; any other value (an overwritten workspace) is
+// reported instead of trusted.
 constexpr int kColStride = 32, kTopWord = 32 * 128, kSyncWords = 32 * 129, kGoStride = 16;
+constexpr unsigned int kGoTag = 0x9E3779B1u;   // odd: c -> c kGoTag is one-to-one mod 2^32
+// Sticky status of a MoE workspace (bit 0: a down pass gave up its wait;
+// bit 1: it found its go word overwritten), at a fixed offset at the end of
+// the route header; the host reads and clears it with moe_workspace_status.
+constexpr int kMoeStatusOffset = 16384 - 64;
+constexpr unsigned int kMoeStatusTimeout = 1u, kMoeStatusCorrupt = 2u;
 #ifndef NVFP4_MOE_FUSED
 #define NVFP4_MOE_FUSED 1
 #endif
@@ -69,7 +84,7 @@ struct MoeRoute {
     int pos_pair[128];
     float pos_w[128];
 };
-static_assert(sizeof(MoeRoute) <= kMoeHeader, "route header");
+static_assert(sizeof(MoeRoute) <= kMoeStatusOffset, "route header");
 
 // The shared expert of the complete MoE layer (all pointers device memory;
 // on == 0 for the routed-only entry point).  Its gate and up outputs come
@@ -503,7 +518,9 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
         }
         __syncthreads();
         if (s_release)
-            for (int i = threadIdx.x; i < n_down; i += blockDim.x) st_dev(&done[kSyncWords + kGoStride * i], 1u);
+            for (int i = threadIdx.x; i < n_down; i += blockDim.x)
+                __hip_atomic_fetch_add(&done[kSyncWords + kGoStride * i], kGoTag, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -619,7 +636,7 @@ template <int CPL, bool FUSED>
 __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
                                                const MoeRoute *__restrict__ route, const float *__restrict__ logits,
                                                int E, int gx, const uint16_t *__restrict__ act, float *__restrict__ y,
-                                               const MoeShared &sh, unsigned int *done) {
+                                               const MoeShared &sh, unsigned int *done, unsigned int *status) {
     __shared__ int s_ex[kDownMaxExperts], s_pb[kDownMaxExperts + 1];
     __shared__ float s_dec[kDownMaxExperts], s_w[kDownMaxPos];
     __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
@@ -719,14 +736,29 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         if (b0 == 0) {
             if constexpr (FUSED) {
                 if (threadIdx.x == 0) {
+                    // this call's tag; the count of calls is advanced whether
+                    // or not the wait succeeds, so a late release of this call
+                    // cannot satisfy the next one
                     unsigned int *go = done + kSyncWords + kGoStride * bx;
-                    int it = 0;
-                    while (ld_dev(go) == 0u && it < kSpinLimit) {
-                        __builtin_amdgcn_s_sleep(2);
-                        ++it;
+                    const unsigned int c = ld_dev(go + 1);
+                    st_dev(go + 1, c + 1u);
+                    const unsigned int want = (c + 1u) * kGoTag;
+                    unsigned int g = ld_dev(go);
+                    int bad = 0;
+                    if (g != want && g != c * kGoTag) {
+                        bad = (int)kMoeStatusCorrupt;
+                    } else {
+                        int it = 0;
+                        while (g != want && it < kSpinLimit) {
+                            __builtin_amdgcn_s_sleep(2);
+                            g = ld_dev(go);
+                            ++it;
+                        }
+                        if (g != want) bad = (int)kMoeStatusTimeout;
                     }
-                    s_late = it >= kSpinLimit;
-                    st_dev(go, 0u);   // ready for the next call
+                    if (bad)
+                        __hip_atomic_fetch_or(status, (unsigned int)bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_late = bad;
                 }
                 __syncthreads();
                 if (s_late) {
@@ -793,7 +825,7 @@ __global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int 
                                                       const uint16_t *__restrict__ act, float *__restrict__ y,
                                                       MoeShared sh) {
     extern __shared__ uint4 smem[];
-    down_rows_role<CPL, false>(smem, blockIdx.x, e, m, topk, route, nullptr, 0, 0, act, y, sh, nullptr);
+    down_rows_role<CPL, false>(smem, blockIdx.x, e, m, topk, route, nullptr, 0, 0, act, y, sh, nullptr, nullptr);
 }
 
 // Gate/up and the row-owner down pass in one launch: workgroups [0, g1) are
@@ -805,14 +837,15 @@ __global__ __launch_bounds__(256) void k_moe_fused(const uint16_t *__restrict__ 
                                                   int m, int E, int topk, nvfp4_moe_weights e,
                                                   int32_t *__restrict__ ids, float *__restrict__ wts,
                                                   uint16_t *__restrict__ act, float *__restrict__ y, MoeShared sh,
-                                                  unsigned int *__restrict__ counters, int gx, int g1) {
+                                                  unsigned int *__restrict__ counters, unsigned int *status, int gx,
+                                                  int g1) {
     extern __shared__ uint4 smem[];
     const int b = blockIdx.x;
     if (b < g1)
         gate_up_role<CPLG, true>(smem, b % gx, b / gx, gx, x, logits, m, E, topk, e, ids, wts, nullptr, act, sh,
                                  counters, (int)gridDim.x - g1);
     else
-        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters);
+        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters, status);
 }
 
 template <int CPL>
@@ -880,7 +913,7 @@ constexpr int kNotResident = 1;   // launch_fused: the grid does not fit at once
 template <int CPLG, int CPLD>
 static int launch_fused_t(int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act, float *y,
-                          const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+                          const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx, int g1) {
     const void *kern = reinterpret_cast<const void *>(k_moe_fused<CPLG, CPLD>);
     const int rc = allow_lds(kern, lds, "moe_w4a16_gemv");
     if (rc) return rc;
@@ -888,27 +921,29 @@ static int launch_fused_t(int grid, size_t lds, hipStream_t s, const uint16_t *x
     // of the launch is resident at once
     if (grid > num_cus() * blocks_per_cu(kern, 256, lds)) return kNotResident;
     hipLaunchKernelGGL((k_moe_fused<CPLG, CPLD>), dim3(grid), dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, act,
-                       y, sh, counters, gx, g1);
+                       y, sh, counters, status, gx, g1);
     return check_launch("moe_w4a16_gemv");
 }
 template <int CPLG>
 static int launch_fused_g(int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m,
                           int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
-                          float *y, const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+                          float *y, const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx,
+                          int g1) {
     switch (cpld) {
-        case 1: return launch_fused_t<CPLG, 1>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
-        case 2: return launch_fused_t<CPLG, 2>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
-        default: return launch_fused_t<CPLG, 4>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        case 1: return launch_fused_t<CPLG, 1>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 2: return launch_fused_t<CPLG, 2>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        default: return launch_fused_t<CPLG, 4>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
     }
 }
 static int launch_fused(int cplg, int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits,
                         int m, int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
-                        float *y, const MoeShared &sh, unsigned int *counters, int gx, int g1) {
+                        float *y, const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx,
+                        int g1) {
     switch (cplg) {
-        case 1: return launch_fused_g<1>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
-        case 2: return launch_fused_g<2>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
-        case 4: return launch_fused_g<4>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
-        default: return launch_fused_g<0>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, gx, g1);
+        case 1: return launch_fused_g<1>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 2: return launch_fused_g<2>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 4: return launch_fused_g<4>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        default: return launch_fused_g<0>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
     }
 }
 
@@ -981,7 +1016,7 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
         const size_t lds = std::max(lds1, pos * I * 2);
         const int frc = launch_fused(cpl_for(H), cpl_for(I), ng1 + ng3, lds, s, x_bf16, router_logits, m, E, top_k,
                                      ev, topk_ids, topk_w, act, y, sh, reinterpret_cast<unsigned int *>(ws + L.sync),
-                                     gx, ng1);
+                                     reinterpret_cast<unsigned int *>(ws + kMoeStatusOffset), gx, ng1);
         if (frc != kNotResident) return frc;
     }
     int rc;
@@ -1023,6 +1058,31 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: workspace not 256-byte aligned");
     return moe_launch(x_bf16, m, router_logits, top_k, e, y, topk_ids, topk_w, reinterpret_cast<char *>(workspace), L,
                       MoeShared{}, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int moe_workspace_status(void *workspace, size_t ws_bytes, uint32_t *status, void *stream) {
+    const char *who = "moe_workspace_status";
+    if (!workspace || !status) return fail(NVFP4_ERR_ARG, "%s: NULL workspace or status", who);
+    if (ws_bytes < (size_t)kMoeHeader) return fail(NVFP4_ERR_WORKSPACE, "%s: not a MoE workspace (%zu bytes)", who, ws_bytes);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return fail(NVFP4_ERR_UNSUPPORTED, "%s: synchronizes the stream; not allowed during graph capture", who);
+    char *word = reinterpret_cast<char *>(workspace) + kMoeStatusOffset;
+    uint32_t v = 0, zero = 0;
+    hipError_t err = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err == hipSuccess && v != 0) {
+        err = hipMemcpyAsync(word, &zero, 4, hipMemcpyHostToDevice, s);
+        if (err == hipSuccess) err = hipStreamSynchronize(s);
+    }
+    if (err != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: %s", who, hipGetErrorString(err));
+    *status = v;
+    if (v & kMoeStatusCorrupt)
+        return fail(NVFP4_ERR_DEVICE, "%s: a down pass found its hand-off word overwritten (status 0x%x); zero the "
+                    "workspace before the next call", who, v);
+    if (v) return fail(NVFP4_ERR_DEVICE, "%s: a down pass gave up waiting for its gate/up pass (status 0x%x)", who, v);
+    return ok();
 }
 
 // Workspace of the complete layer: the routed MoE's, then the shared

@@ -17,6 +17,12 @@ Recipe (stated once here, used everywhere):
 * The exact-arithmetic family draws x from {-3..3}, power-of-two block scales
   in [2^-2, 2^2] and a power-of-two global scale, so that every partial sum
   of every dot product is exactly representable in fp32.
+* The scale-range family keeps x and the codes of the exact family but draws
+  the block scale bytes of a row from one E4M3 binade (8 consecutive bytes)
+  that depends on the row; over the rows the binades cover every byte
+  0x00-0x7E (zero and subnormal scales included), half the rows with the sign
+  bit set.  Within one binade the scales share one quantum, so sums stay
+  exact.
 """
 from __future__ import annotations
 
@@ -108,6 +114,78 @@ def exact_family(seed: int, m: int, n: int, k: int):
     return x, codes, scales, g_dec
 
 
+
+
+# Scale windows: the E4M3 bytes of one binade, [8 j, 8 j + 7] (byte 0x7F
+# excluded), j = (r + seed) mod 16 for row r, so 16 consecutive rows cover
+# every byte 0x00..0x7E.  The values of window j are multiples of one
+# quantum q_j (2^-9 for j <= 1, else 2^(j - 10)) and at most 15 q_j, so a
+# dot product with x in {-3..3} and any E2M1 codes has every partial sum a
+# multiple of q_j / 2 below 288 * 15 * (K / 16) * q_j: under 2^24 quanta for
+# K up to 17408, exact in fp32 in any summation order.
+def scale_window_bytes(rng: np.random.Generator, n: int, nblocks: int, seed: int = 0,
+                       signed: bool = True, binades=None) -> np.ndarray:
+    """binades: the windows j to cycle through (default all 16)."""
+    js = np.arange(16) if binades is None else np.asarray(list(binades), np.int64)
+    w0 = 8 * js[(np.arange(n, dtype=np.int64) + seed) % len(js)]
+    b = np.minimum(w0[:, None] + rng.integers(0, 8, size=(n, nblocks)), 0x7E).astype(np.uint8)
+    if signed:
+        b |= (rng.integers(0, 2, size=(n, 1)) << 7).astype(np.uint8)
+    return b
+
+
+def scale_range_family(seed: int, m: int, n: int, k: int, signed: bool = True, binades=None):
+    """The exact family with block scales over the whole E4M3 range: x in
+    {-3..3}, codes uniform over all 16, scale bytes from per-row windows (see
+    scale_window_bytes; zero, subnormal and normal scales, negative ones when
+    `signed`), g_dec a power of two.  Every dot product is exact in fp32 in
+    any summation order.  Returns (x bf16 bits [m, k], codes, scales, g_dec)."""
+    rng = np.random.default_rng([seed, 7])
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = scale_window_bytes(rng, n, k // 16, seed, signed, binades)
+    g_dec = np.float32(2.0 ** int(rng.integers(-4, 3)))
+    x = f32_to_bf16_bits(rng.integers(-3, 4, size=(m, k)).astype(np.float32))
+    return x, codes, scales, g_dec
+
+
+def scale_decode_rows(m: int, k: int, seed: int = 0):
+    """One weight row per E4M3 scale byte (0x00..0x7E, then 0x80..0xFE: 254
+    rows), every code 1.0 (E2M1 0x2), and activation rows that are one-hot
+    in every 16-element block (value +-1 or +-2 at a random position).  Output
+    (row r, activation i) = g_dec * e4m3(byte r) * sum of x[i] in closed form.
+    Returns (x bf16 bits [m, k], codes, scales, bytes [254])."""
+    rng = np.random.default_rng([seed, 8])
+    byt = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    n = byt.size
+    codes = np.full((n, k // 2), 0x22, np.uint8)
+    scales = np.repeat(byt[:, None], k // 16, axis=1)
+    xf = np.zeros((m, k), np.float32)
+    for i in range(m):
+        pos = rng.integers(0, 16, size=k // 16) + 16 * np.arange(k // 16)
+        xf[i, pos] = rng.choice(np.array([-2.0, -1.0, 1.0, 2.0], np.float32), size=k // 16)
+    return f32_to_bf16_bits(xf), codes, scales, byt
+
+
+def moe_scale_window_experts(seed: int, num_experts: int, hidden: int, inter: int):
+    """Stacked synthetic experts like moe_quantized_experts, but expert e
+    draws all its block-scale bytes from the window [8 (e % 16), 8 (e % 16) + 7]
+    (byte 0x7F excluded), so the experts together cover every scale byte,
+    zero and subnormal ones included.  Its g_dec is the power of two that puts
+    its largest weight magnitude (6 times the window's top scale) near 0.03,
+    so every expert contributes at the same magnitude."""
+    rng = np.random.default_rng([seed, 9])
+    out = []
+    w0 = 8 * (np.arange(num_experts) % 16)
+    top = np.minimum(w0 + 7, 0x7E)
+    e, mt = (top >> 3) & 15, top & 7
+    vmax = np.where(e == 0, mt * 2.0 ** -9, (1 + mt / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
+    g = (2.0 ** np.round(np.log2(0.03 / (6.0 * vmax)))).astype(np.float32)
+    for rows, cols in ((inter, hidden), (inter, hidden), (hidden, inter)):
+        c = _PAIR_LUT[rng.integers(0, 65536, size=(num_experts, rows, cols // 2), dtype=np.uint16)]
+        s = (w0[:, None, None] + rng.integers(0, 8, size=(num_experts, rows, cols // 16))).astype(np.int64)
+        s = np.minimum(s, 0x7E).astype(np.uint8)
+        out.append((c, s, g.copy()))
+    return out
 
 
 def plant_lmhead_rows(codes: np.ndarray, scales: np.ndarray, h_bf16: np.ndarray, seed: int,

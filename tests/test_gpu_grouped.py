@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 from tests.gpu_util import assert_close, bf16_round_f64, dev_bf16, dev_u8
 
 pytestmark = pytest.mark.gpu

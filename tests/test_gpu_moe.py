@@ -3,7 +3,7 @@ routing weights and outputs within |d| <= 1e-3 + 2e-3 |ref|."""
 import numpy as np
 import pytest
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_u8
 
 pytestmark = pytest.mark.gpu

@@ -6,7 +6,7 @@ import os
 import numpy as np
 import pytest
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 from tests.gpu_util import dev_bf16
 
 pytestmark = pytest.mark.gpu

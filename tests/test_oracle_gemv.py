@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
 E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
@@ -97,3 +97,55 @@ def test_dequantize_matches_library_decode(orc):
     codes, scales, glob = orc.quantize(w)
     W = np.array([[float(v) for v in row] for row in _frac_weight(codes, scales, glob[0], 16, 64)])
     assert np.array_equal(orc.dequantize(codes, scales, glob[0], 16, 64), W)
+
+
+def test_scale_range_family_is_exact(orc):
+    """The scale-range family (every E4M3 byte, zero and subnormal scales,
+    negative scales) has exact dot products: the oracle's fp32 result equals
+    the exact rational sum, and fp32 accumulation in a shuffled order of
+    block partials (the GPU's kind of order) gives the same bits."""
+    x, codes, scales, g_dec = synth.scale_range_family(12, 2, 32, 512)
+    assert sorted(set((scales & 0x7F).ravel().tolist())) == list(range(127))
+    y = orc.gemv(x, codes, scales, g_dec)
+    W = _frac_weight(codes, scales, g_dec, 32, 512)
+    xf = synth.bf16_bits_to_f32(x)
+    rng = np.random.default_rng(12)
+    for i in range(2):
+        X = [Fraction(float(v)) for v in xf[i]]
+        for r in range(32):
+            exact = sum(a * b for a, b in zip(X, W[r]))
+            assert Fraction(float(y[i, r])) == exact, (i, r)
+            terms = np.array([float(a * b) for a, b in zip(X, W[r])], np.float32)
+            blocks = [np.float32(0)] * 32
+            for b in range(32):
+                s = np.float32(0)
+                for t in terms[16 * b:16 * b + 16]:
+                    s = np.float32(s + t)
+                blocks[b] = s
+            acc = np.float32(0)
+            for b in rng.permutation(32):
+                acc = np.float32(acc + blocks[b])
+            assert acc == np.float32(y[i, r]), (i, r)
+
+
+def test_scale_range_worst_case_under_2_24_quanta():
+    """The bound behind the family's exactness at K = 17408: in every binade
+    window the largest |x * e2m1 * scale| sum over a row stays below 2^24
+    quanta of half the window's scale quantum."""
+    for j in range(16):
+        lo, hi = 8 * j, min(8 * j + 7, 0x7E)
+        vals = [float(E4M3[b]) for b in range(lo, hi + 1)]
+        quantum = 2.0 ** -9 if j <= 1 else 2.0 ** (j - 10)
+        assert all(v / quantum == round(v / quantum) for v in vals)
+        worst = 17408 * 3 * 6 * max(vals)                 # |x| <= 3, |e2m1| <= 6
+        assert worst / (quantum / 2) < 2.0 ** 24, j
+
+
+def test_decode_rows_closed_form(orc):
+    """One row per E4M3 byte with codes 1.0 and one-hot activations: the
+    oracle gives g_dec * e4m3(byte) * sum(x) (the table of torch's float8)."""
+    x, codes, scales, byt = synth.scale_decode_rows(3, 256, seed=5)
+    y = orc.gemv(x, codes, scales, np.float32(0.5))
+    xs = synth.bf16_bits_to_f32(x).astype(np.float64).sum(axis=1)
+    assert np.array_equal(y, (0.5 * xs[:, None] * E4M3[byt][None, :]).astype(np.float32))
+    assert byt.size == 254 and 0x7F not in byt and 0xFF not in byt

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 plant_rows = synth.plant_lmhead_rows
 
 E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()

@@ -14,7 +14,7 @@ import pytest
 import torch
 from scipy.special import logsumexp
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 
 E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])

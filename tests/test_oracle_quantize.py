@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from nvfp4_w4a16_mtp_amd import synth
+from tests import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_block.json")
 E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
