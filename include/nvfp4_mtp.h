@@ -212,6 +212,27 @@ int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
                        size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * lmhead_gemv_argmax_noalloc -- lmhead_gemv_argmax for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * workspace in a static array of the library, one copy of
+ * NVFP4_NOALLOC_SCRATCH_BYTES per device, held until the process ends.  The
+ * first call on a device looks the array up and clears its counters (a
+ * kernel on `stream`); every call returns them to zero.  All calls on one
+ * device share the array: calls that overlap on a device race (one at a
+ * time per device, as with one workspace).  The grid is the device's
+ * resident LM-head workgroups, each with m partials of 32 bytes; a grid
+ * whose 256 + 32 * round_up(m) * workgroups bytes exceed the array is
+ * refused with NVFP4_ERR_WORKSPACE (256 CUs need at most 131,328 bytes).
+ * Allocates nothing (no hipMalloc, no allocating library routine).
+ * Arguments, outputs and the other errors as lmhead_gemv_argmax.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (1u << 20)
+int lmhead_gemv_argmax_noalloc(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                               int32_t vocab_rows, int32_t *out_idx, float *out_max, uint32_t flags,
+                               void *stream);
+
+/*
  * lmhead_gemv_argmax_logprob -- lmhead_gemv_argmax that also returns, per
  * activation row, the top-1 log-probability of the selected token: the
  * batched argmax of [mtp_head.rs] (`MtpHead` fields) that writes each row's

@@ -14,6 +14,7 @@ Operations (same names as the C ABI):
   lmhead_gemv_argmax_logprob   ... plus the top-1 log-probability
   lmhead_gemv_argmax_masked    ... restricted to a grammar's allowed tokens
   lmhead_gemv_argmax_embed     ... with the draft tokens' embedding rows gathered
+  lmhead_gemv_argmax_noalloc   lmhead_gemv_argmax on the library's own static scratch
   embed_from_argmax            embedding rows of device-resident token ids
   moe_w4a16_gemv               top-k routed NVFP4 expert FFN
   moe_layer_w4a16              router + routed experts + gated shared expert
@@ -72,6 +73,7 @@ def lib():
         L.lmhead_gemv_argmax_workspace_bytes.argtypes = [i32, i32]
         L.lmhead_gemv_argmax_workspace_bytes.restype = sz
         L.lmhead_gemv_argmax.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P]
+        L.lmhead_gemv_argmax_noalloc.argtypes = [P, i32, WP, i32, P, P, u32, P]
         L.lmhead_gemv_argmax_logprob.argtypes = [P, i32, WP, i32, P, P, P, P, sz, u32, P]
         L.lmhead_gemv_argmax_masked.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, sz, u32, P]
         L.embed_from_argmax.argtypes = [P, i32, P, i32, i32, P, ctypes.c_int64, P, P]
@@ -86,6 +88,7 @@ def lib():
         L.moe_workspace_status.argtypes = [P, sz, ctypes.POINTER(u32), P]
         L.nvfp4_mtp_last_error.restype = ctypes.c_char_p
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
+                  "lmhead_gemv_argmax_noalloc",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
                   "moe_w4a16_gemv", "moe_layer_w4a16", "moe_workspace_status"):
             getattr(L, f).restype = ctypes.c_int
@@ -289,6 +292,26 @@ def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf1
                                     _ptr(workspace), workspace.numel(),
                                     NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
            "lmhead_gemv_argmax")
+    return out_idx, out_max
+
+
+def lmhead_gemv_argmax_noalloc(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,
+                               out_idx: torch.Tensor | None = None, out_max: torch.Tensor | None = None):
+    """lmhead_gemv_argmax with the library's static per-device scratch in
+    place of a workspace (nothing is allocated by the call itself; pass
+    out_idx / out_max to allocate nothing here either).  Calls that overlap
+    on one device race."""
+    h = _as_bf16(h)
+    _dev(h, "h")
+    m = h.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    d = w.desc()
+    _check(lib().lmhead_gemv_argmax_noalloc(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(out_idx), _ptr(out_max),
+                                            NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
+           "lmhead_gemv_argmax_noalloc")
     return out_idx, out_max
 
 

@@ -16,6 +16,8 @@
 // `argmax_grammar_masked`, independent of the order workgroups finish in.
 #include <float.h>
 
+#include <mutex>
+
 #include "gemv_core.hpp"
 
 namespace nvfp4 {
@@ -799,22 +801,39 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
 
 // Grid of the persistent LM-head kernel: every workgroup that is resident at
 // once (normally one per CU), never more than the workspace has partials for.
+// Returns NVFP4_OK or the status of a refusal (nothing launched).
 template <int MT, int CPL, bool BK, bool LP, bool MF = false>
-static void launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
-                             char *ws, int32_t *oi, float *om, float *olp, const uint32_t *mask, int mask_words,
-                             const EmbedOut &emb) {
+static int launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m, const nvfp4_weight *w, int v,
+                            char *ws, size_t wsb, int32_t *oi, float *om, float *olp, const uint32_t *mask,
+                            int mask_words, const EmbedOut &emb) {
     constexpr int NW = MF ? kLmMfWaves : lm_waves<MT, CPL>();
     auto kern = mask != nullptr ? k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW, MF, true>
                                 : k_lmhead<MT, lm_rows_per_slot<MT>(), CPL, BK, LP, NW, MF, false>;
-    if (allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax")) return;
+    const int rc = allow_lds(reinterpret_cast<const void *>(kern), lds, "lmhead_gemv_argmax");
+    if (rc) return rc;
     const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kern), 64 * NW, lds);
-    if (per_cu < 1) {
-        fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: a %d-thread workgroup does not fit on a CU", 64 * NW);
-        return;
-    }
-    const int cap = num_cus() * per_cu, nparts = (v + 15) / 16;
-    hipLaunchKernelGGL(kern, dim3(cap < nparts ? cap : nparts), dim3(64 * NW), lds, s, h, m, w->codes, w->scales,
-                       w->global, v, w->k, ws, oi, om, olp, mask, mask_words, emb, nullptr, 0);
+    if (per_cu < 1)
+        return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax: a %d-thread workgroup does not fit on a CU", 64 * NW);
+    const int cap = num_cus() * per_cu, nparts = (v + 15) / 16, grid = cap < nparts ? cap : nparts;
+    const size_t need = (size_t)kLmParts + sizeof(ArgPart) * MT * (size_t)grid;   // what this grid touches
+    if (need > wsb)
+        return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax: %d workgroups need %zu bytes of workspace, %zu available",
+                    grid, need, wsb);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, ws, oi,
+                       om, olp, mask, mask_words, emb, nullptr, 0);
+    return check_launch("lmhead_gemv_argmax");
+}
+
+// The four key / log-probability variants of one unit shape.
+template <int MT, int CPL, bool MF = false>
+static int launch_lm_variant(bool bk, bool lp, size_t lds, hipStream_t s, const uint16_t *h, int m,
+                             const nvfp4_weight *w, int v, char *ws, size_t wsb, int32_t *oi, float *om, float *olp,
+                             const uint32_t *mask, int mask_words, const EmbedOut &emb) {
+    if (bk)
+        return lp ? launch_lm_kernel<MT, CPL, true, true, MF>(lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb)
+                  : launch_lm_kernel<MT, CPL, true, false, MF>(lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb);
+    return lp ? launch_lm_kernel<MT, CPL, false, true, MF>(lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb)
+              : launch_lm_kernel<MT, CPL, false, false, MF>(lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb);
 }
 
 // Persistent streaming GEMV (the LM-head loop with plain outputs) for one
@@ -867,34 +886,21 @@ static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const n
 // The LM head keeps KS = 1 and R = 2 (8-row wavefront units); there are at
 // most ceil(V / 16) partials.  A fixed chunk count when K = 2048.
 template <int MT>
-static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, int32_t *oi, float *om,
-                           float *olp, const uint32_t *mask, int mask_words, const EmbedOut &emb, bool bk,
+static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, size_t wsb, int32_t *oi,
+                           float *om, float *olp, const uint32_t *mask, int mask_words, const EmbedOut &emb, bool bk,
                            hipStream_t s) {
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
-    ok();   // clears the message that a refused LDS request would leave
     if (lm_mf_fits(MT, w->k)) {
         if constexpr (MT >= kLmMfMinRows) {
             const size_t lmf = (size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes;
-            if (bk) lp ? launch_lm_kernel<MT, 0, true, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                       : launch_lm_kernel<MT, 0, true, false, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
-            else lp ? launch_lm_kernel<MT, 0, false, true, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                    : launch_lm_kernel<MT, 0, false, false, true>(lmf, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
+            return launch_lm_variant<MT, 0, true>(bk, lp, lmf, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb);
         }
-    } else if (tc.CPL == 4) {
-        if (bk) lp ? launch_lm_kernel<MT, 4, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                   : launch_lm_kernel<MT, 4, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
-        else lp ? launch_lm_kernel<MT, 4, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                : launch_lm_kernel<MT, 4, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
-    } else {
-        if (bk) lp ? launch_lm_kernel<MT, 0, true, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                   : launch_lm_kernel<MT, 0, true, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
-        else lp ? launch_lm_kernel<MT, 0, false, true>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb)
-                : launch_lm_kernel<MT, 0, false, false>(lds, s, h, m, w, v, ws, oi, om, olp, mask, mask_words, emb);
     }
-    if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
-    return check_launch("lmhead_gemv_argmax");
+    if (tc.CPL == 4)
+        return launch_lm_variant<MT, 4>(bk, lp, lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb);
+    return launch_lm_variant<MT, 0>(bk, lp, lds, s, h, m, w, v, ws, wsb, oi, om, olp, mask, mask_words, emb);
 }
 
 }  // namespace nvfp4
@@ -969,7 +975,7 @@ extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_ro
 static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
                          int32_t *out_idx, float *out_max, float *out_lp, const uint32_t *mask, int32_t mask_words,
                          const EmbedOut &emb, void *workspace, size_t ws_bytes, uint32_t flags, void *stream,
-                         const char *who) {
+                         const char *who, bool sized_by_grid = false) {
     int rc = validate_weight(w, who);
     if (rc) return rc;
     if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "%s: NULL h/out_idx/out_max", who);
@@ -983,18 +989,20 @@ static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *
     const int mt = round_up_mt(m);
     if ((size_t)mt * w->k * 2 > kMaxLds)
         return fail(NVFP4_ERR_UNSUPPORTED, "%s: %d (rounded-up) rows x k=%d activations exceed LDS", who, mt, w->k);
+    // the documented size covers any grid; a fixed scratch is checked
+    // against the grid actually launched
     const size_t need = lmhead_gemv_argmax_workspace_bytes(m, v);
-    if (!workspace || ws_bytes < need)
+    if (!workspace || (!sized_by_grid && ws_bytes < need))
         return fail(NVFP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes for %d rows", who, need, v);
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "%s: workspace not 256-byte aligned", who);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
     switch (mt) {
-        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
-        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
-        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
-        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
     }
 }
 
@@ -1046,4 +1054,62 @@ extern "C" int lmhead_gemv_argmax_embed(const uint16_t *h_bf16, int32_t m, const
                        out_stride / 8, table_vocab, hidden / 8};
     return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, out_logprob, allow_mask,
                          allow_mask ? mask_words : 0, emb, workspace, ws_bytes, flags, stream, who);
+}
+
+// ------------------------------------------------------- no-allocation ----
+// lmhead_gemv_argmax for callers that cannot allocate a workspace (graph
+// capture, serving loops, harnesses that forbid allocation): the same
+// kernels with their workspace in this static device array, one copy per
+// device, held until the process ends.  Its counters (ticket, per-row packed
+// maxima) are zero when the code object is loaded, cleared once more at
+// set-up, and returned to zero by every call.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+struct ScratchTable {
+    std::mutex mu;
+    char *ptr[64] = {};   // device address of `scratch` per device (null until set up)
+};
+ScratchTable &scratch_table() {
+    static ScratchTable t;
+    return t;
+}
+}  // namespace
+
+__global__ void k_scratch_clear(unsigned int *p, int words) {
+    for (int i = threadIdx.x; i < words; i += blockDim.x) p[i] = 0u;
+}
+
+// Device address of this device's scratch: looked up once per device with
+// that device current (the host-side name of the array is not a device
+// address), its counters cleared on `s` by a fill kernel.
+static int scratch_ptr(hipStream_t s, char **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "lmhead_gemv_argmax_noalloc: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax_noalloc: device %d", dev);
+    ScratchTable &t = scratch_table();
+    std::lock_guard<std::mutex> lock(t.mu);
+    if (!t.ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(NVFP4_ERR_HIP, "lmhead_gemv_argmax_noalloc: scratch address: %s", hipGetErrorString(e));
+        hipLaunchKernelGGL(k_scratch_clear, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned int *>(p), kLmParts / 4);
+        const int rc = check_launch("lmhead_gemv_argmax_noalloc(clear)");
+        if (rc) return rc;
+        t.ptr[dev] = reinterpret_cast<char *>(p);
+    }
+    *out = t.ptr[dev];
+    return NVFP4_OK;
+}
+
+extern "C" int lmhead_gemv_argmax_noalloc(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
+                                          int32_t vocab_rows, int32_t *out_idx, float *out_max, uint32_t flags,
+                                          void *stream) {
+    char *p = nullptr;
+    const int rc = scratch_ptr(reinterpret_cast<hipStream_t>(stream), &p);
+    if (rc) return rc;
+    return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, p,
+                         NVFP4_NOALLOC_SCRATCH_BYTES, flags, stream, "lmhead_gemv_argmax_noalloc", true);
 }
