@@ -27,7 +27,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+               "-fno-fast-math", "-fopenmp", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -68,6 +68,8 @@ def lib():
                                     P, P, P, P, P, P, P, P, P,
                                     P, P, f32, P, P, f32, P, P, f32, i64,
                                     P, P, P, P, P]
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_get_threads.restype = ctypes.c_int
         L.orc_moe.argtypes = [P, i64, P, i64, i64, i64, i64,
                               P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -81,6 +83,16 @@ def _p(a):
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
     return a
+
+
+def set_threads(n: int) -> None:
+    """Threads of the loops over independent outputs (results do not depend
+    on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return lib().orc_get_threads()
 
 
 # ---- codecs -----------------------------------------------------------------

@@ -22,6 +22,13 @@
  * operation (compile with -ffp-contract=off); dot products accumulate in fp64,
  * where every term x * e2m1 * e4m3 is exact.
  *
+ * Threads: the loops over independent outputs (rows of a GEMV, logits of
+ * the LM head, rows of an expert's down projection, quantized rows) are
+ * split over OpenMP threads; every output is computed by one thread in the
+ * same order as with one thread, and every scan or sum across outputs (the
+ * argmax, the log-sum-exp, the weighted expert sum) stays sequential, so
+ * the results do not depend on the thread count.  orc_set_threads sets it.
+ *
  * Parity status: every function below is pinned by tests (closed forms,
  * exhaustive codec sweeps, brute force with exact rationals, metamorphic
  * relations).  None is "parity unpinned".
@@ -31,8 +38,12 @@
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
+#include <omp.h>
 
 #define ORC_API __attribute__((visibility("default")))
+
+ORC_API void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+ORC_API int orc_get_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* bf16 <-> fp32 (a bf16 value is the upper half of an fp32 word, as the
@@ -168,6 +179,7 @@ ORC_API void orc_quantize(const uint16_t *w, int64_t n, int64_t k,
     float g[3];
     orc_global_scales(w, n * k, g);
     const float g_enc = g[1];
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
         for (int64_t b = 0; b < k / 16; ++b) {
             const uint16_t *blk = w + r * k + b * 16;
@@ -251,6 +263,8 @@ static double dot_row(const uint16_t *xrow, const uint8_t *crow, const uint8_t *
 
 ORC_API void orc_gemv(const uint16_t *x, int64_t m, const uint8_t *codes, const uint8_t *scales,
                       float g_dec, int64_t n, int64_t k, float *y) {
+    init_tabs();
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int64_t r = 0; r < n; ++r)
             y[i * n + r] = (float)((double)g_dec *
@@ -262,6 +276,8 @@ ORC_API void orc_gemv(const uint16_t *x, int64_t m, const uint8_t *codes, const 
 ORC_API void orc_gemm_sample(const uint16_t *x, const uint8_t *codes, const uint8_t *scales,
                              float g_dec, int64_t k, const int64_t *mi, const int64_t *ni,
                              int64_t count, float *out) {
+    init_tabs();
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < count; ++j)
         out[j] = (float)((double)g_dec * dot_row(x + mi[j] * k, codes + ni[j] * (k / 2),
                                                  scales + ni[j] * (k / 16), k));
@@ -281,17 +297,24 @@ ORC_API void orc_lmhead_argmax(const uint16_t *h, int64_t m, const uint8_t *code
                                uint32_t flags, int32_t *out_idx, float *out_max,
                                float *logits /* optional [m][vrows] */,
                                double *abs_bound /* optional [m][vrows]: g_dec * sum |terms| */) {
+    init_tabs();
+    float *lrow = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
     for (int64_t i = 0; i < m; ++i) {
         float best = -INFINITY, bestlogit = 0.0f;
         int32_t bi = 0;
         int have = 0;
+        /* the logits (independent), then the scan in ascending order */
+#pragma omp parallel for schedule(static)
         for (int64_t r = 0; r < vrows; ++r) {
             const uint8_t *crow = codes + r * (k / 2);
             const uint8_t *srow = scales + r * (k / 16);
             double asum = 0.0;
-            float logit = (float)((double)g_dec * dot_row2(h + i * k, crow, srow, k, &asum));
-            if (logits) logits[i * vrows + r] = logit;
+            lrow[r] = (float)((double)g_dec * dot_row2(h + i * k, crow, srow, k, &asum));
+            if (logits) logits[i * vrows + r] = lrow[r];
             if (abs_bound) abs_bound[i * vrows + r] = (double)g_dec * asum;
+        }
+        for (int64_t r = 0; r < vrows; ++r) {
+            const float logit = lrow[r];
             float key = (flags & 1u) ? orc_bf16_round(logit) : logit;
             if (key > best) { best = key; bi = (int32_t)r; bestlogit = logit; have = 1; }
         }
@@ -302,6 +325,7 @@ ORC_API void orc_lmhead_argmax(const uint16_t *h, int64_t m, const uint8_t *code
         out_idx[i] = bi;
         out_max[i] = bestlogit;
     }
+    free(lrow);
 }
 
 /* ------------------------------------------------------------------ */
@@ -317,16 +341,20 @@ ORC_API void orc_lmhead_argmax(const uint16_t *h, int64_t m, const uint8_t *code
 ORC_API void orc_lmhead_logprob(const uint16_t *h, int64_t m, const uint8_t *codes,
                                 const uint8_t *scales, float g_dec, int64_t k, int64_t vrows,
                                 uint32_t flags, double *out_lp) {
+    init_tabs();
     float *key = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
     for (int64_t i = 0; i < m; ++i) {
         float best = -INFINITY, kbest = 0.0f;
         int have = 0;
         double kmax = -INFINITY;
+#pragma omp parallel for schedule(static)
         for (int64_t r = 0; r < vrows; ++r) {
             const uint8_t *crow = codes + r * (k / 2);
             const uint8_t *srow = scales + r * (k / 16);
             const float logit = (float)((double)g_dec * dot_row(h + i * k, crow, srow, k));
             key[r] = (flags & 1u) ? orc_bf16_round(logit) : logit;
+        }
+        for (int64_t r = 0; r < vrows; ++r) {
             if (key[r] > best) { best = key[r]; kbest = key[r]; have = 1; }
             if ((double)key[r] > kmax) kmax = (double)key[r];
         }
@@ -357,10 +385,12 @@ ORC_API void orc_lmhead_masked(const uint16_t *h, int64_t m, const uint8_t *code
     float *key = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
     float *logit = (float *)malloc(sizeof(float) * (size_t)(vrows > 0 ? vrows : 1));
     char *allowed = (char *)malloc((size_t)(vrows > 0 ? vrows : 1));
+    init_tabs();
     for (int64_t i = 0; i < m; ++i) {
         float best = -INFINITY;
         int32_t bi = 0;
         double kmax = -INFINITY;
+#pragma omp parallel for schedule(static)
         for (int64_t r = 0; r < vrows; ++r) {
             const uint8_t *crow = codes + r * (k / 2);
             const uint8_t *srow = scales + r * (k / 16);
@@ -368,6 +398,8 @@ ORC_API void orc_lmhead_masked(const uint16_t *h, int64_t m, const uint8_t *code
             key[r] = (flags & 1u) ? orc_bf16_round(logit[r]) : logit[r];
             allowed[r] = mask == NULL ||
                          (r / 32 < mask_words && ((mask[i * mask_words + r / 32] >> (r % 32)) & 1u));
+        }
+        for (int64_t r = 0; r < vrows; ++r) {
             if (!allowed[r]) continue;
             if (key[r] > best) { best = key[r]; bi = (int32_t)r; }
             if ((double)key[r] > kmax) kmax = (double)key[r];
@@ -411,6 +443,7 @@ ORC_API void orc_moe(const uint16_t *x, int64_t m, const float *router, int64_t 
                      const uint8_t *uc, const uint8_t *us, const float *udec,
                      const uint8_t *dc, const uint8_t *ds, const float *ddec,
                      float *y, int32_t *ids, float *wts) {
+    init_tabs();
     float *g = (float *)malloc(sizeof(float) * I);
     float *u = (float *)malloc(sizeof(float) * I);
     uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * I);
@@ -445,11 +478,12 @@ ORC_API void orc_moe(const uint16_t *x, int64_t m, const float *router, int64_t 
                 double act = gi / (1.0 + exp(-gi)) * (double)u[i];
                 a[i] = f32_to_bf16_rne((float)act);
             }
+#pragma omp parallel for schedule(static)
             for (int64_t h = 0; h < H; ++h) {
                 float d = (float)((double)ddec[e] *
                                   dot_row(a, dc + e * H * (I / 2) + h * (I / 2),
                                           ds + e * H * (I / 16) + h * (I / 16), I));
-                acc[h] += (double)wts[t * topk + j] * (double)d;
+                acc[h] += (double)wts[t * topk + j] * (double)d;   /* slot order j per h */
             }
         }
         for (int64_t h = 0; h < H; ++h) y[t * H + h] = (float)acc[h];
@@ -498,6 +532,7 @@ ORC_API void orc_moe_layer(const uint16_t *x, int64_t m, const uint8_t *rc, cons
             double gi = g[i];
             a[i] = f32_to_bf16_rne((float)(gi / (1.0 + exp(-gi)) * (double)u[i]));
         }
+#pragma omp parallel for schedule(static)
         for (int64_t h = 0; h < H; ++h) {
             float d = (float)((double)sddec * dot_row(a, sdc + h * (Is / 2), sds + h * (Is / 16), Is));
             y[t * H + h] = (float)((double)y[t * H + h] + sg * (double)d);

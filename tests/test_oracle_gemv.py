@@ -149,3 +149,24 @@ def test_decode_rows_closed_form(orc):
     xs = synth.bf16_bits_to_f32(x).astype(np.float64).sum(axis=1)
     assert np.array_equal(y, (0.5 * xs[:, None] * E4M3[byt][None, :]).astype(np.float32))
     assert byt.size == 254 and 0x7F not in byt and 0xFF not in byt
+
+
+def test_thread_count_does_not_change_results(orc):
+    """The oracle splits independent outputs over threads; one thread and
+    every thread give the same bits (GEMV, LM-head argmax and logits, MoE,
+    quantizer)."""
+    w = synth.weight_bf16(14, 300, 512)
+    x = synth.acts_bf16(14, 3, 512)
+    ex = synth.moe_quantized_experts(14, 16, 256, 128)
+    xm = synth.acts_bf16(15, 2, 256)
+    r = synth.router_logits(15, 2, 16)
+    n0 = orc.get_threads()
+    outs = []
+    for n in (1, max(2, n0)):
+        orc.set_threads(n)
+        c, s, g = orc.quantize(w)
+        outs.append((c, s, orc.gemv(x, c, s, g[0]), *orc.lmhead_argmax(x, c, s, g[0], want_logits=True),
+                     *orc.moe(xm, r, 4, *ex)))
+    orc.set_threads(n0)
+    for a, b in zip(*outs):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
