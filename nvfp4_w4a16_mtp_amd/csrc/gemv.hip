@@ -684,6 +684,128 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     if (lane == 0) st_dev(ticket, 0u);   // ready for the next call
 }
 
+// --------------------------------------------------- MFMA units, K split ----
+// Decode GEMV for 4 to 8 activation rows on the MFMA units, for weights too
+// small for the persistent grid: one workgroup per 16-row unit, its K split
+// into slices of 1024 (8 steps of 128, one scale line), one wavefront per
+// slice.  A wavefront issues every load of its slice at once (8 code-line
+// pairs and one scale line, 9 KiB), stages them through its LDS area into
+// the MFMA layout as the LM head's units do, and runs 16
+// v_mfma_f32_16x16x32_bf16; the slices' sums are added in slice order
+// through LDS.  With the dot2 units the cost of a weight grows with the row
+// count; here it does not, and every load of the launch is in flight at once.
+constexpr int kMfSliceSteps = 8;                        // 128-k steps a wavefront
+constexpr int kMfSliceK = 128 * kMfSliceSteps;          // 1024
+constexpr int kMfMaxSlices = 8;                         // K <= 8192
+constexpr long kMfSplitMaxUnits = 1024;                 // 16-row units (4096 at four rows)
+
+template <int MT>
+__global__ __launch_bounds__(64 * kMfMaxSlices) void k_gemv_mf(const uint16_t *__restrict__ x, int m_rt,
+                                                               const GemvGroups grp, int k, int bf16out) {
+    extern __shared__ uint4 smem[];
+    const int tile = blockIdx.x;
+    const uint8_t *codes = grp.codes[0];
+    const uint8_t *scales = grp.scales[0];
+    const nvfp4_global *g = grp.g[0];
+    void *y = grp.y[0];
+    int n = grp.n[0], t0 = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i) {
+        if (i < grp.count && tile >= grp.tile0[i]) {
+            codes = grp.codes[i];
+            scales = grp.scales[i];
+            g = grp.g[i];
+            y = grp.y[i];
+            n = grp.n[i];
+            t0 = grp.tile0[i];
+        }
+    }
+    const int row0 = (tile - t0) * 16;
+    const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6, nks = blockDim.x >> 6;
+    const int li = lane & 15, q = lane >> 4;
+    const int s0 = ks * kMfSliceSteps;
+    // this wavefront's LDS: its slice of the activation image (MT rows of
+    // 128 chunks, chunk c of row m at c ^ (m % 8)), then its stage area
+    constexpr int kSliceChunks = kMfSliceK / 8;
+    uint4 *xs = smem + (size_t)ks * (MT * kSliceChunks + kMfStageBytes / 16);
+    uint4 *cst = xs + MT * kSliceChunks;                                           // code pair, 2 KiB
+    const uint16_t *sst = reinterpret_cast<const uint16_t *>(cst + 128);            // scale line, 1 KiB
+    // the slice's activations (2 MT chunks a lane), then the weights, all in
+    // flight together; the activation stores wait for the activations only
+    constexpr int XU = 2 * MT;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+    const int cpr = k >> 3;
+    uint4 xv[XU];
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+        const int p = lane + 64 * j, m = p / kSliceChunks, c = p % kSliceChunks;
+        xv[j] = m < m_rt ? xg[(size_t)m * cpr + kSliceChunks * ks + c] : make_uint4(0, 0, 0, 0);
+    }
+    const MfLines ln = mf_lines(codes, scales, n, k, row0, lane);
+    const uint4 sv = ld_stream16(ln.sp + 8 * (size_t)s0);
+    uint4 cw[kMfSliceSteps];
+#pragma unroll
+    for (int d = 0; d < kMfSliceSteps; ++d)
+        cw[d] = ld_stream16((d & 1 ? ln.cb : ln.ca) + 64 * (size_t)s0 + 128 * (d >> 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+        const int p = lane + 64 * j, m = p / kSliceChunks, c = p % kSliceChunks;
+        xs[m * kSliceChunks + (c ^ (m & 7))] = xv[j];
+    }
+    const uint4 *xa[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) xa[b] = mf_xrow(xs, kSliceChunks, MT, li, q, b);
+    const int ws0 = mf_code_wslot(lane, 0), ws1 = mf_code_wslot(lane, 1);
+    const int rs0 = mf_code_rslot(li, q, 0), rs1 = mf_code_rslot(li, q, 1);
+    cst[128 + lane] = sv;
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int d = 0; d < kMfSliceSteps; d += 2) {
+        cst[ws0] = cw[d];
+        cst[ws1] = cw[d + 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint4 a[4], bw[4];
+            mf_xload(xa, d + h, a);
+            const uint4 c = cst[h ? rs1 : rs0];
+            const uint32_t sw = sst[32 * li + 4 * (d + h) + q];
+            mf_dequant(c, sw, bw);
+            mf_mma(a, bw, acc0, acc1);
+        }
+    }
+    // the slices' sums in slice order (wavefront 0 adds them)
+    float *part = reinterpret_cast<float *>(cst);   // this wavefront's stage area, reused
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[4 * lane + r] = acc0[r] + acc1[r];
+    __syncthreads();
+    if (ks != 0) return;
+    const int row = row0 + li;
+    const float dec = g->dec;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = part[4 * lane + r];
+        for (int j = 1; j < nks; ++j)
+            v += reinterpret_cast<const float *>(smem + (size_t)j * (MT * kSliceChunks + kMfStageBytes / 16) +
+                                                 MT * kSliceChunks)[4 * lane + r];
+        const int mm = 4 * q + r;
+        if (mm < m_rt && row < n) {
+            const float o = v * dec;
+            if (bf16out)
+                reinterpret_cast<uint16_t *>(y)[(size_t)mm * n + row] = (uint16_t)f32_to_bf16_bits(o);
+            else
+                reinterpret_cast<float *>(y)[(size_t)mm * n + row] = o;
+        }
+    }
+}
+
+// The K-split MFMA GEMV serves 4 to 8 rows when K is 1024 to 8192 in whole
+// slices and the activation image and the stage areas fit the LDS.
+inline size_t gemv_mf_lds(int mt, int k) { return (size_t)(k / kMfSliceK) * ((size_t)mt * kMfSliceK * 2 + kMfStageBytes); }
+inline bool gemv_mf_fits(int mt, int k) {
+    return mt >= 4 && k % kMfSliceK == 0 && k / kMfSliceK <= kMfMaxSlices && gemv_mf_lds(mt, k) <= kMaxLds;
+}
+
 // ------------------------------------------------------------ dispatch ----
 // Instantiated tile shapes (R rows per slot, KS K-segments, CPL fixed chunks
 // per lane or 0 for the generic loop).
@@ -745,6 +867,10 @@ static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t
 #define NVFP4_GEMV_PERSIST 1
 #endif
 constexpr bool kGemvPersist = NVFP4_GEMV_PERSIST;
+#ifndef NVFP4_GEMV_MF_SPLIT
+#define NVFP4_GEMV_MF_SPLIT 1
+#endif
+constexpr bool kGemvMfSplit = NVFP4_GEMV_MF_SPLIT;
 template <int MT>
 static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16);
 
@@ -766,9 +892,47 @@ static TileChoice wide_tile(TileChoice tc, int mt, int k) {
 }
 
 template <int MT>
+static int launch_gemv_mf(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
+                          hipStream_t s) {
+    const int k = w[0]->k;
+    GemvGroups grp{};
+    grp.count = count;
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        grp.codes[i] = w[i]->codes;
+        grp.scales[i] = w[i]->scales;
+        grp.g[i] = w[i]->global;
+        grp.y[i] = y[i];
+        grp.n[i] = w[i]->n;
+        grp.tile0[i] = tiles;
+        tiles += (w[i]->n + 15) / 16;
+    }
+    for (int i = count; i <= kMaxGroups; ++i) grp.tile0[i] = tiles;
+    if (tiles == 0) return ok();
+    const int nks = k / kMfSliceK;
+    const size_t lds = gemv_mf_lds(MT, k);
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_gemv_mf<MT>), lds, "w4a16_gemv");
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_gemv_mf<MT>, dim3(tiles), dim3(64 * nks), lds, s, x, m, grp, k, bf16);
+    return check_launch("w4a16_gemv");
+}
+
+template <int MT>
 static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
                          hipStream_t s) {
     const int k = w[0]->k;
+    if constexpr (MT >= 4) {
+        // the K split keeps an activation slice per wavefront in LDS, which at
+        // eight rows leaves room for one workgroup a CU: large weights stream
+        // faster on the persistent grid (17408 x 5120 at eight rows: 29.6
+        // against 20.4 us; at four rows 18.5 against 19.1, and 2048 x 4096,
+        // 8192 x 2048 and q|k|v at eight rows 5.6, 6.8, 7.4 against 9.1, 8.0,
+        // 12.0 us on the dot2 or persistent paths)
+        long units = 0;
+        for (int i = 0; i < count; ++i) units += (w[i]->n + 15) / 16;
+        const bool small = units <= kMfSplitMaxUnits || (MT == 4 && units <= 4 * kMfSplitMaxUnits);
+        if (kGemvMfSplit && small && gemv_mf_fits(MT, k)) return launch_gemv_mf<MT>(x, m, w, y, count, bf16, s);
+    }
     if (count == 1 && kGemvPersist) {
         ok();   // clears the message that a refused LDS request would leave
         if (launch_gemv_persist<MT>(s, x, m, w[0], y[0], bf16)) return check_launch("w4a16_gemv");

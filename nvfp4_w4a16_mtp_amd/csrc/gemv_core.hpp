@@ -56,18 +56,43 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t two, float &s0, float &s1
     s1 = f.y;
 }
 
+// Copies `units` 16-byte units into LDS: unit p is src(p) (a load, or zero)
+// and lands where dst(p, value) puts it.  Each thread issues the loads of a
+// batch of kStageBatch units before it stores any of them, so a batch
+// costs one round trip to memory (a loop that stores each unit as it
+// arrives waits one round trip per unit).
+constexpr int kStageBatch = 8;
+template <class Src, class Dst>
+__device__ __forceinline__ void stage_batched(int units, int tid, int nthreads, Src &&src, Dst &&dst) {
+    for (int p0 = tid; p0 < units; p0 += kStageBatch * nthreads) {
+        uint4 v[kStageBatch];
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j) {
+            const int p = p0 + j * nthreads;
+            v[j] = p < units ? src(p) : make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j) {
+            const int p = p0 + j * nthreads;
+            if (p < units) dst(p, v[j]);
+        }
+    }
+}
+
 // LDS image of x: 16-byte units, unit (m, q, c) = x[m][32c + 8q .. 32c + 8q + 8)
 // at index (m * 4 + q) * C + c, so that the 16 lanes of a slot reading
 // consecutive chunks hit consecutive LDS addresses.  Rows m_rt .. MT-1 are
 // zero-filled (the kernel is instantiated for MT >= m_rt rows).
 __device__ __forceinline__ void stage_x(uint4 *xs, const uint4 *__restrict__ x, int m_rt, int mt, int k) {
     const int C = k >> 5, upr = k >> 3;
-    const int units = mt * upr;
-    for (int p = threadIdx.x; p < units; p += blockDim.x) {
-        int mm = p / upr, w = p - mm * upr;
-        int c = w >> 2, q = w & 3;
-        xs[(mm * 4 + q) * C + c] = mm < m_rt ? x[p] : make_uint4(0, 0, 0, 0);
-    }
+    stage_batched(
+        mt * upr, threadIdx.x, blockDim.x,
+        [&](int p) { return p / upr < m_rt ? x[p] : make_uint4(0, 0, 0, 0); },
+        [&](int p, uint4 v) {
+            const int mm = p / upr, w = p - mm * upr;
+            xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = v;
+        });
 }
 
 template <int R, int KS, int NW = 4>
@@ -413,10 +438,13 @@ __device__ __forceinline__ void gemv_tile_loop(const uint4 *xs, const uint8_t *_
 // chunk hit different bank groups.  K % 128 == 0.
 __device__ __forceinline__ void stage_x_mf(uint4 *xs, const uint4 *__restrict__ x, int m_rt, int mt, int k) {
     const int cpr = k >> 3;
-    for (int p = threadIdx.x; p < mt * cpr; p += blockDim.x) {
-        const int m = p / cpr, c = p - m * cpr;
-        xs[m * cpr + (c ^ (m & 7))] = m < m_rt ? x[p] : make_uint4(0, 0, 0, 0);
-    }
+    stage_batched(
+        mt * cpr, threadIdx.x, blockDim.x,
+        [&](int p) { return p / cpr < m_rt ? x[p] : make_uint4(0, 0, 0, 0); },
+        [&](int p, uint4 v) {
+            const int m = p / cpr, c = p - m * cpr;
+            xs[m * cpr + (c ^ (m & 7))] = v;
+        });
 }
 
 // Two E2M1 codes (byte SEL of word) times sf as two bf16 (exact: e2m1 times

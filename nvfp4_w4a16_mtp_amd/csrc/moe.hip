@@ -288,12 +288,17 @@ __device__ __forceinline__ void moe_route_lds(const float *__restrict__ logits, 
 __device__ __forceinline__ void stage_rows(uint4 *xs, const uint16_t *__restrict__ src, const int *rows, int cnt, int mt,
                                            int k) {
     const int C = k >> 5, upr = k >> 3;
-    for (int p = threadIdx.x; p < mt * upr; p += blockDim.x) {
-        int mm = p / upr, w = p - mm * upr;
-        int c = w >> 2, q = w & 3;
-        xs[(mm * 4 + q) * C + c] =
-            mm < cnt ? reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[w] : make_uint4(0, 0, 0, 0);
-    }
+    stage_batched(
+        mt * upr, threadIdx.x, blockDim.x,
+        [&](int p) {
+            const int mm = p / upr;
+            return mm < cnt ? reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[p - mm * upr]
+                            : make_uint4(0, 0, 0, 0);
+        },
+        [&](int p, uint4 v) {
+            const int mm = p / upr, w = p - mm * upr;
+            xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = v;
+        });
 }
 
 // stage_rows for rows another workgroup of the same launch wrote: 16-byte
@@ -306,16 +311,22 @@ __device__ __forceinline__ void stage_rows_dev(uint4 *xs, const uint16_t *__rest
                                                const int *rows, int cnt, int mt, int k) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, (int)(src_rows * k * 2), kBufWord3);
     const int C = k >> 5, upr = k >> 3;
-    for (int p = threadIdx.x; p < mt * upr; p += blockDim.x) {
-        int mm = p / upr, w = p - mm * upr;
-        int c = w >> 2, q = w & 3;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (mm < cnt) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (rows[mm] * k + 8 * w) * 2, 0, kCoherent);
-            v = make_uint4(t.x, t.y, t.z, t.w);
-        }
-        xs[(mm * 4 + q) * C + c] = v;
-    }
+    stage_batched(
+        mt * upr, threadIdx.x, blockDim.x,
+        [&](int p) {
+            const int mm = p / upr;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (mm < cnt) {
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (rows[mm] * k + 8 * (p - mm * upr)) * 2, 0,
+                                                                       kCoherent);
+                v = make_uint4(t.x, t.y, t.z, t.w);
+            }
+            return v;
+        },
+        [&](int p, uint4 v) {
+            const int mm = p / upr, w = p - mm * upr;
+            xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = v;
+        });
 }
 
 // gate/up body for MT >= cnt token rows.

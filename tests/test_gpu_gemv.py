@@ -148,3 +148,34 @@ def test_rows_beyond_the_lds_go_in_groups(orc, m, n, k):
     assert_close(y32, orc.gemv(x, codes, scales, glob[0]), f"m={m} k={k}")
     yb = nv.w4a16_gemv(dev_bf16(x), wd, out_dtype=torch.bfloat16).float().cpu().numpy()
     assert np.array_equal(yb, bf16_round_f64(y32).astype(np.float32))
+
+
+# Four to eight activation rows, K a whole number of 1024-wide slices (1 to
+# 8), few enough 16-row units: the K-split MFMA units (one wavefront per
+# slice, the slices' sums added in slice order), ragged row counts, both
+# families, fp32 and bf16 outputs.
+@pytest.mark.parametrize("m,n,k", [(3, 17, 1024), (4, 333, 3072), (5, 700, 5120), (8, 2050, 7168), (6, 95, 8192),
+                                   (8, 16383, 2048), (4, 40000, 1024)])
+@pytest.mark.parametrize("fam", ["exact", "scales"])
+def test_mfma_k_split_bit_exact(orc, m, n, k, fam):
+    import nvfp4_w4a16_mtp_amd as nv
+    gen = synth.exact_family if fam == "exact" else synth.scale_range_family
+    x, codes, scales, g = gen(230 + m + n, m, n, k)
+    wd = _w(codes, scales, g)
+    ref = orc.gemv(x, codes, scales, g)
+    y = nv.w4a16_gemv(dev_bf16(x), wd).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+    yb = nv.w4a16_gemv(dev_bf16(x), wd, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(yb, bf16_round_f64(ref).astype(np.float32))
+
+
+@pytest.mark.parametrize("m", [4, 7, 8])
+def test_mfma_k_split_grouped_with_empty_groups(orc, m):
+    import nvfp4_w4a16_mtp_amd as nv
+    parts = [synth.exact_family(240 + 5 * i + m, m, n, 4096) for i, n in enumerate((0, 511, 0, 33, 1))]
+    x = parts[1][0]
+    ws = [_w(c, s, g) for _, c, s, g in parts]
+    ys = nv.w4a16_gemv_grouped(dev_bf16(x), ws)
+    for (_, c, s, g), y in zip(parts, ys):
+        if c.shape[0]:
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.gemv(x, c, s, g).view(np.uint32))
