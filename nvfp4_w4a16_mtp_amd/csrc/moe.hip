@@ -115,7 +115,7 @@ struct RouteLds {
     unsigned char jof[kMoeMaxExperts][8];        // slot at which token t chose e
     int sel_i[8][kMoeMaxTopK];
     float sel_w[8][kMoeMaxTopK];
-    int wsum[4];
+    int wsum[16];
     int n_distinct;
     MoeExpert ex[128];
 };
@@ -224,8 +224,8 @@ __device__ __forceinline__ void moe_route_per(const float *__restrict__ logits, 
     }
     for (int e = threadIdx.x; e < E; e += blockDim.x) L.tokmask[e] = 0;
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < m; t += 4) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int t = wave; t < m; t += nw) {
         float my_v;
         int my_i;
         route_token<PER>(logits + (size_t)t * E, E, topk, lane, my_v, my_i);
@@ -241,20 +241,22 @@ __device__ __forceinline__ void moe_route_per(const float *__restrict__ logits, 
     }
     __syncthreads();
     // compact the experts with a nonzero token mask, ascending id: thread q
-    // looks at experts q, q + 256, ...; a ballot and the lane's count of
-    // lower set lanes place each one
+    // looks at experts q, q + blockDim.x, ...; a ballot and the lane's count
+    // of lower set lanes place each one
     int base = 0;
-    for (int e0 = 0; e0 < E; e0 += 256) {
+    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
         const int e = e0 + (int)threadIdx.x;
         const int mask = e < E ? L.tokmask[e] : 0;
         const uint64_t ball = __ballot(mask != 0);
         const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0));
         if (lane == 0) L.wsum[wave] = __popcll(ball);
         __syncthreads();
-        int pos = base;
-        for (int w = 0; w < wave; ++w) pos += L.wsum[w];
+        int pos = base, total = 0;
+        for (int w = 0; w < nw; ++w) {
+            pos += w < wave ? L.wsum[w] : 0;
+            total += L.wsum[w];
+        }
         pos += below;
-        const int total = L.wsum[0] + L.wsum[1] + L.wsum[2] + L.wsum[3];
         if (mask) {
             MoeExpert &me = L.ex[pos];
             me.expert = e;
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict_
 }
 
 // The routing alone (one workgroup), for the planned gate/up launch.
-__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int m, int E, int topk,
+__global__ __launch_bounds__(512) void k_moe_route(const float *__restrict__ logits, int m, int E, int topk,
                                                   nvfp4_moe_weights e, int32_t *__restrict__ ids,
                                                   float *__restrict__ wts, MoeRoute *__restrict__ route) {
     __shared__ RouteLds L;
@@ -643,7 +645,7 @@ constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the
 // the routed experts has finished) and reads the activations with
 // device-coherent loads.  The wait is bounded: past kSpinLimit polls the
 // workgroup writes NaN rows instead of waiting for ever.
-template <int CPL, bool FUSED>
+template <int CPL, bool FUSED, int NW = 4>
 __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
                                                const MoeRoute *__restrict__ route, const float *__restrict__ logits,
                                                int E, int gx, const uint16_t *__restrict__ act, float *__restrict__ y,
@@ -721,7 +723,8 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     const int r0 = bx * kDownRows;
     const int nitems = nd * kDownRows;
     const size_t wsz = (size_t)H * I;
-    for (int b0 = 0; b0 < nitems; b0 += 16 * kDownBatch) {
+    constexpr int kSlots = 4 * NW;
+    for (int b0 = 0; b0 < nitems; b0 += kSlots * kDownBatch) {
         // weight loads of this batch first, then (first batch only) the
         // activation image, so that both are in flight together
         uint4 cw[kDownBatch][CPL];
@@ -730,7 +733,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         for (int n = 0; n < kDownBatch; ++n) {
             // items past the end load a valid row (the last one); their
             // results are never used
-            const int it = min(b0 + sl + 16 * n, nitems - 1);
+            const int it = min(b0 + sl + kSlots * n, nitems - 1);
             const int u = it / kDownRows, row = min(r0 + it % kDownRows, H - 1);
             const bool shared_row = s_ex[u] < 0;
             const uint8_t *dc = (shared_row ? sh.dcodes : e.down_codes + (size_t)s_ex[u] * (wsz / 2)) + (size_t)row * (I / 2);
@@ -790,7 +793,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         }
 #pragma unroll
         for (int n = 0; n < kDownBatch; ++n) {
-            const int it = b0 + sl + 16 * n;
+            const int it = b0 + sl + kSlots * n;
             if (it >= nitems) continue;   // uniform over the slot
             const int u = it / kDownRows, r = it % kDownRows;
             for (int pos = s_pb[u]; pos < s_pb[u + 1]; ++pos) {
@@ -830,13 +833,20 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     }
 }
 
+// The separate row-owner down pass: 16 wavefronts (64 slots) per
+// workgroup, so that a CU keeps 64 items (expert, row) of weights in flight
+// (8 wavefronts for four chunks a lane, whose registers would not fit 16).
 template <int CPL>
-__global__ __launch_bounds__(256) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
-                                                      const float *__restrict__ wts, const MoeRoute *__restrict__ route,
-                                                      const uint16_t *__restrict__ act, float *__restrict__ y,
-                                                      MoeShared sh) {
+constexpr int down_rows_waves() { return CPL >= 4 ? 8 : 16; }
+template <int CPL>
+__global__ __launch_bounds__(64 * down_rows_waves<CPL>()) void k_moe_down_rows(nvfp4_moe_weights e, int m, int topk,
+                                                                      const float *__restrict__ wts,
+                                                                      const MoeRoute *__restrict__ route,
+                                                                      const uint16_t *__restrict__ act,
+                                                                      float *__restrict__ y, MoeShared sh) {
     extern __shared__ uint4 smem[];
-    down_rows_role<CPL, false>(smem, blockIdx.x, e, m, topk, route, nullptr, 0, 0, act, y, sh, nullptr, nullptr);
+    down_rows_role<CPL, false, down_rows_waves<CPL>()>(smem, blockIdx.x, e, m, topk, route, nullptr, 0, 0, act, y, sh,
+                                                       nullptr, nullptr);
 }
 
 // Gate/up and the row-owner down pass in one launch: workgroups [0, g1) are
@@ -865,7 +875,8 @@ static int launch_down_rows(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_w
                             const MoeShared &sh) {
     const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_down_rows<CPL>), lds, "moe_w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL(k_moe_down_rows<CPL>, g, dim3(256), lds, s, e, m, topk, wts, route, act, y, sh);
+    hipLaunchKernelGGL(k_moe_down_rows<CPL>, g, dim3(64 * down_rows_waves<CPL>()), lds, s, e, m, topk, wts, route, act,
+                       y, sh);
     return check_launch("moe_w4a16_gemv(down)");
 }
 
@@ -895,7 +906,8 @@ static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, 
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
                           uint16_t *act, const MoeShared &sh) {
     if (m >= kMoePlanMinTokens) {
-        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), 0, s, logits, m, E, topk, e, ids, wts, route);
+        // one wavefront a token
+        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(64 * round_up_mt(m)), 0, s, logits, m, E, topk, e, ids, wts, route);
         const int rc0 = check_launch("moe_w4a16_gemv(route)");
         if (rc0) return rc0;
         const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, true>), lds, "moe_w4a16_gemv");
@@ -1015,13 +1027,12 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kDownTile - 1) / kDownTile, maxd);
     const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
     const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
-    // the row-owner pass keeps about 8 KiB of static LDS next to the activation rows.
-    // Without a shared expert it serves one token only: at 2 and 3 tokens
-    // (16 and 23 experts) the ticket pass took 22.3 and 30.6 us against 23.4
-    // and 34.2, and the one-launch path needs the row-owner pass only at one.
-    const size_t lds_limit = sh.on ? (size_t)160 * 1024 - 10240 : m == 1 ? (size_t)kLdsBytes - 16384 : 0;
+    // the row-owner pass keeps about 8 KiB of static LDS next to the
+    // activation rows of every pair; with 16 wavefronts a workgroup it beats
+    // the ticket pass at every token count (at 8 tokens 20.8 against 24.4 us)
+    const size_t lds_limit = (size_t)160 * 1024 - 10240;
     const bool row_owner = pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0;
-    if (row_owner && kMoeFused) {
+    if (row_owner && kMoeFused && m == 1) {
         // one launch: gate/up workgroups, then the row-owner down workgroups
         const int gx = (int)g1.x, ng1 = gx * maxd, ng3 = (H + kDownRows - 1) / kDownRows;
         const size_t lds = std::max(lds1, pos * I * 2);
