@@ -221,22 +221,13 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ p
 // 2 x 256 / 919 over 3 x 128 / 815.  A partly filled last round costs a
 // full one, so e.g. 1024 x 17408 (544 tall tiles, 2 rounds) keeps the
 // 128-row tile (1088 tiles, 2 rounds).
-#ifndef NVFP4_GEMM_TALL_ROUND
-#define NVFP4_GEMM_TALL_ROUND 1.18
-#endif
-constexpr double kTallRound = NVFP4_GEMM_TALL_ROUND;
-#ifndef NVFP4_GEMM_MAX_SPLIT
-#define NVFP4_GEMM_MAX_SPLIT 16
-#endif
-#ifndef NVFP4_GEMM_MIN_SLICE_STEPS
-#define NVFP4_GEMM_MIN_SLICE_STEPS 8
-#endif
-constexpr int kMaxSplit = NVFP4_GEMM_MAX_SPLIT;             // K slices at most
+constexpr double kTallRound = 1.18;
+constexpr int kMaxSplit = 16;             // K slices at most
 // 64-k steps per slice at least: at 128 x 2048 x 4096 slices of 8 steps
 // (8 slices) took 18.8-19.6 us against 21.4-22.3 for 16 slices of 4; the
 // other 128- and 1024-row shapes were within noise; at most 4 or 8 slices
 // instead of 16 made 128 x 5120 x 17408 slower (79, 60 against 52 us).
-constexpr int kMinSliceSteps = NVFP4_GEMM_MIN_SLICE_STEPS;
+constexpr int kMinSliceSteps = 8;
 
 struct GemmPlan {
     int bm;       // 128 or 256

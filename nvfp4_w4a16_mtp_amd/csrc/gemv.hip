@@ -37,12 +37,10 @@ struct GemvGroups {
     int count;
 };
 
-#ifndef NVFP4_GEMV_PIPE
-#define NVFP4_GEMV_PIPE 4
-#endif
 // Chunks per lane per pipelined stage of the generic loop (R rows share it).
+constexpr int kGemvPipe = 4;
 template <int R>
-constexpr int gemv_pipe() { return R >= NVFP4_GEMV_PIPE ? 1 : NVFP4_GEMV_PIPE / R; }
+constexpr int gemv_pipe() { return R >= kGemvPipe ? 1 : kGemvPipe / R; }
 
 template <int MT, int R, int KS, int CPL, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
@@ -198,42 +196,23 @@ struct EmbedOut {
 // Wavefronts per LM-head workgroup: one workgroup per CU holding as many
 // wavefronts as the kernel's registers leave resident (3 per SIMD up to 170
 // VGPRs, 4 up to 128 for the one-row generic loop, 2 up to 256, 1 beyond).
-#ifndef NVFP4_LM_NW1
-#define NVFP4_LM_NW1 8
-#endif
-#ifndef NVFP4_LM_NW1G
-#define NVFP4_LM_NW1G 16
-#endif
 template <int MT, int CPL>
 constexpr int lm_waves() {
-    return MT == 1 && CPL == 0 ? NVFP4_LM_NW1G : MT == 1 ? NVFP4_LM_NW1 : MT <= 2 ? 12 : MT == 4 ? 8 : 4;
+    return MT == 1 && CPL == 0 ? 16 : MT == 1 ? 8 : MT <= 2 ? 12 : MT == 4 ? 8 : 4;
 }
 
 // Rows per slot of an LM-head unit: one activation row takes 4-row units
 // (short units keep the wavefronts' end times close together); more rows
 // take 8-row units, whose activation reads from LDS serve two rows.
-#ifndef NVFP4_LM_R1
-#define NVFP4_LM_R1 1
-#endif
 template <int MT>
 constexpr int lm_rows_per_slot() {
-    return MT == 1 && NVFP4_LM_R1 ? 1 : 2;
+    return MT == 1 ? 1 : 2;
 }
 
 // Wavefronts per workgroup of the MFMA units (M >= 2, K % 128 == 0), and
 // whether those units are used.
-#ifndef NVFP4_LM_MF_WAVES
-#define NVFP4_LM_MF_WAVES 8
-#endif
-#ifndef NVFP4_LM_MFMA
-#define NVFP4_LM_MFMA 1
-#endif
-constexpr int kLmMfWaves = NVFP4_LM_MF_WAVES;
-#ifndef NVFP4_LM_MF_DEPTH
-#define NVFP4_LM_MF_DEPTH 8
-#endif
-constexpr int kLmMfDepth = NVFP4_LM_MF_DEPTH;   // 128-k steps of code loads in flight per lane
-constexpr bool kLmMfma = NVFP4_LM_MFMA;
+constexpr int kLmMfWaves = 8;
+constexpr int kLmMfDepth = 8;   // 128-k steps of code loads in flight per lane
 constexpr int kMfStageBytes = 3072;   // per wavefront: one code pair (2 KiB) and one scale round (1 KiB)
 
 // Fewest activation rows served by the MFMA units.  Their cost per unit does
@@ -241,16 +220,13 @@ constexpr int kMfStageBytes = 3072;   // per wavefront: one code pair (2 KiB) an
 // dequantized weight that the dot2 units fold into one per 16), while the
 // dot2 units' grows with M: at K = 2048 the LM head with MFMA units measures
 // 45-47 us at M = 4..8, with dot2 units 37.5, 55 and 103 us at M = 2, 4, 8.
-#ifndef NVFP4_LM_MF_MIN_ROWS
-#define NVFP4_LM_MF_MIN_ROWS 4
-#endif
-constexpr int kLmMfMinRows = NVFP4_LM_MF_MIN_ROWS;
+constexpr int kLmMfMinRows = 4;
 
 // The MFMA units serve MT >= kLmMfMinRows rows when K is a whole number of
 // load rounds and the activation image plus the staging areas fit the LDS
 // (MT = 8: K <= 8192; larger K takes the dot2 units).
 inline bool lm_mf_fits(int mt, int k) {
-    return mt >= kLmMfMinRows && kLmMfma && k % (128 * kLmMfDepth) == 0 &&
+    return mt >= kLmMfMinRows && k % (128 * kLmMfDepth) == 0 &&
            (size_t)mt * k * 2 + (size_t)kLmMfWaves * kMfStageBytes <= kMaxLds;
 }
 
@@ -851,26 +827,14 @@ static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t
 // sweep of 2, 4, 6, 8 and 12 put the q|k|v grouped GEMV at 5.8, 5.3, 4.9,
 // 4.9 and 4.9 us: one tile per workgroup, so more of them keep more loads
 // in flight while the launch ramps up).
-#ifndef NVFP4_GEMV_TPC
-#define NVFP4_GEMV_TPC 6
-#endif
+constexpr int kGemvTilesPerCu = 6;
 // From four activation rows on, 2 per CU: each tile then has more rows and
 // its lanes more arithmetic between loads (q|k|v grouped at M = 4 in 6.9 us
 // against 8.3 at 6 per CU; the single q, fc and 4096 x 2048 GEMVs equal or
 // faster).
-#ifndef NVFP4_GEMV_TPC_M4
-#define NVFP4_GEMV_TPC_M4 2
-#endif
+constexpr int kGemvTilesPerCuM4 = 2;
 // One launch over `count` weights with a common K (their tiles concatenated);
 // the tile shape is chosen for the total row count.
-#ifndef NVFP4_GEMV_PERSIST
-#define NVFP4_GEMV_PERSIST 1
-#endif
-constexpr bool kGemvPersist = NVFP4_GEMV_PERSIST;
-#ifndef NVFP4_GEMV_MF_SPLIT
-#define NVFP4_GEMV_MF_SPLIT 1
-#endif
-constexpr bool kGemvMfSplit = NVFP4_GEMV_MF_SPLIT;
 template <int MT>
 static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16);
 
@@ -879,11 +843,8 @@ static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const n
 // too few to keep the weight loads in flight: then wide workgroups of
 // 16 rows whose K is split over 2 (two workgroups fit) or 4 (one fits)
 // wavefront groups.
-#ifndef NVFP4_GEMV_WIDE
-#define NVFP4_GEMV_WIDE 1
-#endif
 static TileChoice wide_tile(TileChoice tc, int mt, int k) {
-    if (!NVFP4_GEMV_WIDE || tc.KS != 1 || tc.CPL != 0) return tc;
+    if (tc.KS != 1 || tc.CPL != 0) return tc;
     const size_t image = (size_t)mt * k * 2, cu_lds = 160 * 1024;
     if (4 * image < cu_lds) return tc;
     const TileChoice w4{1, 4, 0, 16}, w2{1, 2, 0, 8};
@@ -931,16 +892,16 @@ static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w,
         long units = 0;
         for (int i = 0; i < count; ++i) units += (w[i]->n + 15) / 16;
         const bool small = units <= kMfSplitMaxUnits || (MT == 4 && units <= 4 * kMfSplitMaxUnits);
-        if (kGemvMfSplit && small && gemv_mf_fits(MT, k)) return launch_gemv_mf<MT>(x, m, w, y, count, bf16, s);
+        if (small && gemv_mf_fits(MT, k)) return launch_gemv_mf<MT>(x, m, w, y, count, bf16, s);
     }
-    if (count == 1 && kGemvPersist) {
+    if (count == 1) {
         ok();   // clears the message that a refused LDS request would leave
         if (launch_gemv_persist<MT>(s, x, m, w[0], y[0], bf16)) return check_launch("w4a16_gemv");
         if (nvfp4_mtp_last_error()[0]) return NVFP4_ERR_UNSUPPORTED;   // allow_lds refused
     }
     int total_n = 0;
     for (int i = 0; i < count; ++i) total_n += w[i]->n;
-    const int tpc = MT >= 4 ? NVFP4_GEMV_TPC_M4 : NVFP4_GEMV_TPC;
+    const int tpc = MT >= 4 ? kGemvTilesPerCuM4 : kGemvTilesPerCu;
     const TileChoice tc = canonical(wide_tile(choose_tile(total_n, k, MT, tpc * num_cus(), 0), MT, k));
     const int rows = 4 * (tc.NW / tc.KS) * tc.R;
     GemvGroups grp{};
@@ -1007,10 +968,7 @@ static int launch_lm_variant(bool bk, bool lp, size_t lds, hipStream_t s, const 
 // as every fourth wavefront gets a unit (at 151936 x 2048: 35.8 and 37.9 us
 // at M = 4 and 8, against 50.5 and 127 us on the per-tile grid).  Returns
 // false (nothing launched) when the persistent grid is not used.
-#ifndef NVFP4_GEMV_PERSIST_UNITS
-#define NVFP4_GEMV_PERSIST_UNITS 2
-#endif
-constexpr int kPersistUnits = NVFP4_GEMV_PERSIST_UNITS;
+constexpr int kPersistUnits = 2;
 
 template <int MT, int CPL, bool MF>
 static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y,

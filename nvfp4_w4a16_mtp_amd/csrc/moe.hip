@@ -2,23 +2,27 @@
 // `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain that new.rs
 // (`MtpHead::new`) names for the head's MoE, with the NVFP4 expert
 // gate/up [inter][hidden] and down [hidden][inter] matrices it quantizes.
+// The routing is decided on the device (no host round trip): top-k by
+// logit with the lower id first on ties, softmax over the selected logits,
+// the distinct experts in ascending id with their tokens and (token, slot)
+// pairs.  Each selected expert's weights are streamed once per call however
+// many tokens chose it.
 //
-// Two launches, sized for the worst case, with the routing decided on the
-// device (no host round trip):
-//  1. gate_up (row tiles x distinct experts): every workgroup first computes
-//             the routing in LDS -- top-k by logit with the lower id first on
-//             ties (one wavefront per token, DPP argmax over register-held
-//             logits), softmax over the selected logits, the distinct experts
-//             in ascending id with their tokens and (token, slot) pairs --
-//             then runs the gate and up GEMVs over
-//             exactly the tokens that chose the expert -- its weights are
-//             streamed once however many tokens use it -- then
-//             a = bf16(silu(g) * u) for each (token, slot) pair;
-//  2. down    (row tiles x distinct experts): d = down(a) for the same
-//             pairs; the last expert to finish a 16-row tile (a ticket per
-//             tile, returned to zero afterwards) writes y[t] = sum_j w[t][j] *
-//             d[t][j] in slot order for those rows -- deterministic, no
-//             floating-point atomics.
+// Launch structure:
+//  * one token, when the whole grid is resident: one launch (k_moe_fused).
+//    The gate/up workgroups route for themselves, run 16 rows of gate and up
+//    for the tokens that chose their expert and store a = bf16(silu(g) * u);
+//    the down workgroups, after them in dispatch order, route for
+//    themselves, prefetch their weights and wait for a per-call tagged go
+//    word before reading the activations;
+//  * otherwise: routing (in every gate/up workgroup, or from three tokens on
+//    once, in its own one-workgroup launch), gate/up, then the down pass:
+//    the row-owner pass (k_moe_down_rows: a workgroup owns 8 output rows of
+//    every routed expert, all pairs' activations in LDS, y summed per token
+//    in ascending expert order) when the activations fit in LDS, else the
+//    ticket pass (k_moe_down: 64-row tiles per expert, d per pair to the
+//    workspace, the last expert of a tile sums y in slot order).
+// No floating-point atomics: y is deterministic for given inputs.
 #include <algorithm>
 
 #include "gemv_core.hpp"
@@ -28,10 +32,7 @@ namespace nvfp4 {
 constexpr int kMoeMaxTopK = 16;
 constexpr int kMoeMaxExperts = 1024;
 constexpr int kMoeHeader = 16384;   // route header bytes at the start of the workspace
-#ifndef NVFP4_PAIR_U
-#define NVFP4_PAIR_U 1
-#endif
-constexpr int kPairU = NVFP4_PAIR_U;   // chunks per pipeline stage of the gate|up row pair
+constexpr int kPairU = 1;   // chunks per pipeline stage of the gate|up row pair
 constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
 constexpr int kSpinLimit = 1 << 22;    // polls of the fused down pass's wait (seconds)
 // Hand-off words of the fused launch, each counter on its own 128-byte line:
@@ -54,10 +55,6 @@ constexpr unsigned int kGoTag = 0x9E3779B1u;   // odd: c -> c kGoTag is one-to-o
 // the route header; the host reads and clears it with moe_workspace_status.
 constexpr int kMoeStatusOffset = 16384 - 64;
 constexpr unsigned int kMoeStatusTimeout = 1u, kMoeStatusCorrupt = 2u;
-#ifndef NVFP4_MOE_FUSED
-#define NVFP4_MOE_FUSED 1
-#endif
-constexpr bool kMoeFused = NVFP4_MOE_FUSED;
 constexpr size_t kMoeMaxLds = 160 * 1024 - 4096;   // dynamic LDS of one workgroup, static LDS aside
 
 // One distinct expert of a call: the tokens that chose it (ascending) and,
@@ -894,12 +891,9 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
     return L;
 }
 
-#ifndef NVFP4_MOE_PLAN_MIN_TOKENS
-#define NVFP4_MOE_PLAN_MIN_TOKENS 3
-#endif
 // Fewest tokens for which the two-launch path routes once, in its own
 // kernel, instead of in every gate/up workgroup.
-constexpr int kMoePlanMinTokens = NVFP4_MOE_PLAN_MIN_TOKENS;
+constexpr int kMoePlanMinTokens = 3;
 
 template <int CPL>
 static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
@@ -1032,7 +1026,7 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     // the ticket pass at every token count (at 8 tokens 20.8 against 24.4 us)
     const size_t lds_limit = (size_t)160 * 1024 - 10240;
     const bool row_owner = pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0;
-    if (row_owner && kMoeFused && m == 1) {
+    if (row_owner && m == 1) {
         // one launch: gate/up workgroups, then the row-owner down workgroups
         const int gx = (int)g1.x, ng1 = gx * maxd, ng3 = (H + kDownRows - 1) / kDownRows;
         const size_t lds = std::max(lds1, pos * I * 2);

@@ -30,10 +30,7 @@ __global__ void k_quant_clear(nvfp4_global *g) {
     }
 }
 
-#ifndef NVFP4_ABSMAX_LOADS
-#define NVFP4_ABSMAX_LOADS 4
-#endif
-constexpr int kAbsmaxLoads = NVFP4_ABSMAX_LOADS;
+constexpr int kAbsmaxLoads = 4;
 
 __global__ __launch_bounds__(256) void k_quant_absmax(const uint4 *__restrict__ w, int64_t nvec,
                                                      nvfp4_global *g) {
@@ -185,10 +182,7 @@ __global__ __launch_bounds__(256) void k_quant_encode(const uint4 *__restrict__ 
     }
 }
 
-#ifndef NVFP4_ABSMAX_PER_CU
-#define NVFP4_ABSMAX_PER_CU 4
-#endif
-constexpr int kAbsmaxPerCu = NVFP4_ABSMAX_PER_CU;
+constexpr int kAbsmaxPerCu = 4;
 
 static int grid_for(int64_t items, int per_cu) {
     int64_t blocks = (items + 255) / 256;

@@ -77,3 +77,65 @@ def test_moe(orc, m, topk):
     assert np.array_equal(ids.cpu().numpy(), rids)
     assert_close(wts.cpu().numpy(), rw, "weights")
     assert_close(y.cpu().numpy(), ry, f"moe m={m}")
+
+
+def _routed_union(r, topk):
+    """Experts in some token's top-k (ascending): restricted to them, every
+    token keeps its own top-k, in the same order (random logits, no ties)."""
+    return np.unique(np.argsort(-r, axis=1, kind="stable")[:, :topk])
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_moe_256_experts_full_width(orc, m):
+    """All 256 experts of 2048 x 7168 / 7168 x 2048 on the device (the
+    benchmarked stack, 6.3 GB of NVFP4): the experts some token routes to
+    hold synthetic weights, the others zeros (a kernel that read one would
+    change the result).  The oracle runs on the routed experts with the
+    router logits restricted to them; its ids map back through the
+    ascending expert list.  256 experts give each routing lane four."""
+    import nvfp4_w4a16_mtp_amd as nv
+    E = 256
+    x = synth.acts_bf16(150 + m, m, H)
+    r = synth.router_logits(151 + m, m, E)
+    sel = _routed_union(r, 8)
+    rng = np.random.default_rng([152, m])
+    parts = []
+    for rows, cols in ((I, H), (I, H), (H, I)):
+        codes = torch.zeros((E, rows, cols // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.zeros((E, rows, cols // 16), dtype=torch.uint8, device="cuda")
+        glob = torch.zeros((E, 4), dtype=torch.float32, device="cuda")
+        cs, ss, gs = [], [], []
+        for e in sel:
+            c, s, g = synth.quantized_domain_weight(rng, rows, cols)
+            codes[int(e)] = dev_u8(c)
+            scales[int(e)] = dev_u8(s)
+            glob[int(e), 0] = float(g)
+            cs.append(c)
+            ss.append(s)
+            gs.append(g)
+        parts.append((codes, scales, glob))
+        parts.append((np.stack(cs), np.stack(ss), np.array(gs, np.float32)))
+    dex = nv.NVFP4Experts(*parts[0], *parts[2], *parts[4])
+    y, ids, wts = nv.moe_w4a16_gemv(dev_bf16(x), dev_f32(r), 8, dex)
+    ry, rids, rw = orc.moe(x, np.ascontiguousarray(r[:, sel]), 8, parts[1], parts[3], parts[5])
+    assert np.array_equal(ids.cpu().numpy(), sel[rids])
+    assert_close(wts.cpu().numpy(), rw, "weights")
+    assert_close(y.cpu().numpy(), ry, f"moe 256 experts m={m}")
+
+
+@pytest.mark.parametrize("m", [4, 8])
+def test_lmhead_full_vocabulary_rows(orc, m):
+    """All 129280 rows at m = 4 (dot2 units) and 8 (MFMA units: K = 7168 is
+    a whole number of 1024-wide load rounds) with planted winners and
+    duplicates below them; the maximum logit within tolerance."""
+    import nvfp4_w4a16_mtp_amd as nv
+    codes, scales, g = synth.quantized_domain_weight(np.random.default_rng([160, m]), V, H)
+    h = synth.acts_bf16(161 + m, m, H)
+    info = synth.plant_lmhead_rows(codes, scales, h, seed=162 + m, n_near=4, dup=True)
+    idx, mx = nv.lmhead_gemv_argmax(dev_bf16(h), _w(codes, scales, g))
+    idx = idx.cpu().numpy()
+    for i in range(m):
+        assert idx[i] == min([info["star"][i]] + info["dups"][i])
+    ridx, rmx = orc.lmhead_argmax(h, codes, scales, g)
+    assert np.array_equal(idx, ridx)
+    assert_close(mx.cpu().numpy(), rmx, "max logit")
