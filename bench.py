@@ -52,7 +52,6 @@ NCOPIES = 5                 # weight copies of the whole step (1.1 GB each)
 ROT_BYTES = 1 << 30         # distinct weight bytes a timed row rotates through (4x the Infinity Cache)
 MIN_LAUNCHES = 30           # launches per timed graph at least
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "decode_kernels_counters.md")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lmhead_v151936_m1_traffic.md")
 SOURCES = ("gemv.hip", "gemv_core.hpp", "common.hpp", "moe.hip", "quantize.hip")
 
 
@@ -479,30 +478,31 @@ def _profile_fields(path):
     return fields
 
 
-def lmhead_traffic():
-    """HBM bytes per LM-head launch (M = 1) from the committed FETCH_SIZE /
-    WRITE_SIZE passes, or None when the kernel sources changed since."""
-    f = _profile_fields(TRAFFIC_PROFILE)
-    h = hashlib.sha256()
-    for name in ("gemv.hip", "gemv_core.hpp", "common.hpp"):
-        with open(os.path.join(ROOT, "nvfp4_w4a16_mtp_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
-    if f.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in f:
-        return None
-    return int(f["traffic_bytes_per_launch"])
+def counter_table():
+    """The committed per-row counter figures, or {} when the kernel sources
+    changed since the counter passes were taken."""
+    f = _profile_fields(COUNTER_PROFILE)
+    if f.get("source_sha256") != sources_sha256():
+        return {}
+    return json.loads(f.get("rows_json", "{}"))
+
+
+def lmhead_traffic(lm_bytes):
+    """HBM bytes per LM-head launch (M = 1): the counter passes' FETCH_SIZE +
+    WRITE_SIZE ratio to the algorithmic bytes, or None."""
+    ratio = counter_table().get(f"lmhead_v{VOCAB}", {}).get("traffic_ratio")
+    return round(ratio * lm_bytes) if ratio else None
 
 
 def attach_counters(rows):
-    """Adds each row's counter figures (traffic ratio, VALUBusy, effective
-    clock) from the committed summary, if the kernel sources still match."""
-    f = _profile_fields(COUNTER_PROFILE)
-    if f.get("source_sha256") != sources_sha256():
-        return False
-    table = json.loads(f.get("rows_json", "{}"))
+    """Adds each row's counter figures (traffic ratio, VALUBusy, median
+    launch time, clock) from the committed summary, if the kernel sources
+    still match."""
+    table = counter_table()
     for name, vals in table.items():
         if name in rows:
             rows[name]["counters"] = vals
-    return True
+    return bool(table)
 
 
 def _csv_records(d):
@@ -532,8 +532,8 @@ def copy_calibration(fetch_dir, write_dir):
 
 def summarize_counters(dirs, copy_dirs):
     """Markdown table of the --counters passes (rocprofv3 output dirs: any of
-    FETCH_SIZE, WRITE_SIZE, VALUBusy + GRBM_GUI_ACTIVE passes and a kernel
-    trace), rows split at the marker kernel, row order from
+    FETCH_SIZE, WRITE_SIZE and VALUBusy passes and a kernel trace), rows
+    split at the marker kernels, row order from
     gpurun_out/counters_order.json; byte counters scaled by the plain-copy
     calibration passes."""
     cal = copy_calibration(*copy_dirs)
@@ -563,7 +563,7 @@ def summarize_counters(dirs, copy_dirs):
              f"(factor {cal['FETCH_SIZE']['factor']:.4f}), WRITE_SIZE {cal['WRITE_SIZE']['kib_per_copy']:.1f} KiB "
              f"(factor {cal['WRITE_SIZE']['factor']:.4f}).", "",
              "| row | kernels | launches | dispatches | median us a launch | algorithmic bytes | FETCH+WRITE bytes "
-             "(scaled) | ratio | VALUBusy % | SCLK MHz |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "(scaled) | ratio | GB/s (algorithmic) | VALUBusy % |", "|---|---|---|---|---|---|---|---|---|---|"]
     table = {}
     for i, o in enumerate(order):
         recs = [r for p in passes for r in p.get(i, [])]
@@ -582,18 +582,17 @@ def summarize_counters(dirs, copy_dirs):
         if traced and n_disp:
             med = sum(statistics.median((int(traced[j * n_disp + q]["end"]) - int(traced[j * n_disp + q]["start"]))
                                         / 1e3 for j in range(L)) for q in range(n_disp))
-        grbm = per_launch("GRBM_GUI_ACTIVE")
         traffic = fetch * 1024 * cal["FETCH_SIZE"]["factor"] + write * 1024 * cal["WRITE_SIZE"]["factor"] \
             if fetch is not None and write is not None else None
-        sclk = grbm / 8 / (med * 1e-6) / 1e6 if grbm and med else None
         ent = {"traffic_ratio": round(traffic / o["bytes"], 4) if traffic else None,
                "valu_busy_pct": round(statistics.median(valu), 1) if valu else None,
-               "median_us": round(med, 2) if med else None, "sclk_mhz": round(sclk) if sclk else None}
+               "median_us": round(med, 2) if med else None,
+               "gbs": round(o["bytes"] / (med * 1e-6) / 1e9, 1) if med else None}
         table[o["row"]] = ent
         names = sorted({r["name"].split("(")[0].replace("void ", "") for r in recs})
         lines.append(f"| {o['row']} | {'<br>'.join('`' + n + '`' for n in names)} | {L} | {n_disp} | "
                      f"{ent['median_us']} | {round(o['bytes'])} | {round(traffic) if traffic else None} | "
-                     f"{ent['traffic_ratio']} | {ent['valu_busy_pct']} | {ent['sclk_mhz']} |")
+                     f"{ent['traffic_ratio']} | {ent['gbs']} | {ent['valu_busy_pct']} |")
     lines += ["", f"source_sha256: {sources_sha256()}", f"rows_json: {json.dumps(table)}"]
     return "\n".join(lines)
 
@@ -728,7 +727,7 @@ def main():
                                                          out_max=r1["out_max"]), max(a.steps, 5 * nl), env.s)
     lm_bytes = nvfp4_bytes(VOCAB, H) + H * 2 + 8
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
-    lm_traffic = lmhead_traffic()
+    lm_traffic = lmhead_traffic(lm_bytes)
     ms_per_step = r1["ms_per_step"]
     value = r1["step_bytes"] / (ms_per_step * 1e-3) / 1e9
     rot_b = NCOPIES * (sum(nvfp4_bytes(n, k) for _, n, k in PROJ) + 3 * E * nvfp4_bytes(I, H)) \

@@ -399,8 +399,12 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         const int ws0 = mf_code_wslot(lane, 0), ws1 = mf_code_wslot(lane, 1);
         const int rs0 = mf_code_rslot(li, q, 0), rs1 = mf_code_rslot(li, q, 1);
         // issue order as in the loop (scales, then the code pairs), so that
-        // each wait there only covers what it needs
-        uint4 sv = ld_stream16(cur.sp);
+        // each wait there only covers what it needs.  A scale load covers
+        // half of each row's 128-byte line (8 steps) and the other half is
+        // read a round later: the scales go through the L2 with the normal
+        // policy, so that the line is still there (streamed like the codes,
+        // the line was fetched twice: 7% more bytes at K = 2048)
+        uint4 sv = ld_l2_16(cur.sp);
         __builtin_amdgcn_sched_barrier(0);
         uint4 cw[D];
 #pragma unroll
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
                 const uint8_t *lb = last ? nxt.cb : cur.cb + 64 * (size_t)(s0 + D);
                 const uint8_t *ls = last ? nxt.sp : cur.sp + 8 * (size_t)(s0 + D);
                 cst[128 + lane] = sv;   // the round's scales to LDS (row r at byte 64 r)
-                sv = ld_stream16(ls);
+                sv = ld_l2_16(ls);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int d = 0; d < D; d += 2) {
@@ -718,7 +722,7 @@ __global__ __launch_bounds__(64 * kMfMaxSlices) void k_gemv_mf(const uint16_t *_
         xv[j] = m < m_rt ? xg[(size_t)m * cpr + kSliceChunks * ks + c] : make_uint4(0, 0, 0, 0);
     }
     const MfLines ln = mf_lines(codes, scales, n, k, row0, lane);
-    const uint4 sv = ld_stream16(ln.sp + 8 * (size_t)s0);
+    const uint4 sv = ld_l2_16(ln.sp + 8 * (size_t)s0);   // the slices of a line share it
     uint4 cw[kMfSliceSteps];
 #pragma unroll
     for (int d = 0; d < kMfSliceSteps; ++d)

@@ -47,6 +47,9 @@ __device__ __forceinline__ uint4 ld_stream16(const uint8_t *p) {
 __device__ __forceinline__ uint32_t ld_stream2(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
 }
+// A 16-byte load with the default cache policy (its line stays in the L2
+// for a later load of the rest of it).
+__device__ __forceinline__ uint4 ld_l2_16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // Both E4M3FN scale bytes of a chunk (low byte first) -> fp32, exactly.
 __device__ __forceinline__ void e4m3x2_to_f32(uint32_t two, float &s0, float &s1) {
