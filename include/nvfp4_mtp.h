@@ -326,16 +326,19 @@ int lmhead_gemv_argmax_embed(const uint16_t *h_bf16, int32_t m, const nvfp4_weig
  *   topk_w         out [m][top_k] fp32: softmax over the selected logits.
  *   workspace      at least moe_w4a16_gemv_workspace_bytes(m, top_k, e),
  *                  256-byte aligned, zero-filled before its first use (it
- *                  holds ticket counters and hand-off flags that every call
- *                  returns to zero).  One call at a time per workspace.
+ *                  holds ticket and column counters, which every call
+ *                  returns to zero, per-call tagged hand-off words and a
+ *                  sticky status word: see moe_workspace_status).  One
+ *                  call at a time per workspace.
  * Per selected expert: g = gate x, u = up x (fp32),
  * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
  * read once per call however many rows select it.  Requires H, I % 32 == 0
  * and round_up(m, 1|2|4|8) * max(H, I) * 2 <= 159744 bytes of LDS (H up to
- * 9984 at m = 8); NVFP4_ERR_UNSUPPORTED otherwise.  One launch when the
- * down pass's activation rows fit in LDS and the whole grid is resident at
- * once (decode at the usual shapes), else two (routing + gate/up, down +
- * combine).
+ * 9984 at m = 8); NVFP4_ERR_UNSUPPORTED otherwise.  One launch at one
+ * token when the down pass's activation rows fit in LDS and the whole grid
+ * is resident at once (decode at the usual shapes); else routing with
+ * gate/up (from three tokens on the routing is a launch of its own), then
+ * the down pass with the combine.
  */
 size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
 int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,

@@ -192,6 +192,7 @@ struct EmbedOut {
     int64_t stride_units;
     int vocab, units;
 };
+constexpr int kEmbBatch = 16;   // 16-byte loads in flight per lane in the gather
 
 // Wavefronts per LM-head workgroup: one workgroup per CU holding as many
 // wavefronts as the kernel's registers leave resident (3 per SIMD up to 170
@@ -650,15 +651,31 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         if constexpr (LP) out_lp[mm] = f.ls > 0.0f ? wkey - (f.lm + __logf(f.ls)) : __builtin_nanf("");
     }
     if (emb.table != nullptr) {
-        // the selected token of row mm is lane mm's
+        // the selected token of row mm is lane mm's.  Lane l copies units
+        // l, l + 64, ... of every row: item t of a lane is unit
+        // lane + 64 (t mod per) of row t / per.  A batch's loads are all
+        // issued before its stores (a load-store pair per unit waited one
+        // memory round trip per unit: 32 of them at eight rows).
         const int sel = lane < m_rt && f.key > -INFINITY ? f.idx : 0;
-        for (int mm = 0; mm < m_rt; ++mm) {
-            const int id = __shfl(sel, mm, 64);
-            const bool in = id >= 0 && id < emb.vocab;
-            const uint4 *src = emb.table + (size_t)(in ? id : 0) * emb.units;
-            uint4 *dst = emb.out + (size_t)mm * emb.stride_units;
-            for (int u = lane; u < emb.units; u += 64) dst[u] = in ? src[u] : make_uint4(0, 0, 0, 0);
-            if (lane == 0 && emb.id_log != nullptr) emb.id_log[mm] = id;
+        if (lane < m_rt && emb.id_log != nullptr) emb.id_log[lane] = sel;
+        const int per = (emb.units + 63) / 64, total = m_rt * per;
+        for (int t0 = 0; t0 < total; t0 += kEmbBatch) {
+            uint4 v[kEmbBatch];
+            int row[kEmbBatch], unit[kEmbBatch];   // unit -1: nothing to store
+#pragma unroll
+            for (int j = 0; j < kEmbBatch; ++j) {
+                const int t = t0 + j < total ? t0 + j : total - 1;
+                const int mm = t / per, u = lane + 64 * (t - mm * per);
+                const int id = __shfl(sel, mm, 64);
+                const bool in = id >= 0 && id < emb.vocab, live = t0 + j < total && u < emb.units;
+                v[j] = emb.table[(size_t)(in ? id : 0) * emb.units + (live ? u : 0)];
+                if (!in) v[j] = make_uint4(0, 0, 0, 0);
+                row[j] = mm;
+                unit[j] = live ? u : -1;
+            }
+#pragma unroll
+            for (int j = 0; j < kEmbBatch; ++j)
+                if (unit[j] >= 0) emb.out[(size_t)row[j] * emb.stride_units + unit[j]] = v[j];
         }
     }
     if (lane == 0) st_dev(ticket, 0u);   // ready for the next call

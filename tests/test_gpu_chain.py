@@ -190,17 +190,23 @@ def test_chain_in_a_graph():
         assert again == eager
 
 
-@pytest.mark.parametrize("m,masked,logprob", [(1, False, False), (3, True, True), (8, False, True)])
-def test_argmax_embed_fused(orc, m, masked, logprob):
+@pytest.mark.parametrize("m,masked,logprob,hidden,table_rows", [
+    (1, False, False, 1024, 7000), (3, True, True, 1024, 7000), (8, False, True, 1024, 7000),
+    (8, False, False, 7168, 7000),     # 14 units a lane per row: several load batches
+    (5, True, False, 1000, 3000),      # 125 units a row (not a multiple of 64); ids past the table
+    (1, False, False, 8, 7000)])       # one 16-byte unit a row
+def test_argmax_embed_fused(orc, m, masked, logprob, hidden, table_rows):
     """lmhead_gemv_argmax_embed equals lmhead_gemv_argmax(_masked/_logprob)
-    followed by embed_from_argmax, bit for bit, and writes nothing else."""
+    followed by embed_from_argmax, bit for bit, gathers what the oracle
+    gathers (a zero row for an id past the table), and writes nothing else."""
     import nvfp4_w4a16_mtp_amd as nv
-    v, k, hidden = 6000, 2048, 1024
+    v, k = 6000, 2048
     rng = np.random.default_rng([80, m])
     codes, scales, g = synth.quantized_domain_weight(rng, v, k)
     wd = _w(codes, scales, np.float32(g * 300))
     h = dev_bf16(synth.acts_bf16(81 + m, m, k))
-    table = dev_bf16(synth.acts_bf16(82, 7000, hidden))
+    table_h = synth.acts_bf16(82, table_rows, hidden)
+    table = dev_bf16(table_h)
     mask = _dev_mask(_mask_bits(rng.random((m, v)) < 0.2)) if masked else None
     if masked:
         ri, rm, rlp = nv.lmhead_gemv_argmax_masked(h, wd, mask, with_logprob=True)
@@ -218,6 +224,7 @@ def test_argmax_embed_fused(orc, m, masked, logprob):
         assert np.array_equal(lp.cpu().numpy().view(np.uint32), rlp.cpu().numpy().view(np.uint32))
     host = buf.cpu().numpy()
     assert np.array_equal(host[:, 16:16 + hidden].view(np.uint16), ref_rows.cpu().view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(host[:, 16:16 + hidden].view(np.uint16), orc.embed_rows(ri.cpu().numpy(), table_h))
     assert (host[:, :16] == 5).all() and (host[:, 16 + hidden:] == 5).all()
     assert np.array_equal(log.cpu().numpy(), ri.cpu().numpy())
 
