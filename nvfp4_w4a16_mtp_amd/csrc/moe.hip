@@ -398,36 +398,46 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
 // The routing's outputs: ids and weights, and (route != nullptr) the plan of
 // the two-launch path -- distinct experts, and per pair position (in
 // (expert, token) order) its token, pair and weight.  One workgroup.
-__device__ __forceinline__ void write_route(const RouteLds &L, const nvfp4_moe_weights &e, int m, int topk,
+__device__ __forceinline__ void write_route(RouteLds &L, const nvfp4_moe_weights &e, int m, int topk,
                                             int32_t *__restrict__ ids, float *__restrict__ wts,
-                                            MoeRoute *__restrict__ route) {
+                                            MoeRoute *__restrict__ route, const float *dec_lds = nullptr) {
     for (int p = threadIdx.x; p < m * topk; p += blockDim.x) {
         ids[p] = L.sel_i[p / topk][p % topk];
         wts[p] = L.sel_w[p / topk][p % topk];
     }
     if (route == nullptr) return;
     // thread q writes distinct expert q and its pairs; its first pair
-    // position is the count of the pairs before it (a serial loop in one
-    // thread took 10 us at 8 tokens)
+    // position is the exclusive prefix sum of the pair counts (nd <= 128):
+    // a scan inside each of the first two wavefronts, the second adding the
+    // first's total (a serial sum per thread cost a dependent LDS read per
+    // expert before it: about 2 us at 8 tokens)
     const int nd = L.n_distinct;
-    for (int q = threadIdx.x; q <= nd; q += blockDim.x) {
-        int pb = 0;
-        for (int j = 0; j < q; ++j) pb += L.ex[j].cnt;
-        route->pb[q] = pb;
-        if (q == nd) {
-            route->n_distinct = nd;
-            route->n_pairs = pb;
-            continue;
-        }
-        const MoeExpert &me = L.ex[q];
-        route->ex[q] = me;
-        route->ex_id[q] = me.expert;
-        route->ddec[q] = e.down_global[me.expert].dec;
-        for (int c = 0; c < me.cnt; ++c) {
-            route->pos_tok[pb + c] = me.tok[c];
-            route->pos_pair[pb + c] = me.pair[c];
-            route->pos_w[pb + c] = L.sel_w[me.tok[c]][me.pair[c] - me.tok[c] * topk];
-        }
+    const int q = threadIdx.x, lane = q & 63;
+    const int c = q < nd ? L.ex[q].cnt : 0;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63 && q < 128) L.wsum[q >> 6] = incl;
+    __syncthreads();
+    if (q > nd) return;
+    const int pb = q < 64 ? incl - c : q < 128 ? incl - c + L.wsum[0] : L.wsum[0] + L.wsum[1];
+    route->pb[q] = pb;
+    if (q == nd) {
+        route->n_distinct = nd;
+        route->n_pairs = pb;
+        return;
+    }
+    const MoeExpert &me = L.ex[q];
+    route->ex[q] = me;
+    route->ex_id[q] = me.expert;
+    route->ddec[q] = dec_lds != nullptr ? dec_lds[me.expert] : e.down_global[me.expert].dec;
+    for (int k = 0; k < me.cnt; ++k) {
+        route->pos_tok[pb + k] = me.tok[k];
+        route->pos_pair[pb + k] = me.pair[k];
+        route->pos_w[pb + k] = L.sel_w[me.tok[k]][me.pair[k] - me.tok[k] * topk];
     }
 }
 
@@ -550,8 +560,24 @@ __global__ __launch_bounds__(512) void k_moe_route(const float *__restrict__ log
                                                   nvfp4_moe_weights e, int32_t *__restrict__ ids,
                                                   float *__restrict__ wts, MoeRoute *__restrict__ route) {
     __shared__ RouteLds L;
+    __shared__ float s_dec[kMoeMaxExperts];
+    // every expert's down scale, loaded by the first 256 threads (the
+    // launch has 256 or 512) before the routing and kept in registers until
+    // it is done (the plan needs those of the routed experts)
+    float dec[kMoeMaxExperts / 256];
+#pragma unroll
+    for (int j = 0; j < kMoeMaxExperts / 256; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        dec[j] = threadIdx.x < 256 && i < E ? e.down_global[i].dec : 0.0f;
+    }
     moe_route_lds(logits, m, E, topk, L);
-    write_route(L, e, m, topk, ids, wts, route);
+#pragma unroll
+    for (int j = 0; j < kMoeMaxExperts / 256; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i < E && threadIdx.x < 256) s_dec[i] = dec[j];
+    }
+    __syncthreads();
+    write_route(L, e, m, topk, ids, wts, route, s_dec);
 }
 
 // Rows per slot of the ticket down pass: 4 (a 64-row tile, about 37 KB of
@@ -630,7 +656,7 @@ __global__ __launch_bounds__(256) void k_moe_down(nvfp4_moe_weights e, int m, in
 // once, and write d into LDS; the workgroup then forms y = sum of w * d per
 // token in ascending expert order.  No scratch buffer, no ticket, one pass.
 constexpr int kDownRows = 8;
-constexpr int kDownBatch = 4;   // items per slot in flight
+constexpr int kDownBatch = 2;   // items per slot in a batch; two batches in flight
 constexpr int kDownMaxExperts = 129;   // routed (<= 128) + the shared one
 constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the shared expert
 
@@ -642,6 +668,96 @@ constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the
 // the routed experts has finished) and reads the activations with
 // device-coherent loads.  The wait is bounded: past kSpinLimit polls the
 // workgroup writes NaN rows instead of waiting for ever.
+// The items of the row-owner down pass: item it is row r0 + it % kDownRows
+// of distinct expert it / kDownRows (the shared expert where s_ex is -1).
+// Slot sl takes items b0 + sl + kSlots n of a batch; items past the end load
+// a valid row (the last one) and are never computed.
+struct DownItems {
+    const uint8_t *codes, *scales;     // the routed experts' down matrices
+    const uint8_t *scodes, *sscales;   // the shared expert's
+    const int *s_ex;
+    int nitems, r0, H, I, sl, tl;
+};
+
+template <int CPL>
+__device__ __forceinline__ void down_rows_load(const DownItems &d, int b0, int kSlots, uint4 (&cw)[kDownBatch][CPL],
+                                               uint32_t (&sw)[kDownBatch][CPL]) {
+    const size_t wsz = (size_t)d.H * d.I;
+#pragma unroll
+    for (int n = 0; n < kDownBatch; ++n) {
+        const int it = min(b0 + d.sl + kSlots * n, d.nitems - 1);
+        const int u = it / kDownRows, row = min(d.r0 + it % kDownRows, d.H - 1);
+        // selects, not branches: a branch here made the compiler wait for
+        // loads already in flight
+        const int ex = d.s_ex[u];
+        const size_t eo = (size_t)(ex < 0 ? 0 : ex) * wsz;
+        const uint8_t *dc = (ex < 0 ? d.scodes : d.codes) + eo / 2 + (size_t)row * (d.I / 2);
+        const uint8_t *ds = (ex < 0 ? d.sscales : d.scales) + eo / 16 + (size_t)row * (d.I / 16);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = d.tl + 16 * j;
+            cw[n][j] = ld_stream16(dc + 16 * c);
+            sw[n][j] = ld_stream2(ds + 2 * c);
+        }
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void down_rows_fma(const DownItems &d, int b0, int kSlots,
+                                              const uint4 (&cw)[kDownBatch][CPL],
+                                              const uint32_t (&sw)[kDownBatch][CPL], const int *s_pb,
+                                              const float *s_dec, const uint4 *smem, int C,
+                                              float (*contrib)[kDownRows]) {
+#pragma unroll
+    for (int n = 0; n < kDownBatch; ++n) {
+        const int it = b0 + d.sl + kSlots * n;
+        if (it >= d.nitems) continue;   // uniform over the slot
+        const int u = it / kDownRows, r = it % kDownRows;
+        for (int pos = s_pb[u]; pos < s_pb[u + 1]; ++pos) {
+            float acc[1] = {0.0f};
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)pos * 4 * C, C, d.tl + 16 * j, acc);
+            const float v = row16_sum(acc[0]);
+            if (d.tl == 0) contrib[pos][r] = v * s_dec[u];
+        }
+    }
+}
+
+// stage_rows in two steps, so that loads issued in between do not delay the
+// image: the first kStageBatch units of each thread into registers, then
+// their stores and the rest of the image.
+__device__ __forceinline__ void stage_rows_first(uint4 (&v)[kStageBatch], const uint16_t *__restrict__ src,
+                                                 const int *rows, int cnt, int k) {
+    const int upr = k >> 3, units = cnt * upr;
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        const int p = threadIdx.x + j * blockDim.x, mm = p / upr;
+        v[j] = p < units ? reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[p - mm * upr]
+                         : make_uint4(0, 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void stage_rows_rest(uint4 *xs, const uint4 (&v)[kStageBatch],
+                                                const uint16_t *__restrict__ src, const int *rows, int cnt, int k) {
+    const int C = k >> 5, upr = k >> 3, units = cnt * upr, done = kStageBatch * blockDim.x;
+    auto put = [&](int p, uint4 val) {
+        const int mm = p / upr, w = p - mm * upr;
+        xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = val;
+    };
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        const int p = threadIdx.x + j * blockDim.x;
+        if (p < units) put(p, v[j]);
+    }
+    if (units > done)
+        stage_batched(
+            units - done, threadIdx.x, blockDim.x,
+            [&](int q) {
+                const int p = q + done, mm = p / upr;
+                return reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[p - mm * upr];
+            },
+            [&](int q, uint4 val) { put(q + done, val); });
+}
+
 template <int CPL, bool FUSED, int NW = 4>
 __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
                                                const MoeRoute *__restrict__ route, const float *__restrict__ logits,
@@ -719,88 +835,74 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     const int sl = wave * 4 + (lane >> 4);
     const int r0 = bx * kDownRows;
     const int nitems = nd * kDownRows;
-    const size_t wsz = (size_t)H * I;
-    constexpr int kSlots = 4 * NW;
-    for (int b0 = 0; b0 < nitems; b0 += kSlots * kDownBatch) {
-        // weight loads of this batch first, then (first batch only) the
-        // activation image, so that both are in flight together
-        uint4 cw[kDownBatch][CPL];
-        uint32_t sw[kDownBatch][CPL];
-#pragma unroll
-        for (int n = 0; n < kDownBatch; ++n) {
-            // items past the end load a valid row (the last one); their
-            // results are never used
-            const int it = min(b0 + sl + kSlots * n, nitems - 1);
-            const int u = it / kDownRows, row = min(r0 + it % kDownRows, H - 1);
-            const bool shared_row = s_ex[u] < 0;
-            const uint8_t *dc = (shared_row ? sh.dcodes : e.down_codes + (size_t)s_ex[u] * (wsz / 2)) + (size_t)row * (I / 2);
-            const uint8_t *ds = (shared_row ? sh.dscales : e.down_scales + (size_t)s_ex[u] * (wsz / 16)) +
-                                (size_t)row * (I / 16);
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = tl + 16 * j;
-                cw[n][j] = ld_stream16(dc + 16 * c);
-                sw[n][j] = ld_stream2(ds + 2 * c);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any arithmetic
-        if (b0 == 0) {
-            if constexpr (FUSED) {
-                if (threadIdx.x == 0) {
-                    // this call's tag; the count of calls is advanced whether
-                    // or not the wait succeeds, so a late release of this call
-                    // cannot satisfy the next one
-                    unsigned int *go = done + kSyncWords + kGoStride * bx;
-                    const unsigned int c = ld_dev(go + 1);
-                    st_dev(go + 1, c + 1u);
-                    const unsigned int want = (c + 1u) * kGoTag;
-                    unsigned int g = ld_dev(go);
-                    int bad = 0;
-                    if (g != want && g != c * kGoTag) {
-                        bad = (int)kMoeStatusCorrupt;
-                    } else {
-                        int it = 0;
-                        while (g != want && it < kSpinLimit) {
-                            __builtin_amdgcn_s_sleep(2);
-                            g = ld_dev(go);
-                            ++it;
-                        }
-                        if (g != want) bad = (int)kMoeStatusTimeout;
-                    }
-                    if (bad)
-                        __hip_atomic_fetch_or(status, (unsigned int)bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    s_late = bad;
-                }
-                __syncthreads();
-                if (s_late) {
-                    for (int i = threadIdx.x; i < m * kDownRows; i += blockDim.x) {
-                        const int row = r0 + i % kDownRows;
-                        if (row < H) y[(size_t)(i / kDownRows) * H + row] = __builtin_nanf("");
-                    }
-                    return;
-                }
-                if (sh.on && threadIdx.x < m) s_w[P0 + threadIdx.x] = ld_dev(&sh.sgate[threadIdx.x]);
-                stage_rows_dev(smem, act, (size_t)m * topk, s_pair, P0, P0, I);
-                if (sh.on) stage_rows_dev(smem + (size_t)P0 * 4 * C, sh.sact, (size_t)m, s_pair + P0, m, m, I);
+    constexpr int kSlots = 4 * NW, kStep = kSlots * kDownBatch;
+    const DownItems it{e.down_codes, e.down_scales, sh.dcodes, sh.dscales, s_ex, nitems, r0, H, I, sl, tl};
+    // two register batches of weights, both issued before the activation
+    // image is complete; from then on the loads of one batch are in flight
+    // while the other is computed
+    uint4 ca[kDownBatch][CPL], cb[kDownBatch][CPL];
+    uint32_t sa[kDownBatch][CPL], sb[kDownBatch][CPL];
+    if constexpr (FUSED) {
+        // the weights first: they stream while gate/up still runs
+        down_rows_load<CPL>(it, 0, kSlots, ca, sa);
+        down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
+        __builtin_amdgcn_sched_barrier(0);
+        if (threadIdx.x == 0) {
+            // this call's tag; the count of calls is advanced whether
+            // or not the wait succeeds, so a late release of this call
+            // cannot satisfy the next one
+            unsigned int *go = done + kSyncWords + kGoStride * bx;
+            const unsigned int c = ld_dev(go + 1);
+            st_dev(go + 1, c + 1u);
+            const unsigned int want = (c + 1u) * kGoTag;
+            unsigned int g = ld_dev(go);
+            int bad = 0;
+            if (g != want && g != c * kGoTag) {
+                bad = (int)kMoeStatusCorrupt;
             } else {
-                stage_rows(smem, act, s_pair, P0, P0, I);   // row pos of the image = pair position pos
-                if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
+                int n = 0;
+                while (g != want && n < kSpinLimit) {
+                    __builtin_amdgcn_s_sleep(2);
+                    g = ld_dev(go);
+                    ++n;
+                }
+                if (g != want) bad = (int)kMoeStatusTimeout;
             }
-            __syncthreads();
+            if (bad)
+                __hip_atomic_fetch_or(status, (unsigned int)bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_late = bad;
         }
-#pragma unroll
-        for (int n = 0; n < kDownBatch; ++n) {
-            const int it = b0 + sl + kSlots * n;
-            if (it >= nitems) continue;   // uniform over the slot
-            const int u = it / kDownRows, r = it % kDownRows;
-            for (int pos = s_pb[u]; pos < s_pb[u + 1]; ++pos) {
-                float acc[1] = {0.0f};
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)pos * 4 * C, C, tl + 16 * j, acc);
-                const float d = row16_sum(acc[0]);
-                if (tl == 0) contrib[pos][r] = d * s_dec[u];
+        __syncthreads();
+        if (s_late) {
+            for (int i = threadIdx.x; i < m * kDownRows; i += blockDim.x) {
+                const int row = r0 + i % kDownRows;
+                if (row < H) y[(size_t)(i / kDownRows) * H + row] = __builtin_nanf("");
             }
+            return;
         }
+        if (sh.on && threadIdx.x < m) s_w[P0 + threadIdx.x] = ld_dev(&sh.sgate[threadIdx.x]);
+        stage_rows_dev(smem, act, (size_t)m * topk, s_pair, P0, P0, I);
+        if (sh.on) stage_rows_dev(smem + (size_t)P0 * 4 * C, sh.sact, (size_t)m, s_pair + P0, m, m, I);
+    } else {
+        // the activation loads first, so that waiting for them does not wait
+        // for the weights issued after them
+        uint4 av[kStageBatch];
+        stage_rows_first(av, act, s_pair, P0, I);   // row pos of the image = pair position pos
+        down_rows_load<CPL>(it, 0, kSlots, ca, sa);
+        down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
+        __builtin_amdgcn_sched_barrier(0);
+        stage_rows_rest(smem, av, act, s_pair, P0, I);
+        if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < nitems; b0 += 2 * kStep) {
+        down_rows_fma<CPL>(it, b0, kSlots, ca, sa, s_pb, s_dec, smem, C, contrib);
+        if (b0 + 2 * kStep < nitems) down_rows_load<CPL>(it, b0 + 2 * kStep, kSlots, ca, sa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b0 + kStep >= nitems) break;
+        down_rows_fma<CPL>(it, b0 + kStep, kSlots, cb, sb, s_pb, s_dec, smem, C, contrib);
+        if (b0 + 3 * kStep < nitems) down_rows_load<CPL>(it, b0 + 3 * kStep, kSlots, cb, sb);
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // y[t][row] = sum over token t's pairs, in ascending expert order, of
