@@ -404,7 +404,8 @@ def gemm_rows(env, shapes):
         w = nv.nvfp4_quantize(env.randn((n, k), 0.02))
         x = env.randn((m, k))
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ms = _time(torch, lambda i: nv.w4a16_gemm_m128(x, w, out=y), 10, env.s)
+        ws = nv.gemm_workspace(m, n, k, dev)
+        ms = _time(torch, lambda i: nv.w4a16_gemm_m128(x, w, out=y, workspace=ws), 10, env.s)
         tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
         out[f"gemm_{name}_m{m}"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                                     "frac_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}

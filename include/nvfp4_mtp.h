@@ -170,11 +170,13 @@ int w4a16_gemv_grouped(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
  *   y          [m][w->n] fp32 or bf16 (y_dtype), 4-byte aligned.
  *   workspace  NULL, or 16-byte aligned device scratch of at least
  *              w4a16_gemm_m128_workspace_bytes(m, w->n, w->k) bytes.  When
- *              the output tiles are too few to fill the device, K is cut
- *              into slices whose fp32 partial sums go to the workspace and
- *              are added in slice order by a second kernel (the same order
- *              on every call).  NULL: one pass over K.  Nothing needs to be
- *              initialised; calls that overlap on one workspace race.
+ *              the output tiles are too few to fill the device, or a last
+ *              round of them would leave most of it idle, K of those tiles
+ *              is cut into slices whose fp32 partial sums go to the
+ *              workspace and are added in slice order by a second kernel
+ *              (the same order on every call).  NULL: one pass over K.
+ *              Nothing needs to be initialised; calls that overlap on one
+ *              workspace race.
  * Any n >= 0; rows and columns outside the tiles are masked.  Errors:
  * NVFP4_ERR_WORKSPACE for a non-NULL workspace below the size needed, and
  * those of w4a16_gemv.

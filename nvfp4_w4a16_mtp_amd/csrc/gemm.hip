@@ -14,10 +14,12 @@
 // to spread the rows of an operand load and of a staging store over the
 // banks.  The global scale is applied in the epilogue.
 //
-// Prompt chunks too short to fill the chip with output tiles (a few hundred
-// rows) split K over up to 16 workgroups per tile, which write fp32 partial
-// planes to the caller's workspace; a second kernel sums them in slice order
-// and applies the global scale.
+// The tiles of a call fill the chip in rounds of resident workgroups, and a
+// last round that is only partly filled costs a full one.  With a workspace
+// the tiles of that last round (all tiles, for prompt chunks too short to
+// fill one round) split K over up to 16 workgroups each, in the same launch
+// as the whole tiles; the slices write fp32 tile-shaped partial planes and a
+// second kernel sums them in slice order and applies the global scale.
 //
 // The dequantization runs on the same SIMDs as the MFMAs and the two hardly
 // overlap (timed: 4 MFMAs and 32 fp32 multiplies per wavefront cost close to
@@ -51,15 +53,23 @@ __device__ __forceinline__ uint32_t dq2(uint32_t word, float sf) {
 // activation tile and 8192 / (2 BM) weights.  Tall tiles raise the wave
 // priority over their MFMA phase, so that the CU's other workgroup stages
 // in the gaps (measured +1-5% at 8192 rows; it slowed the 128-row tile).
-// K split: slice z = blockIdx.z of gridDim.z takes the K steps
-// [z S / Z, (z + 1) S / Z) of the S = ceil(K / 64) and, with PART, writes
-// its fp32 sums without the global scale to plane z of `part` (row-major
-// [M][N] planes, `plane` floats apart) for k_gemm_reduce.
-template <int BM, bool BF16OUT, bool PART>
+// Work items (blockIdx.x): tiles [0, full) in row-major tile order (column
+// tiles fastest) over the whole K, written to y; then `nz` slices of each
+// later tile.  Slice z takes the K steps [z S / nz, (z + 1) S / nz) of the
+// S = ceil(K / 64) and writes its fp32 sums without the global scale to
+// partial plane (tile - full) nz + z of `part`, a BM x 128 row-major plane
+// per (tile, slice), for k_gemm_reduce.
+struct GemmWork {
+    int cols;      // column tiles
+    int full;      // tiles computed whole
+    int nz;        // K slices of each later tile
+    float *part;   // partial planes of the split tiles
+};
+
+template <int BM, bool BF16OUT>
 __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 4 : 3))) void k_gemm(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-    const nvfp4_global *__restrict__ g, int M, int N, int K, void *__restrict__ y, float *__restrict__ part,
-    size_t plane) {
+    const nvfp4_global *__restrict__ g, int M, int N, int K, void *__restrict__ y, GemmWork wk) {
     constexpr int NT = 2 * BM;          // threads
     constexpr int BPR = NT / kBN;       // weight staging parts per tile row: 2 or 4
     constexpr int CPT = 64 / BPR / 8;   // code dwords (8 codes each) per thread: 4 or 2
@@ -69,7 +79,11 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
 
     const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kBN;
+    const int id = blockIdx.x;
+    const bool split = id >= wk.full;
+    const int tile = split ? wk.full + (id - wk.full) / wk.nz : id;
+    const int z = split ? (id - wk.full) % wk.nz : 0, nz = split ? wk.nz : 1;
+    const int m0 = tile / wk.cols * BM, n0 = tile % wk.cols * kBN;
 
     // staging roles: activation rows th / 8 + (NT / 8) q, q = 0..3, chunk th % 8
     // (8 bf16) of the K step -- each load instruction of a wavefront covers
@@ -123,7 +137,7 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int steps = (K + kBK - 1) / kBK, nz = gridDim.z, z = blockIdx.z;
+    const int steps = (K + kBK - 1) / kBK;
     const int kb0 = (int)((long)z * steps / nz) * kBK, kb1 = min(K, (int)((long)(z + 1) * steps / nz) * kBK);
     if (kb0 < kb1) load_step(kb0);
     for (int k0 = kb0; k0 < kb1; k0 += kBK) {
@@ -161,8 +175,21 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
         __syncthreads();
     }
 
-    const float dec = PART ? 1.0f : g->dec;
-    float *pz = PART ? part + (size_t)z * plane : nullptr;
+    if (split) {
+        // the whole plane, rows and columns past the matrix included (the
+        // reduction reads them and drops them)
+        float *pz = wk.part + ((size_t)(tile - wk.full) * nz + z) * (BM * kBN);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 64 * wn + 16 * j + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pz[(64 * wm + 16 * i + 4 * (lane >> 4) + r) * kBN + c] = acc[i][j][r];
+            }
+        return;
+    }
+    const float dec = g->dec;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -173,9 +200,7 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
                 const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + r;
                 if (m < M && n < N) {
                     const float o = acc[i][j][r] * dec;
-                    if constexpr (PART)
-                        pz[(size_t)m * N + n] = o;
-                    else if constexpr (BF16OUT)
+                    if constexpr (BF16OUT)
                         reinterpret_cast<uint16_t *>(y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(o);
                     else
                         reinterpret_cast<float *>(y)[(size_t)m * N + n] = o;
@@ -184,33 +209,38 @@ __global__ __launch_bounds__(2 * BM) __attribute__((amdgpu_waves_per_eu(BM == 25
         }
 }
 
-// Sum of the K-slice partials of each output in slice order (the same
-// order on every call), times the global scale, as fp32 or bf16.  Planes are
-// padded to a multiple of 4 floats, so the float4 reads of a last group stay
-// inside the plane.
-template <bool BF16OUT>
-__global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ part, size_t plane, int nz,
-                                                     size_t count, const nvfp4_global *__restrict__ g,
+// Sum of the K-slice partials of each output of the split tiles in slice
+// order (the same order on every call), times the global scale, as fp32 or
+// bf16.  Thread items are 4 consecutive columns of one tile row.
+template <int BM, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ part, int tiles, int nz, int first,
+                                                     int cols, int M, int N, const nvfp4_global *__restrict__ g,
                                                      void *__restrict__ y) {
+    constexpr int kPlane = BM * kBN;
     const float dec = g->dec;
-    const size_t stride = (size_t)gridDim.x * 256 * 4;
+    const size_t count = (size_t)tiles * kPlane, stride = (size_t)gridDim.x * 256 * 4;
     for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; e < count; e += stride) {
-        float4 a = *reinterpret_cast<const float4 *>(part + e);
-        for (int z = 1; z < nz; ++z) {
-            const float4 b = *reinterpret_cast<const float4 *>(part + (size_t)z * plane + e);
+        const int t = (int)(e / kPlane), local = (int)(e % kPlane);
+        const float *src = part + (size_t)t * nz * kPlane + local;
+        float4 a = *reinterpret_cast<const float4 *>(src);
+        for (int s = 1; s < nz; ++s) {
+            const float4 b = *reinterpret_cast<const float4 *>(src + (size_t)s * kPlane);
             a.x += b.x;
             a.y += b.y;
             a.z += b.z;
             a.w += b.w;
         }
+        const int tile = first + t;
+        const int m = tile / cols * BM + local / kBN, n = tile % cols * kBN + local % kBN;
+        if (m >= M) continue;
         const float v[4] = {a.x * dec, a.y * dec, a.z * dec, a.w * dec};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (e + c >= count) break;
+            if (n + c >= N) break;
             if constexpr (BF16OUT)
-                reinterpret_cast<uint16_t *>(y)[e + c] = (uint16_t)f32_to_bf16_bits(v[c]);
+                reinterpret_cast<uint16_t *>(y)[(size_t)m * N + n + c] = (uint16_t)f32_to_bf16_bits(v[c]);
             else
-                reinterpret_cast<float *>(y)[e + c] = v[c];
+                reinterpret_cast<float *>(y)[(size_t)m * N + n + c] = v[c];
         }
     }
 }
@@ -218,59 +248,99 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ p
 // Tile choice by rounds of resident workgroups: a 256-row round (2 per CU)
 // takes about kTallRound times a 128-row round (3 per CU) -- measured at
 // 8192 x 17408 x 5120, where both fill the chip: 919 against 815 TFLOP/s,
-// 2 x 256 / 919 over 3 x 128 / 815.  A partly filled last round costs a
-// full one, so e.g. 1024 x 17408 (544 tall tiles, 2 rounds) keeps the
-// 128-row tile (1088 tiles, 2 rounds).
+// 2 x 256 / 919 over 3 x 128 / 815.  Without a split a partly filled last
+// round costs a full one (1024 x 17408: 544 tall tiles on 512 slots take two
+// rounds).  With a workspace the last round's tiles are split over K: S
+// slices each, S = min(kMaxSplit, slots / tiles of that round, steps /
+// kMinSliceSteps), so the slices take about 1 / S of a round, plus the
+// reduction's traffic.
 constexpr double kTallRound = 1.18;
 constexpr int kMaxSplit = 16;             // K slices at most
 // 64-k steps per slice at least: at 128 x 2048 x 4096 slices of 8 steps
 // (8 slices) took 18.8-19.6 us against 21.4-22.3 for 16 slices of 4; the
 // other 128- and 1024-row shapes were within noise; at most 4 or 8 slices
 // instead of 16 made 128 x 5120 x 17408 slower (79, 60 against 52 us).
-constexpr int kMinSliceSteps = 8;
+// 256-row tiles that all split (less than one round of them) need longer
+// slices: 4 and 8 ways in slices of 8 steps, 8192 x 512 x 2048 and 1024 x
+// 2048 x 4096 took 43.6 and 40.9 us against 35.9 and 37.0 us as 128-row
+// tiles; the tiles of a last round split in slices of 8 steps (1024 x 17408
+// x 5120: 32 tiles in 10 slices, 204 us against 238-252 us unsplit).
+constexpr int kMinSliceSteps = 8, kMinSliceSteps256 = 24;
+constexpr long kMaxSplitRounds = 3;   // split the last round of at most this many
+// Rates of whole rounds (bf16 TFLOP/s, 128- and 256-row tiles) and of the
+// reduction (bytes/us), for the cost of a split in rounds.
+constexpr double kRate128 = 815e6, kRate256 = 919e6, kReduceRate = 5e6, kReduceLaunchUs = 4.0;
 
 struct GemmPlan {
     int bm;       // 128 or 256
-    int split;    // K slices (128-row tiles only)
-    size_t plane; // floats per partial plane (split > 1)
+    int cols;     // column tiles
+    int full;     // tiles computed whole
+    int split;    // tiles split over K (the last ones)
+    int nz;       // K slices of a split tile
+    size_t ws;    // workspace bytes for the partial planes
 };
 
-// 256-row tiles where they take fewer rounds; else 128-row tiles, with K cut
-// into slices when the tiles fill less than one round of resident
-// workgroups (prompt chunks of a few hundred rows): then up to kMaxSplit
-// slices bring the grid to about one round.
-static GemmPlan gemm_plan(int m, int n, int k) {
-    const long cols = (n + kBN - 1) / kBN;
-    const long slots_s = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<128, false, false>), 256, 0);
-    const long slots_t = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<256, false, false>), 512, 0);
-    const long tiles_s = cols * ((m + 127) / 128), tiles_t = cols * ((m + 255) / 256);
-    const long rounds_s = (tiles_s + slots_s - 1) / slots_s, rounds_t = (tiles_t + slots_t - 1) / slots_t;
-    GemmPlan p{128, 1, 0};
-    if (kTallRound * rounds_t < rounds_s) {
-        p.bm = 256;
-        return p;
-    }
+static GemmPlan gemm_plan_bm(int bm, long slots, int m, int n, int k, bool can_split, double &cost) {
+    const long cols = (n + kBN - 1) / kBN, tiles = cols * ((m + bm - 1) / bm);
     const long steps = (k + kBK - 1) / kBK;
-    long split = slots_s / (tiles_s > 0 ? tiles_s : 1);
-    split = split < kMaxSplit ? split : kMaxSplit;
-    split = split < steps / kMinSliceSteps ? split : steps / kMinSliceSteps;
-    if (split >= 2) {
-        p.split = (int)split;
-        p.plane = ((size_t)m * n + 3) & ~(size_t)3;
-    }
+    const double c = bm == 256 ? kTallRound : 1.0;
+    const long rounds = (tiles + slots - 1) / slots;
+    GemmPlan p{bm, (int)cols, (int)tiles, 0, 1, 0};
+    cost = rounds * c;
+    // after several rounds the workgroups no longer start in step, and a
+    // last partial round costs less than a whole one: 8192 x 17408 x 5120
+    // (8.5 rounds of tall tiles) took 1445 us with its last 256 tiles split
+    // against 1302-1310 us unsplit, while 8192 x 5120 x 17408 (2.5 rounds)
+    // gained 1459 -> 1375 us
+    if (!can_split || rounds > kMaxSplitRounds) return p;
+    const long tail = tiles - (rounds - 1) * slots;   // tiles of the last round
+    long nz = slots / tail;
+    nz = nz < kMaxSplit ? nz : kMaxSplit;
+    const long min_steps = bm == 256 && rounds == 1 ? kMinSliceSteps256 : kMinSliceSteps;
+    nz = nz < steps / min_steps ? nz : steps / min_steps;
+    if (nz < 2) return p;
+    const double round_us = 2.0 * bm * kBN * (double)k * slots / (bm == 256 ? kRate256 : kRate128);
+    const double red_us = (double)tail * nz * bm * kBN * 4 / kReduceRate + kReduceLaunchUs;
+    const double split_cost = (rounds - 1) * c + c / nz + red_us / round_us;
+    if (split_cost >= cost) return p;
+    cost = split_cost;
+    p.full = (int)(tiles - tail);
+    p.split = (int)tail;
+    p.nz = (int)nz;
+    p.ws = (size_t)tail * nz * bm * kBN * sizeof(float);
     return p;
 }
 
-template <int BM, bool PART>
-static void launch_gemm(const uint16_t *x, int m, const nvfp4_weight *w, void *y, bool bf16, float *part, size_t plane,
-                        int split, hipStream_t s) {
-    dim3 grid((w->n + kBN - 1) / kBN, (m + BM - 1) / BM, split);
+static GemmPlan gemm_plan(int m, int n, int k, bool can_split) {
+    const long slots_s = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<128, false>), 256, 0);
+    const long slots_t = (long)num_cus() * blocks_per_cu(reinterpret_cast<const void *>(k_gemm<256, false>), 512, 0);
+    double cs, ct;
+    const GemmPlan ps = gemm_plan_bm(128, slots_s, m, n, k, can_split, cs);
+    const GemmPlan pt = gemm_plan_bm(256, slots_t, m, n, k, can_split, ct);
+    return ct < cs ? pt : ps;
+}
+
+template <int BM>
+static void launch_gemm(const uint16_t *x, int m, const nvfp4_weight *w, void *y, bool bf16, const GemmPlan &p,
+                        float *part, hipStream_t s) {
+    const GemmWork wk{p.cols, p.full, p.nz, part};
+    const dim3 grid(p.full + p.split * p.nz);
     if (bf16)
-        hipLaunchKernelGGL((k_gemm<BM, true, PART>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m,
-                           w->n, w->k, y, part, plane);
+        hipLaunchKernelGGL((k_gemm<BM, true>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n,
+                           w->k, y, wk);
     else
-        hipLaunchKernelGGL((k_gemm<BM, false, PART>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global,
-                           m, w->n, w->k, y, part, plane);
+        hipLaunchKernelGGL((k_gemm<BM, false>), grid, dim3(2 * BM), 0, s, x, w->codes, w->scales, w->global, m, w->n,
+                           w->k, y, wk);
+    if (p.split == 0) return;
+    const size_t groups = (size_t)p.split * BM * kBN / 4;
+    const size_t want = (groups + 255) / 256, cap = (size_t)num_cus() * 8;
+    const unsigned blocks = (unsigned)(want < cap ? want : cap);
+    if (bf16)
+        hipLaunchKernelGGL((k_gemm_reduce<BM, true>), dim3(blocks), dim3(256), 0, s, part, p.split, p.nz, p.full,
+                           p.cols, m, w->n, w->global, y);
+    else
+        hipLaunchKernelGGL((k_gemm_reduce<BM, false>), dim3(blocks), dim3(256), 0, s, part, p.split, p.nz, p.full,
+                           p.cols, m, w->n, w->global, y);
 }
 
 }  // namespace nvfp4
@@ -279,8 +349,7 @@ using namespace nvfp4;
 
 extern "C" size_t w4a16_gemm_m128_workspace_bytes(int32_t m, int32_t n, int32_t k) {
     if (m < 1 || n < 1 || k < 32) return 0;
-    const GemmPlan p = gemm_plan(m, n, k);
-    return p.split > 1 ? (size_t)p.split * p.plane * sizeof(float) : 0;
+    return gemm_plan(m, n, k, true).ws;
 }
 
 extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, void *y, int32_t y_dtype,
@@ -294,36 +363,20 @@ extern "C" int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_we
         return fail(NVFP4_ERR_ARG, "w4a16_gemm_m128: unknown y_dtype %d", y_dtype);
     if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: x not 16-byte aligned");
     if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: y not 4-byte aligned");
-    if ((w->n + kBN - 1) / kBN > 2147483647 || (m + 127) / 128 > 65535)
-        return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemm_m128: grid too large");
+    const long items = (long)((w->n + kBN - 1) / kBN) * ((m + 127) / 128) * kMaxSplit;
+    if (items > 2147483647L) return fail(NVFP4_ERR_UNSUPPORTED, "w4a16_gemm_m128: grid too large");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = y_dtype == NVFP4_OUT_BF16;
-    GemmPlan p = gemm_plan(m, w->n, w->k);
-    if (p.split > 1 && workspace == nullptr) p.split = 1;   // no workspace: one pass over K
-    if (p.split > 1) {
-        const size_t need = (size_t)p.split * p.plane * sizeof(float);
-        if (ws_bytes < need)
-            return fail(NVFP4_ERR_WORKSPACE, "w4a16_gemm_m128: workspace of %zu bytes, %zu needed", ws_bytes, need);
+    const GemmPlan p = gemm_plan(m, w->n, w->k, workspace != nullptr);   // no workspace: one pass over K
+    if (p.split > 0) {
+        if (ws_bytes < p.ws)
+            return fail(NVFP4_ERR_WORKSPACE, "w4a16_gemm_m128: workspace of %zu bytes, %zu needed", ws_bytes, p.ws);
         if (!aligned(workspace, 16)) return fail(NVFP4_ERR_ALIGN, "w4a16_gemm_m128: workspace not 16-byte aligned");
-        float *part = reinterpret_cast<float *>(workspace);
-        launch_gemm<128, true>(x_bf16, m, w, y, bf16, part, p.plane, p.split, s);
-        rc = check_launch("w4a16_gemm_m128");
-        if (rc) return rc;
-        const size_t count = (size_t)m * w->n;
-        const size_t groups = (count + 3) / 4;
-        const size_t want = (groups + 255) / 256, cap = (size_t)num_cus() * 8;
-        const unsigned blocks = (unsigned)(want < cap ? want : cap);
-        if (bf16)
-            hipLaunchKernelGGL(k_gemm_reduce<true>, dim3(blocks), dim3(256), 0, s, part, p.plane, p.split, count,
-                               w->global, y);
-        else
-            hipLaunchKernelGGL(k_gemm_reduce<false>, dim3(blocks), dim3(256), 0, s, part, p.plane, p.split, count,
-                               w->global, y);
-        return check_launch("w4a16_gemm_m128");
     }
+    float *part = reinterpret_cast<float *>(workspace);
     if (p.bm == 256)
-        launch_gemm<256, false>(x_bf16, m, w, y, bf16, nullptr, 0, 1, s);
+        launch_gemm<256>(x_bf16, m, w, y, bf16, p, part, s);
     else
-        launch_gemm<128, false>(x_bf16, m, w, y, bf16, nullptr, 0, 1, s);
+        launch_gemm<128>(x_bf16, m, w, y, bf16, p, part, s);
     return check_launch("w4a16_gemm_m128");
 }

@@ -544,8 +544,12 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     }
 }
 
+// Without a plan (one or two tokens) every workgroup routes for itself and
+// its latency chain is long: 128 registers, four workgroups a CU, took two
+// tokens from 26.3 to 22.5 us (a few bytes spill); the planned kernel keeps
+// its 152 registers (capped, it was slower).
 template <int CPL, bool PLANNED>
-__global__ __launch_bounds__(256) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PLANNED ? 1 : 4))) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                     int m, int E, int topk, nvfp4_moe_weights e,
                                                     int32_t *__restrict__ ids, float *__restrict__ wts,
                                                     MoeRoute *__restrict__ route, uint16_t *__restrict__ act,

@@ -53,6 +53,34 @@ def test_split_k_equals_one_pass(orc, m, n, k):
     assert np.array_equal(y1.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("m,n,k,first_tail", [
+    (256, 66560, 2048, 65536),     # 520 tall tiles on 512 slots: the last 8 split over K
+    (128, 102400, 2048, 98304)])   # 800 tiles on 768 slots: the last 32 split over K
+def test_last_round_split_bit_exact(orc, m, n, k, first_tail):
+    """With 256 CUs these shapes fill one round of resident workgroups and
+    spill a few tiles into a second; with a workspace those tiles split K
+    over several workgroups in the same launch (tile-shaped partials, summed
+    in slice order).  Exact family: the split call, one pass over K and the
+    oracle agree bit for bit -- the oracle on 3000 random outputs and on
+    three whole rows of the split tiles, one pass on every output."""
+    import nvfp4_w4a16_mtp_amd as nv
+    ws = nv.gemm_workspace(m, n, k, torch.device("cuda"))
+    assert ws is not None
+    x, codes, scales, g = synth.exact_family(220 + m, m, n, k)
+    wd = _w(codes, scales, g)
+    xd = dev_bf16(x)
+    ys = nv.w4a16_gemm_m128(xd, wd, workspace=ws)
+    y1 = nv.w4a16_gemm_m128(xd, wd, split_k=False)
+    assert torch.equal(ys.view(torch.int32), y1.view(torch.int32))
+    rng = np.random.default_rng(221)
+    tail_n = np.arange(first_tail, n)
+    mi = np.concatenate([rng.integers(0, m, 3000), np.repeat([0, m // 2 + 1, m - 1], tail_n.size)])
+    ni = np.concatenate([rng.integers(0, n, 3000), np.tile(tail_n, 3)])
+    got = ys[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    ref = orc.gemm_sample(x, codes, scales, g, mi, ni)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 def test_split_k_workspace_too_small():
     import nvfp4_w4a16_mtp_amd as nv
     x, codes, scales, g = synth.exact_family(5, 128, 512, 1024)
