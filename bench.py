@@ -3,8 +3,8 @@
 A step is one draft step of a Qwen-shaped MTP head at M decode rows: the
 fc / q|k|v (grouped) / o W4A16 GEMVs, the routed MoE FFN (256 NVFP4
 experts, top-8) and the full-vocabulary (151936 x 2048) NVFP4 LM head fused
-with argmax, whose last workgroup gathers the draft token's embedding into
-the next step's fc input (device-resident chaining).  The step is captured
+with argmax, whose draft ids stay on the device: the next step's fc reads
+the embedding row of each id itself (device-resident chaining).  The step is captured
 in a HIP graph and replayed in rotation over NCOPIES independent copies of
 every weight (5.5 GB, 21x the 256 MB Infinity Cache), each step with its own
 router logits, so the weights stream from HBM as in serving.  The headline
@@ -210,22 +210,25 @@ def draft_step(env, copies, lm_pool, embed_table, M, steps, warmup):
     out_max = torch.empty(M, dtype=torch.float32, device=dev)
     draft_log = torch.zeros(NCOPIES * M, dtype=torch.int32, device=dev)
 
+    hfc = env.randn((M, H))   # the hidden-state half of the fc input rows
+
     def step(c):
         ws = copies[c]
-        nv.w4a16_gemv(xs["fc"], ws["fc"], out=ys["fc"])
+        # fc over [embedding of the previous step's draft token | hidden state]:
+        # the GEMV reads the embedding row by the id the LM head wrote
+        prev = draft_log[((c - 1) % NCOPIES) * M:((c - 1) % NCOPIES + 1) * M]
+        nv.w4a16_gemv_embed(prev, embed_table, hfc, ws["fc"], out=ys["fc"])
         nv.w4a16_gemv_grouped(xs["q"], [ws["q"], ws["k"], ws["v"]], outs=[ys["q"], ys["k"], ys["v"]])
         nv.w4a16_gemv(xs["o"], ws["o"], out=ys["o"])
         nv.moe_w4a16_gemv(xm, routers[c], TOPK, ws["moe"], workspace=moe_ws, out=ymoe, topk_ids=ids, topk_w=wts)
-        # the LM head's last workgroup gathers the draft token's embedding
-        # into the next step's fc input and logs the id
-        nv.lmhead_gemv_argmax_embed(hl, lm_pool[c], embed_table, xs["fc"][:, :H], vocab_rows=VOCAB,
-                                    id_log=draft_log[c * M:(c + 1) * M], workspace=lm_ws, out_idx=out_idx,
-                                    out_max=out_max)
+        # the draft ids stay on the device: the next step's fc reads them
+        nv.lmhead_gemv_argmax(hl, lm_pool[c], vocab_rows=VOCAB, workspace=lm_ws,
+                              out_idx=draft_log[c * M:(c + 1) * M], out_max=out_max)
 
     nd = distinct_experts(nv, torch, xm, routers, copies[0]["moe"], moe_ws, M)
     gemv_b = sum(nvfp4_bytes(n, k) + M * n * 4 for name, n, k in PROJ) + M * 2 * (4096 + 2048 + 4096)
     lm_b = nvfp4_bytes(VOCAB, H) + M * H * 2 + M * 8
-    emb_b = M * (4 + 2 * H * 2)            # draft id in, embedding row read and written
+    emb_b = M * 4                          # the draft id the fc reads (its embedding row is in gemv_b)
     step_b = gemv_b + float(np.mean([moe_bytes(n, M) for n in nd])) + lm_b + emb_b
 
     s = env.s
@@ -751,7 +754,7 @@ def main():
                    "proj": {n: [r_, c_] for n, r_, c_ in PROJ}, "moe": {"experts": E, "top_k": TOPK, "inter": I},
                    "lm_head": [VOCAB, H], "weight_copies_rotated": NCOPIES, "weight_bytes_allocated": int(rot_b),
                    "graph": f"{NCOPIES} steps per graph, each its own weight copy and router logits",
-                   "chained": "the LM head gathers the draft token's embedding into the next step's fc input"},
+                   "chained": "the next step's fc reads the embedding row of the draft id the LM head wrote"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": round(r1["step_bytes"]),
         "drafts_per_s": round(1 / (lm_ms * 1e-3), 1),

@@ -314,6 +314,29 @@ int lmhead_gemv_argmax_embed(const uint16_t *h_bf16, int32_t m, const nvfp4_weig
                              void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * w4a16_gemv_embed -- w4a16_gemv whose activation rows begin with the
+ * embedding rows of the tokens in idx, read by the GEMV itself: the next
+ * draft step's fc over [embed(draft token) | hidden state] with the gather of
+ * embed_from_argmax ([mtp_head.rs] `MtpHead` fields; [v4_mtp.rs] `propose`
+ * feeds each draft into the next step) folded into its activation loads, so
+ * the embedding row is fetched while the weights stream and no kernel
+ * writes it.  Activation row i, element kk: table[idx[i]][kk] for kk <
+ * hidden (a zero row for an id outside [0, table_vocab)), x_rest[i][kk -
+ * hidden] for kk >= hidden.
+ *   idx          device int32 [m] (e.g. out_idx of lmhead_gemv_argmax).
+ *   table_bf16   device bf16 [table_vocab][hidden], 16-byte aligned;
+ *                hidden a positive multiple of 32, at most w->k.
+ *   x_rest_bf16  device bf16 [m][w->k - hidden], 16-byte aligned (NULL
+ *                when hidden == w->k).
+ *   m, w, y, y_dtype, stream, the kernels and the other errors as
+ *                w4a16_gemv; the result equals w4a16_gemv of the
+ *                concatenated rows bit for bit.
+ */
+int w4a16_gemv_embed(const int32_t *idx, const uint16_t *table_bf16, int32_t table_vocab,
+                     int32_t hidden, const uint16_t *x_rest_bf16, int32_t m, const nvfp4_weight *w,
+                     void *y, int32_t y_dtype, void *stream);
+
+/*
  * moe_w4a16_gemv -- routed-expert MoE FFN for decode rows: the
  * `moe_topk_softmax` -> `moe_silu_mul` -> weighted-sum chain named in
  * [new.rs] `MtpHead::new`, on NVFP4 experts.

@@ -77,6 +77,7 @@ def lib():
         L.lmhead_gemv_argmax_logprob.argtypes = [P, i32, WP, i32, P, P, P, P, sz, u32, P]
         L.lmhead_gemv_argmax_masked.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, sz, u32, P]
         L.embed_from_argmax.argtypes = [P, i32, P, i32, i32, P, ctypes.c_int64, P, P]
+        L.w4a16_gemv_embed.argtypes = [P, P, i32, i32, P, i32, WP, P, i32, P]
         L.lmhead_gemv_argmax_embed.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, i32, i32, P, ctypes.c_int64, P,
                                                P, sz, u32, P]
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
@@ -90,6 +91,7 @@ def lib():
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
                   "lmhead_gemv_argmax_noalloc",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
+                  "w4a16_gemv_embed",
                   "moe_w4a16_gemv", "moe_layer_w4a16", "moe_workspace_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -209,6 +211,32 @@ def w4a16_gemv(x: torch.Tensor, w: NVFP4Weight, out_dtype=torch.float32, out: to
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     d = w.desc()
     _check(lib().w4a16_gemv(_ptr(x), m, ctypes.byref(d), _ptr(out), _out_code(out.dtype), _stream(x)), "w4a16_gemv")
+    return out
+
+
+def w4a16_gemv_embed(idx: torch.Tensor, table: torch.Tensor, x_rest: torch.Tensor | None, w: NVFP4Weight,
+                     out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """w4a16_gemv over rows [table[idx[i]] | x_rest[i]]: the embedding rows
+    of the tokens in idx (int32, e.g. the LM head's out_idx; zero rows for
+    ids outside the table) are read by the GEMV itself."""
+    _dev(idx, "idx")
+    _dev(table, "table")
+    if table.dtype != torch.bfloat16 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("table must be a contiguous bf16 [vocab][hidden] tensor")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 tensor")
+    m = idx.numel()
+    vocab, hidden = table.shape
+    if x_rest is not None:
+        x_rest = _as_bf16(x_rest)
+        _dev(x_rest, "x_rest")
+        if x_rest.shape != (m, w.k - hidden):
+            raise ValueError(f"x_rest must be [{m}][{w.k - hidden}]")
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype, device=table.device)
+    d = w.desc()
+    _check(lib().w4a16_gemv_embed(_ptr(idx), _ptr(table), vocab, hidden, _ptr(x_rest), m, ctypes.byref(d), _ptr(out),
+                                  _out_code(out.dtype), _stream(table)), "w4a16_gemv_embed")
     return out
 
 

@@ -42,8 +42,8 @@ constexpr int kGemvPipe = 4;
 template <int R>
 constexpr int gemv_pipe() { return R >= kGemvPipe ? 1 : kGemvPipe / R; }
 
-template <int MT, int R, int KS, int CPL, int NW = 4>
-__global__ __launch_bounds__(64 * NW) void k_gemv(const uint16_t *__restrict__ x, int m_rt, const GemvGroups grp, int k,
+template <int MT, int R, int KS, int CPL, int NW = 4, bool XG = false>
+__global__ __launch_bounds__(64 * NW) void k_gemv(const XRows x, int m_rt, const GemvGroups grp, int k,
                                              int bf16out) {
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
@@ -78,20 +78,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemv(const uint16_t *__restrict__ x
         else
             reinterpret_cast<float *>(y)[(size_t)mm * n + row] = o;
     };
+    // gathered rows: their table rows first (the row addresses wait for them)
+    int lid = 0;
+    if constexpr (XG) lid = xids_issue(x, m_rt);
     if constexpr (MT == 1 && CPL > 0) {
         TileRegs<MT, R, KS, CPL> t;
         gemv_tile_load(t, codes, scales, n, k, row0);
         XRegs<CPL> xr;
-        load_xregs<KS, CPL>(xr, x);
+        load_xregs<KS, CPL, XG>(xr, x, k, lid);
         gemv_tile_compute_x1(t, xr, n, row0, red, epi);
     } else if constexpr (CPL > 0) {
         TileRegs<MT, R, KS, CPL> t;
         gemv_tile_load(t, codes, scales, n, k, row0);   // weight loads in flight while x is staged
-        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        stage_x<MT, XG>(xs, x, m_rt, k, lid);
         __syncthreads();
         gemv_tile_compute(t, xs, n, k, row0, red, epi);
     } else {
-        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        stage_x<MT, XG>(xs, x, m_rt, k, lid);
         __syncthreads();
         gemv_tile_loop<MT, R, KS, gemv_pipe<R>(), false, (NW > 4)>(xs, codes, scales, n, k, row0, red, epi);
     }
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             mcur = load_mask(u);
         }
         XRegs<CPL> xr;
-        load_xregs<1, CPL>(xr, x);
+        load_xregs<1, CPL, false>(xr, xrows_plain(x), k);
         __syncthreads();
         int qn = lm_draw<NW>(&s_q, lane);
         while (u < nunits) {
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             gemv_tile_load<MT, R, 1, CPL, true>(cur, codes, scales, v, k, u * rows);
             mcur = load_mask(u);
         }
-        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        stage_x<MT, false>(xs, xrows_plain(x), m_rt, k);
         __syncthreads();
         int qn = lm_draw<NW>(&s_q, lane);
         while (u < nunits) {
@@ -522,7 +525,7 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             u = un;
         }
     } else {
-        stage_x(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        stage_x<MT, false>(xs, xrows_plain(x), m_rt, k);
         __syncthreads();
         int q = wave, qn = lm_draw<NW>(&s_q, lane);
         for (int u = b0 + G * q; u < nunits; u = b0 + G * q) {
@@ -696,8 +699,8 @@ constexpr int kMfSliceK = 128 * kMfSliceSteps;          // 1024
 constexpr int kMfMaxSlices = 8;                         // K <= 8192
 constexpr long kMfSplitMaxUnits = 1024;                 // 16-row units (4096 at four rows)
 
-template <int MT>
-__global__ __launch_bounds__(64 * kMfMaxSlices) void k_gemv_mf(const uint16_t *__restrict__ x, int m_rt,
+template <int MT, bool XG = false>
+__global__ __launch_bounds__(64 * kMfMaxSlices) void k_gemv_mf(const XRows x, int m_rt,
                                                                const GemvGroups grp, int k, int bf16out) {
     extern __shared__ uint4 smem[];
     const int tile = blockIdx.x;
@@ -729,21 +732,46 @@ __global__ __launch_bounds__(64 * kMfMaxSlices) void k_gemv_mf(const uint16_t *_
     const uint16_t *sst = reinterpret_cast<const uint16_t *>(cst + 128);            // scale line, 1 KiB
     // the slice's activations (2 MT chunks a lane), then the weights, all in
     // flight together; the activation stores wait for the activations only
+    // (a lane's unit j lies in activation row j / 2: 128 chunks a row)
     constexpr int XU = 2 * MT;
-    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-    const int cpr = k >> 3;
+    static_assert(kSliceChunks == 128, "two units a row per lane");
     uint4 xv[XU];
+    if constexpr (!XG) {
+        const uint4 *xg = reinterpret_cast<const uint4 *>(x.x);
+        const int cpr = k >> 3;
 #pragma unroll
-    for (int j = 0; j < XU; ++j) {
-        const int p = lane + 64 * j, m = p / kSliceChunks, c = p % kSliceChunks;
-        xv[j] = m < m_rt ? xg[(size_t)m * cpr + kSliceChunks * ks + c] : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < XU; ++j) {
+            const int p = lane + 64 * j, m = p / kSliceChunks, c = p % kSliceChunks;
+            xv[j] = m < m_rt ? xg[(size_t)m * cpr + kSliceChunks * ks + c] : make_uint4(0, 0, 0, 0);
+        }
     }
+    int lid = 0;
+    if constexpr (XG) lid = xids_issue(x, m_rt);   // before the weights: see below
     const MfLines ln = mf_lines(codes, scales, n, k, row0, lane);
     const uint4 sv = ld_l2_16(ln.sp + 8 * (size_t)s0);   // the slices of a line share it
     uint4 cw[kMfSliceSteps];
 #pragma unroll
     for (int d = 0; d < kMfSliceSteps; ++d)
         cw[d] = ld_stream16((d & 1 ? ln.cb : ln.ca) + 64 * (size_t)s0 + 128 * (d >> 1));
+    if constexpr (XG) {
+        __builtin_amdgcn_sched_barrier(0);
+        // gathered rows: their addresses wait for the table rows, so the
+        // weights go first (rows from m_rt on load row m_rt - 1 and are masked)
+        XRow g[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) g[m] = xrow(x, m < m_rt ? m : m_rt - 1, k, lid);
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+            const int c = (lane + 64 * j) % kSliceChunks;
+            xv[j] = *reinterpret_cast<const uint4 *>(xrow_addr(g[j / 2], 8 * (kSliceChunks * ks + c), x.kt));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+            const int m = j / 2, c = (lane + 64 * j) % kSliceChunks;
+            xv[j] = xmask(xv[j], m >= m_rt || xrow_zero(g[m], 8 * (kSliceChunks * ks + c), x.kt));
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < XU; ++j) {
@@ -838,8 +866,13 @@ static TileChoice canonical(TileChoice tc) {
 }
 
 template <int MT, int R, int KS, int CPL, int NW = 4>
-static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const uint16_t *x, int m, const GemvGroups &grp,
+static void launch_gemv_cfg(dim3 grid, size_t lds, hipStream_t s, const XRows &x, int m, const GemvGroups &grp,
                             int k, int bf16) {
+    if (x.kt > 0) {   // the activation rows begin with gathered embedding rows
+        if (allow_lds(reinterpret_cast<const void *>(k_gemv<MT, R, KS, CPL, NW, true>), lds, "w4a16_gemv")) return;
+        hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL, NW, true>), grid, dim3(64 * NW), lds, s, x, m, grp, k, bf16);
+        return;
+    }
     if (allow_lds(reinterpret_cast<const void *>(k_gemv<MT, R, KS, CPL, NW>), lds, "w4a16_gemv")) return;
     hipLaunchKernelGGL((k_gemv<MT, R, KS, CPL, NW>), grid, dim3(64 * NW), lds, s, x, m, grp, k, bf16);
 }
@@ -857,7 +890,7 @@ constexpr int kGemvTilesPerCuM4 = 2;
 // One launch over `count` weights with a common K (their tiles concatenated);
 // the tile shape is chosen for the total row count.
 template <int MT>
-static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16);
+static bool launch_gemv_persist(hipStream_t s, const XRows &x, int m, const nvfp4_weight *w, void *y, int bf16);
 
 // An activation image that leaves LDS for at most three workgroups a CU (a
 // quarter of it or more) caps the per-tile grid at 4 to 12 wavefronts a CU,
@@ -874,7 +907,7 @@ static TileChoice wide_tile(TileChoice tc, int mt, int k) {
 }
 
 template <int MT>
-static int launch_gemv_mf(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
+static int launch_gemv_mf(const XRows &x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
                           hipStream_t s) {
     const int k = w[0]->k;
     GemvGroups grp{};
@@ -893,14 +926,19 @@ static int launch_gemv_mf(const uint16_t *x, int m, const nvfp4_weight *const *w
     if (tiles == 0) return ok();
     const int nks = k / kMfSliceK;
     const size_t lds = gemv_mf_lds(MT, k);
-    const int rc = allow_lds(reinterpret_cast<const void *>(k_gemv_mf<MT>), lds, "w4a16_gemv");
+    const void *kern = x.kt > 0 ? reinterpret_cast<const void *>(k_gemv_mf<MT, true>)
+                                : reinterpret_cast<const void *>(k_gemv_mf<MT, false>);
+    const int rc = allow_lds(kern, lds, "w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL(k_gemv_mf<MT>, dim3(tiles), dim3(64 * nks), lds, s, x, m, grp, k, bf16);
+    if (x.kt > 0)
+        hipLaunchKernelGGL((k_gemv_mf<MT, true>), dim3(tiles), dim3(64 * nks), lds, s, x, m, grp, k, bf16);
+    else
+        hipLaunchKernelGGL((k_gemv_mf<MT, false>), dim3(tiles), dim3(64 * nks), lds, s, x, m, grp, k, bf16);
     return check_launch("w4a16_gemv");
 }
 
 template <int MT>
-static int launch_gemv_m(const uint16_t *x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
+static int launch_gemv_m(const XRows &x, int m, const nvfp4_weight *const *w, void *const *y, int count, int bf16,
                          hipStream_t s) {
     const int k = w[0]->k;
     if constexpr (MT >= 4) {
@@ -992,7 +1030,7 @@ static int launch_lm_variant(bool bk, bool lp, size_t lds, hipStream_t s, const 
 constexpr int kPersistUnits = 2;
 
 template <int MT, int CPL, bool MF>
-static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y,
+static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const XRows &x, int m, const nvfp4_weight *w, void *y,
                                   int bf16) {
     constexpr int NW = MF ? kLmMfWaves : lm_waves<MT, CPL>();
     constexpr int rows = MF ? 16 : 4 * lm_rows_per_slot<MT>();
@@ -1001,13 +1039,14 @@ static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const uint16_t *x, 
     const long units = (w->n + rows - 1) / rows, waves = (long)num_cus() * per_cu * NW;
     if (per_cu < 1 || (MF ? 4 * units < waves : units < kPersistUnits * waves)) return false;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "w4a16_gemv")) return false;
-    hipLaunchKernelGGL(kern, dim3(num_cus() * per_cu), dim3(64 * NW), lds, s, x, m, w->codes, w->scales, w->global,
+    hipLaunchKernelGGL(kern, dim3(num_cus() * per_cu), dim3(64 * NW), lds, s, x.x, m, w->codes, w->scales, w->global,
                        w->n, w->k, nullptr, nullptr, nullptr, nullptr, nullptr, 0, EmbedOut{}, y, bf16);
     return true;
 }
 
 template <int MT>
-static bool launch_gemv_persist(hipStream_t s, const uint16_t *x, int m, const nvfp4_weight *w, void *y, int bf16) {
+static bool launch_gemv_persist(hipStream_t s, const XRows &x, int m, const nvfp4_weight *w, void *y, int bf16) {
+    if (x.kt > 0) return false;   // gathered rows: the per-tile grid
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     if (lds > kMaxLds) return false;
@@ -1050,7 +1089,7 @@ static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int 
 
 using namespace nvfp4;
 
-static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *const *w, void *const *y, int count,
+static int gemv_common(const XRows &x, int32_t m, const nvfp4_weight *const *w, void *const *y, int count,
                        int32_t y_dtype, void *stream, const char *who) {
     if (count < 1 || count > kMaxGroups) return fail(NVFP4_ERR_ARG, "%s: count=%d outside 1..%d", who, count, kMaxGroups);
     if (!w) return fail(NVFP4_ERR_ARG, "%s: NULL weight list", who);
@@ -1068,9 +1107,10 @@ static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
         total_n += w[i]->n;
     }
     if (total_n == 0) return ok();   // empty outputs: nothing to read or write
-    if (!x_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL x", who);
-    if (!aligned(x_bf16, 16)) return fail(NVFP4_ERR_ALIGN, "%s: x not 16-byte aligned", who);
     const int k = w[0]->k;
+    if (x.kt > k) return fail(NVFP4_ERR_SHAPE, "%s: gathered prefix of %d elements exceeds k=%d", who, x.kt, k);
+    if (x.kt < k && !x.x) return fail(NVFP4_ERR_ARG, "%s: NULL x", who);
+    if (!aligned(x.x, 16)) return fail(NVFP4_ERR_ALIGN, "%s: x not 16-byte aligned", who);
     if ((size_t)k * 2 > kMaxLds)
         return fail(NVFP4_ERR_UNSUPPORTED, "%s: one activation row of k=%d exceeds the LDS", who, k);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1084,7 +1124,9 @@ static int gemv_common(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *co
         void *yg[kMaxGroups];
         for (int i = 0; i < count; ++i)
             yg[i] = w[i]->n > 0 ? static_cast<char *>(y[i]) + (size_t)r0 * w[i]->n * (bf16 ? 2 : 4) : nullptr;
-        const uint16_t *xg = x_bf16 + (size_t)r0 * k;
+        XRows xg = x;
+        if (xg.x) xg.x += (size_t)r0 * (k - x.kt);
+        if (xg.idx) xg.idx += r0;
         int rc;
         switch (round_up_mt(mg)) {
             case 1: rc = launch_gemv_m<1>(xg, mg, w, yg, count, bf16, s); break;
@@ -1101,12 +1143,28 @@ extern "C" int w4a16_gemv(const uint16_t *x_bf16, int32_t m, const nvfp4_weight 
                           void *stream) {
     const nvfp4_weight *ws[1] = {w};
     void *ys[1] = {y};
-    return gemv_common(x_bf16, m, ws, ys, 1, y_dtype, stream, "w4a16_gemv");
+    return gemv_common(xrows_plain(x_bf16), m, ws, ys, 1, y_dtype, stream, "w4a16_gemv");
 }
 
 extern "C" int w4a16_gemv_grouped(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *const *w, void *const *y,
                                   int32_t count, int32_t y_dtype, void *stream) {
-    return gemv_common(x_bf16, m, w, y, count, y_dtype, stream, "w4a16_gemv_grouped");
+    return gemv_common(xrows_plain(x_bf16), m, w, y, count, y_dtype, stream, "w4a16_gemv_grouped");
+}
+
+extern "C" int w4a16_gemv_embed(const int32_t *idx, const uint16_t *table_bf16, int32_t table_vocab, int32_t hidden,
+                                const uint16_t *x_rest_bf16, int32_t m, const nvfp4_weight *w, void *y,
+                                int32_t y_dtype, void *stream) {
+    const char *who = "w4a16_gemv_embed";
+    if (!idx || !table_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL idx or table", who);
+    if (table_vocab < 1 || hidden < 32 || hidden % 32)
+        return fail(NVFP4_ERR_SHAPE, "%s: need table_vocab >= 1 and hidden a positive multiple of 32 (vocab=%d "
+                    "hidden=%d)", who, table_vocab, hidden);
+    if (!aligned(table_bf16, 16) || !aligned(idx, 4))
+        return fail(NVFP4_ERR_ALIGN, "%s: table needs 16-byte, idx 4-byte alignment", who);
+    const nvfp4_weight *ws[1] = {w};
+    void *ys[1] = {y};
+    const XRows x{x_rest_bf16, idx, table_bf16, table_vocab, hidden};
+    return gemv_common(x, m, ws, ys, 1, y_dtype, stream, who);
 }
 
 extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows) {

@@ -83,19 +83,110 @@ __device__ __forceinline__ void stage_batched(int units, int tid, int nthreads, 
     }
 }
 
+// The activation rows of a call.  Row mm, element kk: x[mm][kk] for a plain
+// call (kt = 0); with a gathered prefix (the next draft step's fc input, its
+// first kt elements the embedding row of the token the LM head chose),
+// element kk < kt of table row idx[mm] (a zero row for an id outside
+// [0, vocab)) and element kk >= kt of x[mm][kk - kt] (rows of k - kt
+// elements).  kt % 32 == 0.
+struct XRows {
+    const uint16_t *x;
+    const int32_t *idx;
+    const uint16_t *table;
+    int vocab, kt;
+};
+__host__ __device__ inline XRows xrows_plain(const uint16_t *x) { return XRows{x, nullptr, nullptr, 0, 0}; }
+
+// The table rows of the first (up to 64) activation rows: lane l loads
+// idx[min(l, m_rt - 1)].  Issued before the weights, it is the first vector
+// load to return, so waiting for it does not wait for them.
+__device__ __forceinline__ int xids_issue(const XRows &xr, int m_rt) {
+    const int lane = threadIdx.x & 63;
+    const int v = xr.idx[lane < m_rt ? lane : m_rt - 1];
+    __builtin_amdgcn_sched_barrier(0);
+    return v;
+}
+// One gathered activation row, wavefront-uniform: its table row (row 0 for
+// an id outside the table, then read as zeros) and the rest of its elements.
+// lid: xids_issue()'s value; m < 64.
+struct XRow {
+    const uint16_t *t;   // table row
+    const uint16_t *r;   // elements kt .. k-1
+    bool z;              // the prefix reads as zeros
+};
+__device__ __forceinline__ XRow xrow(const XRows &xr, int m, int k, int lid) {
+    const int id = __builtin_amdgcn_readlane(lid, m);
+    XRow g;
+    g.z = (unsigned int)id >= (unsigned int)xr.vocab;
+    g.t = xr.table + (size_t)(g.z ? 0 : id) * xr.kt;
+    g.r = xr.x + (size_t)m * (k - xr.kt);
+    return g;
+}
+// Address of elements [kk, ...) of a gathered row, within one 32-element
+// chunk (kt % 32 == 0, so a chunk lies wholly in the prefix or wholly after
+// it), and whether that chunk reads as zeros.
+__device__ __forceinline__ const uint16_t *xrow_addr(const XRow &g, int kk, int kt) {
+    return kk < kt ? g.t + kk : g.r + (kk - kt);
+}
+__device__ __forceinline__ bool xrow_zero(const XRow &g, int kk, int kt) { return kk < kt && g.z; }
+// The loads are unconditional (their addresses are always valid) and a zero
+// chunk is masked where the value is first used, after the batch of loads
+// has been issued: masking at the load made every load wait for the one
+// before it.
+__device__ __forceinline__ uint4 xmask(uint4 v, bool zero) {
+    const uint32_t keep = zero ? 0u : ~0u;
+    return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+}
+// Addresses of row mm (per lane) among the first MT gathered rows (a select
+// chain; the zero flag is not picked).
+template <int MT>
+__device__ __forceinline__ XRow xrow_pick(const XRow (&g)[MT], int mm) {
+    XRow o = g[0];
+#pragma unroll
+    for (int m = 1; m < MT; ++m) {
+        o.t = mm == m ? g[m].t : o.t;
+        o.r = mm == m ? g[m].r : o.r;
+    }
+    return o;
+}
+
 // LDS image of x: 16-byte units, unit (m, q, c) = x[m][32c + 8q .. 32c + 8q + 8)
 // at index (m * 4 + q) * C + c, so that the 16 lanes of a slot reading
 // consecutive chunks hit consecutive LDS addresses.  Rows m_rt .. MT-1 are
 // zero-filled (the kernel is instantiated for MT >= m_rt rows).
-__device__ __forceinline__ void stage_x(uint4 *xs, const uint4 *__restrict__ x, int m_rt, int mt, int k) {
+template <int MT, bool XG>
+__device__ __forceinline__ void stage_x(uint4 *xs, const XRows &xr, int m_rt, int k, int lid = 0) {
+    static_assert(MT <= 8, "up to 8 activation rows");
     const int C = k >> 5, upr = k >> 3;
-    stage_batched(
-        mt * upr, threadIdx.x, blockDim.x,
-        [&](int p) { return p / upr < m_rt ? x[p] : make_uint4(0, 0, 0, 0); },
-        [&](int p, uint4 v) {
-            const int mm = p / upr, w = p - mm * upr;
-            xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = v;
-        });
+    auto put = [&](int p, uint4 v) {
+        const int mm = p / upr, w = p - mm * upr;
+        xs[(mm * 4 + (w & 3)) * C + (w >> 2)] = v;
+    };
+    if constexpr (!XG) {
+        const uint4 *x = reinterpret_cast<const uint4 *>(xr.x);
+        stage_batched(
+            MT * upr, threadIdx.x, blockDim.x, [&](int p) { return p / upr < m_rt ? x[p] : make_uint4(0, 0, 0, 0); },
+            put);
+    } else {
+        // rows from m_rt on load row m_rt - 1 and are masked
+        XRow g[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) g[m] = xrow(xr, m < m_rt ? m : m_rt - 1, k, lid);
+        uint32_t zrows = 0;   // rows whose prefix reads as zeros, and rows from m_rt on
+#pragma unroll
+        for (int m = 0; m < MT; ++m) zrows |= (m >= m_rt || g[m].z) ? 1u << m : 0u;
+        stage_batched(
+            MT * upr, threadIdx.x, blockDim.x,
+            [&](int p) {
+                const int mm = p / upr;
+                return *reinterpret_cast<const uint4 *>(xrow_addr(xrow_pick<MT>(g, mm), 8 * (p - mm * upr), xr.kt));
+            },
+            [&](int p, uint4 v) {
+                const int mm = p / upr;
+                const int kk = 8 * (p - mm * upr);
+                put(p, xmask(v, mm >= m_rt || (kk < xr.kt && ((zrows >> mm) & 1u))));
+            });
+    }
 }
 
 template <int R, int KS, int NW = 4>
@@ -255,15 +346,18 @@ struct XRegs {
     uint32_t w[CPL][16];
 };
 
-template <int KS, int CPL>
-__device__ __forceinline__ void load_xregs(XRegs<CPL> &xr, const uint16_t *__restrict__ x) {
+template <int KS, int CPL, bool XG>
+__device__ __forceinline__ void load_xregs(XRegs<CPL> &xr, const XRows &x, int k, int lid = 0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tl = lane & 15;
     const int ks = (KS == 1) ? 0 : (wave % KS);
     const int c_lo = ks * 16 * CPL;
+    XRow g{};
+    if constexpr (XG) g = xrow(x, 0, k, lid);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(x + 32 * (c_lo + tl + 16 * j));
+        const int kk = 32 * (c_lo + tl + 16 * j);
+        const uint4 *p = reinterpret_cast<const uint4 *>(XG ? xrow_addr(g, kk, x.kt) : x.x + kk);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 u = p[q];
@@ -271,6 +365,14 @@ __device__ __forceinline__ void load_xregs(XRegs<CPL> &xr, const uint16_t *__res
             xr.w[j][4 * q + 1] = u.y;
             xr.w[j][4 * q + 2] = u.z;
             xr.w[j][4 * q + 3] = u.w;
+        }
+    }
+    if constexpr (XG) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const uint32_t keep = xrow_zero(g, 32 * (c_lo + tl + 16 * j), x.kt) ? 0u : ~0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xr.w[j][i] &= keep;
         }
     }
 }

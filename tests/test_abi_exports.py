@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax", "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed", "moe_w4a16_gemv", "moe_layer_w4a16",
+    for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax", "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed", "w4a16_gemv_embed", "moe_w4a16_gemv", "moe_layer_w4a16",
               "moe_workspace_status", "lmhead_gemv_argmax_noalloc", "lmhead_gemv_argmax_workspace_bytes", "moe_w4a16_gemv_workspace_bytes", "w4a16_gemm_m128_workspace_bytes",
               "nvfp4_mtp_last_error"):
         assert f in names, f
@@ -44,6 +44,10 @@ def test_argument_errors_need_no_gpu():
     assert L.nvfp4_quantize(ctypes.c_void_p(16), 4, 48, ctypes.c_void_p(16), ctypes.c_void_p(16),
                             ctypes.c_void_p(16), None) == -2
     assert L.lmhead_gemv_argmax_workspace_bytes(8, 151936) >= 8 * 16
+    ok_ptr = ctypes.c_void_p(256)
+    assert L.w4a16_gemv_embed(None, ok_ptr, 10, 32, ok_ptr, 1, ctypes.byref(w), ok_ptr, 0, None) == -1
+    assert L.w4a16_gemv_embed(ok_ptr, ok_ptr, 10, 40, ok_ptr, 1, ctypes.byref(w), ok_ptr, 0, None) == -2
+    assert b"hidden" in L.nvfp4_mtp_last_error()
     st = ctypes.c_uint32(7)
     assert L.moe_workspace_status(None, 1 << 20, ctypes.byref(st), None) == -1
     assert L.moe_workspace_status(ctypes.c_void_p(256), 64, ctypes.byref(st), None) == -4

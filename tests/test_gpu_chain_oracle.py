@@ -13,8 +13,11 @@ largest scale), computed on the oracle's chain, so every step's winner is
 certified by a margin far above the fp32 bound; the GPU's draft-id log must
 equal the oracle's exactly, each gathered row must equal the oracle's gather
 bit for bit, and each step's fc output must be within one bf16 ulp of the
-oracle's GEMV of the GPU's own input row (plus the fp32 bound).  Eager calls, the fused
-argmax + gather and a HIP graph of the whole chain are checked."""
+oracle's GEMV of the GPU's own input row (plus the fp32 bound).  Three ways
+of chaining are checked: argmax then embed_from_argmax, the argmax with the
+gather fused into its last workgroup, and the argmax followed by an fc that
+gathers the embedding row itself (w4a16_gemv_embed); eagerly and as a HIP
+graph of the whole chain."""
 import numpy as np
 import pytest
 import torch
@@ -116,49 +119,60 @@ def test_chain_matches_oracle(orc, m):
     log = torch.zeros((STEPS, m), dtype=torch.int32, device="cuda")
     xlog = torch.empty((STEPS, m, 2 * H), dtype=torch.bfloat16, device="cuda")
     hlog = torch.empty((STEPS, m, H), dtype=torch.bfloat16, device="cuda")
+    hprev = torch.empty((STEPS, m, H), dtype=torch.bfloat16, device="cuda")
 
     h0_d = dev_bf16(h0)
 
-    def chain(fused):
+    def chain(mode):
         hcur.copy_(h0_d)
         for j in range(STEPS):
-            if fused:
-                nv.lmhead_gemv_argmax_embed(hcur, lm_d, table_d, xin[:, :H], id_log=log[j], workspace=ws,
-                                            out_idx=idx, out_max=mx)
+            hprev[j].copy_(hcur)
+            if mode == "consumer":
+                # the argmax writes the id log; the fc reads the embedding row itself
+                nv.lmhead_gemv_argmax(hcur, lm_d, workspace=ws, out_idx=log[j], out_max=mx)
+                nv.w4a16_gemv_embed(log[j], table_d, hprev[j], fc_d, out=hcur, out_dtype=torch.bfloat16)
             else:
-                nv.lmhead_gemv_argmax(hcur, lm_d, workspace=ws, out_idx=idx, out_max=mx)
-                nv.embed_from_argmax(idx, table_d, out=xin[:, :H], id_log=log[j])
-            xin[:, H:].copy_(hcur)
-            xlog[j].copy_(xin)
-            nv.w4a16_gemv(xin, fc_d, out=hcur, out_dtype=torch.bfloat16)
+                if mode == "fused":
+                    nv.lmhead_gemv_argmax_embed(hcur, lm_d, table_d, xin[:, :H], id_log=log[j], workspace=ws,
+                                                out_idx=idx, out_max=mx)
+                else:
+                    nv.lmhead_gemv_argmax(hcur, lm_d, workspace=ws, out_idx=idx, out_max=mx)
+                    nv.embed_from_argmax(idx, table_d, out=xin[:, :H], id_log=log[j])
+                xin[:, H:].copy_(hcur)
+                xlog[j].copy_(xin)
+                nv.w4a16_gemv(xin, fc_d, out=hcur, out_dtype=torch.bfloat16)
             hlog[j].copy_(hcur)
 
-    def check():
+    def check(mode):
         torch.cuda.synchronize()
         ids = log.cpu().numpy()
         assert np.array_equal(ids, ref_ids), (ids, ref_ids)
-        xs = xlog.cpu().view(torch.int16).numpy().view(np.uint16)
         hs = hlog.cpu().view(torch.int16).numpy().view(np.uint16)
+        hp = hprev.cpu().view(torch.int16).numpy().view(np.uint16)
+        xs = xlog.cpu().view(torch.int16).numpy().view(np.uint16)
         for j in range(STEPS):
-            assert np.array_equal(xs[j][:, :H], orc.embed_rows(ids[j], table))     # the gather, bit for bit
-            _fc_within_bound(orc, hs[j], xs[j], fc)                               # the step's fc GEMV
+            x = np.concatenate([orc.embed_rows(ids[j], table), hp[j]], axis=1)   # the oracle's gather
+            if mode != "consumer":
+                assert np.array_equal(xs[j], x)                                     # the GPU's, bit for bit
+            _fc_within_bound(orc, hs[j], x, fc)                                     # the step's fc GEMV
 
-    for fused in (False, True):
+    for mode in ("separate", "fused", "consumer"):
         log.zero_()
-        chain(fused)
-        check()
+        chain(mode)
+        check(mode)
     s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        chain(True)
+    for mode in ("fused", "consumer"):
+        with torch.cuda.stream(s):
+            chain(mode)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                chain(mode)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            chain(True)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        log.zero_()
-        xlog.zero_()
-        g.replay()
-        check()
-        chain(False)                                  # eager work between replays
-        check()
+        for rep in range(3):
+            log.zero_()
+            xlog.zero_()
+            g.replay()
+            check(mode)
+            chain("separate")                             # eager work between replays
+            check("separate")
