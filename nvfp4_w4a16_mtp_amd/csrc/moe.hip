@@ -727,6 +727,38 @@ __device__ __forceinline__ void down_rows_fma(const DownItems &d, int b0, int kS
     }
 }
 
+// down_rows_fma for one register batch when each expert has a single
+// activation row (position u of expert u): the batch's items are computed
+// together in one straight-line block, so that their dot products overlap (a
+// wavefront per SIMD has no other work to hide their latency behind).
+template <int CPL>
+__device__ __forceinline__ void down_rows_fma_one(const DownItems &d, int b0, int kSlots,
+                                                  const uint4 (&cw)[kDownBatch][CPL],
+                                                  const uint32_t (&sw)[kDownBatch][CPL], const float *s_dec,
+                                                  const uint4 *smem, int C, float (*contrib)[kDownRows]) {
+    int itn[kDownBatch];
+    float acc[kDownBatch][1];
+#pragma unroll
+    for (int n = 0; n < kDownBatch; ++n) {
+        itn[n] = b0 + d.sl + kSlots * n;
+        // an item past the end is computed on the last item's rows, not stored
+        const int u = min(itn[n], d.nitems - 1) / kDownRows;
+        acc[n][0] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)u * 4 * C, C, d.tl + 16 * j, acc[n]);
+    }
+    float v[kDownBatch];
+#pragma unroll
+    for (int n = 0; n < kDownBatch; ++n) v[n] = row16_sum(acc[n][0]);
+#pragma unroll
+    for (int n = 0; n < kDownBatch; ++n)
+        if (itn[n] < d.nitems && d.tl == 0) {
+            const int u = itn[n] / kDownRows;
+            contrib[u][itn[n] % kDownRows] = v[n] * s_dec[u];
+        }
+}
+
 // stage_rows in two steps, so that loads issued in between do not delay the
 // image: the first kStageBatch units of each thread into registers, then
 // their stores and the rest of the image.
@@ -899,14 +931,22 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
     }
     __syncthreads();
-    for (int b0 = 0; b0 < nitems; b0 += 2 * kStep) {
-        down_rows_fma<CPL>(it, b0, kSlots, ca, sa, s_pb, s_dec, smem, C, contrib);
-        if (b0 + 2 * kStep < nitems) down_rows_load<CPL>(it, b0 + 2 * kStep, kSlots, ca, sa);
-        __builtin_amdgcn_sched_barrier(0);
-        if (b0 + kStep >= nitems) break;
-        down_rows_fma<CPL>(it, b0 + kStep, kSlots, cb, sb, s_pb, s_dec, smem, C, contrib);
-        if (b0 + 3 * kStep < nitems) down_rows_load<CPL>(it, b0 + 3 * kStep, kSlots, cb, sb);
-        __builtin_amdgcn_sched_barrier(0);
+    if (FUSED && CPL <= 2 && P == nd && nitems <= 2 * kStep) {
+        // one position per expert (position u is expert u's); the separate
+        // pass has four times the wavefronts to overlap its items instead,
+        // and neither it nor wider rows have the registers
+        down_rows_fma_one<CPL>(it, 0, kSlots, ca, sa, s_dec, smem, C, contrib);
+        if (kStep < nitems) down_rows_fma_one<CPL>(it, kStep, kSlots, cb, sb, s_dec, smem, C, contrib);
+    } else {
+        for (int b0 = 0; b0 < nitems; b0 += 2 * kStep) {
+            down_rows_fma<CPL>(it, b0, kSlots, ca, sa, s_pb, s_dec, smem, C, contrib);
+            if (b0 + 2 * kStep < nitems) down_rows_load<CPL>(it, b0 + 2 * kStep, kSlots, ca, sa);
+            __builtin_amdgcn_sched_barrier(0);
+            if (b0 + kStep >= nitems) break;
+            down_rows_fma<CPL>(it, b0 + kStep, kSlots, cb, sb, s_pb, s_dec, smem, C, contrib);
+            if (b0 + 3 * kStep < nitems) down_rows_load<CPL>(it, b0 + 3 * kStep, kSlots, cb, sb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     __syncthreads();
     // y[t][row] = sum over token t's pairs, in ascending expert order, of
@@ -957,7 +997,7 @@ __global__ __launch_bounds__(64 * down_rows_waves<CPL>()) void k_moe_down_rows(n
 // rows each.  The down workgroups come after every gate/up workgroup in
 // dispatch order, so the ones they wait for are already running.
 template <int CPLG, int CPLD>
-__global__ __launch_bounds__(256) void k_moe_fused(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CPLD <= 2 ? 3 : 1))) void k_moe_fused(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                   int m, int E, int topk, nvfp4_moe_weights e,
                                                   int32_t *__restrict__ ids, float *__restrict__ wts,
                                                   uint16_t *__restrict__ act, float *__restrict__ y, MoeShared sh,
