@@ -139,9 +139,10 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Top-k of one token's logits; lane s < topk receives the s-th selection.
+// nsel < topk: only the first nsel selections (the same ones).
 template <int PER>
 __device__ __forceinline__ void route_token(const float *__restrict__ lg, int E, int topk, int lane, float &my_v,
-                                            int &my_i) {
+                                            int &my_i, int nsel = -1) {
     float v[PER];
     int id[PER];
     int rem = 0;
@@ -169,7 +170,8 @@ __device__ __forceinline__ void route_token(const float *__restrict__ lg, int E,
         }
     my_v = -INFINITY;
     my_i = 0;
-    for (int s = 0; s < topk; ++s) {
+    const int ns = nsel < 0 ? topk : nsel;
+    for (int s = 0; s < ns; ++s) {
         const float mx = wave_max(rem > 0 ? v[0] : -INFINITY);
         uint64_t ball = __ballot(rem > 0 && v[0] == mx);
         if (!ball) ball = __ballot(rem > 0);   // only with NaN logits: any untaken expert, never out of range
@@ -271,6 +273,20 @@ __device__ __forceinline__ void moe_route_per(const float *__restrict__ logits, 
     }
     if (threadIdx.x == 0) L.n_distinct = base;
     __syncthreads();
+}
+
+// The expert of the u-th selection of a single token (u < topk), from
+// wavefront 0 after u + 1 selections; valid in every lane of wavefront 0.
+__device__ __forceinline__ int moe_route_nth(const float *__restrict__ logits, int E, int topk, int u) {
+    const int lane = threadIdx.x & 63, per = (E + 63) / 64;
+    float v;
+    int i;
+    if (per <= 1) route_token<1>(logits, E, topk, lane, v, i, u + 1);
+    else if (per <= 2) route_token<2>(logits, E, topk, lane, v, i, u + 1);
+    else if (per <= 4) route_token<4>(logits, E, topk, lane, v, i, u + 1);
+    else if (per <= 8) route_token<8>(logits, E, topk, lane, v, i, u + 1);
+    else route_token<16>(logits, E, topk, lane, v, i, u + 1);
+    return __builtin_amdgcn_readlane(i, u);
 }
 
 __device__ __forceinline__ void moe_route_lds(const float *__restrict__ logits, int m, int E, int topk, RouteLds &L) {
@@ -488,6 +504,21 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
         if (threadIdx.x < 8 && u < route->n_distinct) {
             tok[threadIdx.x] = route->ex[u].tok[threadIdx.x];
             prs[threadIdx.x] = route->ex[u].pair[threadIdx.x];
+        }
+    } else if (FUSED && m == 1) {
+        // one token, one launch: column u takes the u-th selected expert
+        // (pair u), known after u + 1 selections, so that the early columns'
+        // weights start streaming while the later ones still select; a down
+        // workgroup publishes the ids and weights
+        if (threadIdx.x < 64) {
+            const int id = u < topk ? moe_route_nth(logits, E, topk, u) : 0;
+            if (threadIdx.x == 0) {
+                s_nd = topk;
+                s_ex = id;
+                s_cnt = 1;
+                tok[0] = 0;
+                prs[0] = u;
+            }
         }
     } else {
         moe_route_lds(logits, m, E, topk, L);
@@ -798,7 +829,8 @@ template <int CPL, bool FUSED, int NW = 4>
 __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
                                                const MoeRoute *__restrict__ route, const float *__restrict__ logits,
                                                int E, int gx, const uint16_t *__restrict__ act, float *__restrict__ y,
-                                               const MoeShared &sh, unsigned int *done, unsigned int *status) {
+                                               const MoeShared &sh, unsigned int *done, unsigned int *status,
+                                               int32_t *__restrict__ ids = nullptr, float *__restrict__ wts = nullptr) {
     __shared__ int s_ex[kDownMaxExperts], s_pb[kDownMaxExperts + 1];
     __shared__ float s_dec[kDownMaxExperts], s_w[kDownMaxPos];
     __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
@@ -811,6 +843,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     if constexpr (FUSED) {
         RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // the activation image overwrites it later
         moe_route_lds(logits, m, E, topk, L);
+        if (bx == 0 && ids != nullptr) write_route(L, e, m, topk, ids, wts, nullptr);
         const int nr = L.n_distinct;
         for (int q = threadIdx.x; q < nr; q += blockDim.x) {
             s_ex[q] = L.ex[q].expert;
@@ -1009,7 +1042,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CPLD <= 2 ?
         gate_up_role<CPLG, true>(smem, b % gx, b / gx, gx, x, logits, m, E, topk, e, ids, wts, nullptr, act, sh,
                                  counters, (int)gridDim.x - g1);
     else
-        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters, status);
+        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters, status, ids,
+                                   wts);
 }
 
 template <int CPL>
