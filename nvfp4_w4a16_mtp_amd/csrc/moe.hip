@@ -37,19 +37,21 @@ constexpr int kMoeRows = 16;        // rows per workgroup tile (R = 1, KS = 1)
 constexpr int kSpinLimit = 1 << 22;    // polls of the fused down pass's wait (seconds)
 // Hand-off words of the fused launch, each counter on its own 128-byte line:
 // per expert column u a count of its finished gate/up workgroups (word
-// 32 u), a count of finished columns (word 32 * 128), both zero between
-// calls; then per down workgroup i, kGoStride words apart, its go word
-// (+0) and its count of calls (+1).  The go word of down workgroup i holds
-// kGoTag times the number of releases it has received and its count the
-// number of calls it has run, so at the start of its call c (count c) the
-// go word is c kGoTag, or (c + 1) kGoTag once this call's release landed;
-// the release adds kGoTag.  A release left over from an earlier call whose
-// wait gave up has landed before the next launch starts (launches on one
-// workspace are serialized) and only brings the word to c kGoTag, which the
-// next call does not accept; any other value (an overwritten workspace) is
+// 32 u, zero between calls); then per down workgroup i, kGoStride words
+// apart, its go word (+0) and its count (+1).  The workgroup that completes
+// a column adds kGoTag to every down workgroup's go word, so a call releases
+// each of them once per column; the count holds kGoTag times the number of
+// releases the down workgroup expected up to and including its last call.
+// At the start of a call with r columns the go word lies between the count
+// c and c + r kGoTag (the releases of this call that have landed); the call
+// waits for c + r kGoTag and stores that as the new count.  Releases left
+// over from an earlier call whose wait gave up have landed before the next
+// launch starts (launches on one workspace are serialized), so they never
+// count towards a later call; any other value (an overwritten workspace) is
 // reported instead of trusted.
-constexpr int kColStride = 32, kTopWord = 32 * 128, kSyncWords = 32 * 129, kGoStride = 16;
-constexpr unsigned int kGoTag = 0x9E3779B1u;   // odd: c -> c kGoTag is one-to-one mod 2^32
+constexpr int kColStride = 32, kSyncWords = 32 * 128, kGoStride = 16;
+constexpr unsigned int kGoTag = 0x9E3779B1u;      // odd, so multiplying by it is one-to-one mod 2^32
+constexpr unsigned int kGoTagInv = 0x0E8B2F51u;   // its inverse mod 2^32
 // Sticky status of a MoE workspace (bit 0: a down pass gave up its wait;
 // bit 1: it found its go word overwritten), at a fixed offset at the end of
 // the route header; the host reads and clears it with moe_workspace_status.
@@ -550,9 +552,8 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     else if (mt == 4) gate_up_body<4, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     else gate_up_body<8, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     if constexpr (FUSED) {
-        // count this workgroup in its column; the one that completes a column
-        // counts the column, and the one that completes the last column
-        // releases every down workgroup through its own go flag
+        // count this workgroup in its column; the one that completes the
+        // column releases it to every down workgroup through its go word
         __shared__ int s_release;
         wait_mem();   // this workgroup's activations have reached device scope
         __syncthreads();
@@ -560,10 +561,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
             int rel = 0;
             if (atomicAdd(&done[kColStride * u], 1u) == (unsigned int)(gx - 1)) {
                 st_dev(&done[kColStride * u], 0u);
-                if (atomicAdd(&done[kTopWord], 1u) == (unsigned int)(s_nd - 1)) {
-                    st_dev(&done[kTopWord], 0u);
-                    rel = 1;
-                }
+                rel = 1;
             }
             s_release = rel;
         }
@@ -917,16 +915,16 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
         __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x == 0) {
-            // this call's tag; the count of calls is advanced whether
-            // or not the wait succeeds, so a late release of this call
-            // cannot satisfy the next one
+            // one release per routed expert column; the count is advanced
+            // whether or not the wait succeeds, so a late release of this
+            // call cannot satisfy the next one
             unsigned int *go = done + kSyncWords + kGoStride * bx;
             const unsigned int c = ld_dev(go + 1);
-            st_dev(go + 1, c + 1u);
-            const unsigned int want = (c + 1u) * kGoTag;
+            const unsigned int want = c + (unsigned int)nr * kGoTag;
+            st_dev(go + 1, want);
             unsigned int g = ld_dev(go);
             int bad = 0;
-            if (g != want && g != c * kGoTag) {
+            if ((g - c) * kGoTagInv > (unsigned int)nr) {   // not c plus up to nr releases
                 bad = (int)kMoeStatusCorrupt;
             } else {
                 int n = 0;

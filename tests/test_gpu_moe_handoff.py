@@ -1,11 +1,12 @@
 """The one-launch MoE's hand-off between its gate/up and down workgroups.
-Each down workgroup waits for a go word that the gate/up workgroup finishing
-the last expert column advances by a per-call tag; the down workgroup keeps
-its own count of calls.  A release left over from an earlier call (one whose
-wait gave up) must not start a later call's down pass early, and a go word
-holding a value no call writes must be reported through the workspace's
-status word (moe_workspace_status), not trusted.  The workspace words are
-set from the host between ordinary calls; nothing waits for long."""
+Each down workgroup waits for its go word to receive one tagged release per
+routed expert column (added by the gate/up workgroup that completes the
+column) and keeps, next to it, the total it expected up to its last call.  A
+release left over from an earlier call (one whose wait gave up) must not
+start a later call's down pass early, and a go word holding a value no call
+writes must be reported through the workspace's status word
+(moe_workspace_status), not trusted.  The workspace words are set from the
+host between ordinary calls; nothing waits for long."""
 import numpy as np
 import pytest
 import torch
@@ -16,11 +17,18 @@ from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_u8
 pytestmark = pytest.mark.gpu
 
 # Workspace layout of moe_w4a16_gemv (see moe.hip): route header, one ticket
-# word per 16 output rows (256-byte aligned), then the hand-off words: expert
-# column counters, the column total, and per down workgroup (8 output rows)
-# its go word and call count, 16 words apart.
-HEADER, SYNC_WORDS, GO_STRIDE, TAG = 16384, 32 * 129, 16, 0x9E3779B1
+# word per 16 output rows (256-byte aligned), then the hand-off words: 128
+# expert column counters (32 words apart), and per down workgroup (8 output
+# rows) its go word and expected total, 16 words apart.
+HEADER, SYNC_WORDS, GO_STRIDE, TAG = 16384, 32 * 128, 16, 0x9E3779B1
+TOPK = 8
+
+
 E, H, I = 64, 512, 512
+
+
+def _u32(v):
+    return np.uint32(v & 0xFFFFFFFF)
 
 
 def _layout():
@@ -60,15 +68,17 @@ def test_stale_release_does_not_start_a_later_call(orc):
         assert np.array_equal(ids.cpu().numpy(), rids)
         assert_close(y.cpu().numpy(), ry, f"call {call}")
         w = _words(ws)
-        # the one-launch path ran: every down workgroup counted its calls and
-        # received one tagged release per call
-        assert (w[go + 1].cpu().numpy() == call + 1).all()
-        assert (w[go].cpu().numpy().astype(np.uint32) == np.uint32(((call + 1) * TAG) & 0xFFFFFFFF)).all()
-    # a call whose wait gave up (its count advanced) and whose release then
-    # landed late: the next call must wait for its own release
+        # the one-launch path ran: every down workgroup received one tagged
+        # release per expert column of every call, and expected as many
+        done = _u32((call + 1) * TOPK * TAG)
+        assert (w[go + 1].cpu().numpy().astype(np.uint32) == done).all()
+        assert (w[go].cpu().numpy().astype(np.uint32) == done).all()
+    # a call whose wait gave up (its expected total advanced) and whose
+    # releases then landed late: the next call must wait for its own releases
+    late = torch.tensor(np.array([_u32(4 * TOPK * TAG)]).view(np.int32)[0], device="cuda")
     w = _words(ws)
-    w[go + 1] += 1
-    w[go] = torch.tensor(np.array([np.uint32((4 * TAG) & 0xFFFFFFFF)]).view(np.int32)[0], device="cuda")
+    w[go + 1] = late
+    w[go] = late
     torch.cuda.synchronize()
     y, ids, _ = nv.moe_w4a16_gemv(dev_bf16(x), dev_f32(r), 8, dex, workspace=ws)
     assert nv.moe_workspace_status(ws) == 0
