@@ -382,8 +382,6 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
                 mi[r] = row;
             }
         };
-        stage_x_mf(xs, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
-        __syncthreads();
         // the code loads run kLmMfDepth steps ahead (and the scale loads one
         // round of kLmMfDepth steps) as one stream across the wavefront's
         // units (the launch keeps the step count a multiple of the depth);
@@ -394,20 +392,18 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
         uint4 *cst = smem + (size_t)MT * cpr + (size_t)wave * (kMfStageBytes / 16);   // code pair, 2 KiB
         const uint16_t *sst = reinterpret_cast<const uint16_t *>(cst + 128);            // scale round, 1 KiB
         int u = b0 + G * wave;
-        int un = b0 + G * lm_draw<NW>(&s_q, lane);
         MfLines cur = mf_lines(codes, scales, v, k, (u < nunits ? u : 0) * rows, lane);
-        MfLines nxt = mf_lines(codes, scales, v, k, (un < nunits ? un : 0) * rows, lane);
-        const uint4 *xa[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) xa[b] = mf_xrow(xs, cpr, MT, li, q, b);
-        const int ws0 = mf_code_wslot(lane, 0), ws1 = mf_code_wslot(lane, 1);
-        const int rs0 = mf_code_rslot(li, q, 0), rs1 = mf_code_rslot(li, q, 1);
-        // issue order as in the loop (scales, then the code pairs), so that
-        // each wait there only covers what it needs.  A scale load covers
-        // half of each row's 128-byte line (8 steps) and the other half is
-        // read a round later: the scales go through the L2 with the normal
-        // policy, so that the line is still there (streamed like the codes,
-        // the line was fetched twice: 7% more bytes at K = 2048)
+        // the activations, then the first unit's weights, all in flight
+        // before the image is stored (its stores wait for the activations
+        // only).  Issue order as in the loop (scales, then the code pairs),
+        // so that each wait there only covers what it needs.  A scale load
+        // covers half of each row's 128-byte line (8 steps) and the other
+        // half is read a round later: the scales go through the L2 with the
+        // normal policy, so that the line is still there (streamed like the
+        // codes, the line was fetched twice: 7% more bytes at K = 2048)
+        uint4 xv[kStageBatch];
+        stage_x_mf_first(xv, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __builtin_amdgcn_sched_barrier(0);
         uint4 sv = ld_l2_16(cur.sp);
         __builtin_amdgcn_sched_barrier(0);
         uint4 cw[D];
@@ -416,6 +412,15 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             cw[d] = ld_stream16((d & 1 ? cur.cb : cur.ca) + 128 * (d >> 1));
             __builtin_amdgcn_sched_barrier(0);
         }
+        stage_x_mf_rest(xs, xv, reinterpret_cast<const uint4 *>(x), m_rt, MT, k);
+        __syncthreads();
+        int un = b0 + G * lm_draw<NW>(&s_q, lane);
+        MfLines nxt = mf_lines(codes, scales, v, k, (un < nunits ? un : 0) * rows, lane);
+        const uint4 *xa[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xa[b] = mf_xrow(xs, cpr, MT, li, q, b);
+        const int ws0 = mf_code_wslot(lane, 0), ws1 = mf_code_wslot(lane, 1);
+        const int rs0 = mf_code_rslot(li, q, 0), rs1 = mf_code_rslot(li, q, 1);
         while (u < nunits) {
             if constexpr (MASKED) {
                 const int word = (u * rows) >> 5;

@@ -551,6 +551,37 @@ __device__ __forceinline__ void stage_x_mf(uint4 *xs, const uint4 *__restrict__ 
             xs[m * cpr + (c ^ (m & 7))] = v;
         });
 }
+// stage_x_mf in two steps, so that loads issued in between (the first
+// weights) are in flight with the activations and the image's stores wait
+// for the activations only: the first kStageBatch units of each thread into
+// registers, then their stores and the rest of the image.
+__device__ __forceinline__ void stage_x_mf_first(uint4 (&v)[kStageBatch], const uint4 *__restrict__ x, int m_rt,
+                                                 int mt, int k) {
+    const int cpr = k >> 3, units = mt * cpr;
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        const int p = threadIdx.x + j * blockDim.x;
+        v[j] = p < units && p / cpr < m_rt ? x[p] : make_uint4(0, 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void stage_x_mf_rest(uint4 *xs, const uint4 (&v)[kStageBatch], const uint4 *__restrict__ x,
+                                                int m_rt, int mt, int k) {
+    const int cpr = k >> 3, units = mt * cpr, done = kStageBatch * blockDim.x;
+    auto put = [&](int p, uint4 val) {
+        const int m = p / cpr, c = p - m * cpr;
+        xs[m * cpr + (c ^ (m & 7))] = val;
+    };
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+        const int p = threadIdx.x + j * blockDim.x;
+        if (p < units) put(p, v[j]);
+    }
+    if (units > done)
+        stage_batched(
+            units - done, threadIdx.x, blockDim.x,
+            [&](int q) { return (q + done) / cpr < m_rt ? x[q + done] : make_uint4(0, 0, 0, 0); },
+            [&](int q, uint4 val) { put(q + done, val); });
+}
 
 // Two E2M1 codes (byte SEL of word) times sf as two bf16 (exact: e2m1 times
 // an E4M3 scale has at most 6 significant bits).
