@@ -6,9 +6,10 @@ mtp_head.rs `MtpHead` fields: `embed_from_argmax`; deepseek_v4_mtp.rs
 GEMV of the concatenated rows, with its own gather (zero rows for ids
 outside the table).  Exact-arithmetic inputs (table and rest rows in
 {-3..3}, exact-family weights) are compared bit for bit, on every kernel
-the shape reaches: the one-row register path, the LDS path, the K-split
-MFMA units and the persistent grid; random inputs equal w4a16_gemv of the
-concatenated rows bit for bit."""
+the shapes reach: the one-row register path, the LDS path and the K-split
+MFMA units (gathered rows never take the persistent grid; the largest
+shape is one that would for plain rows); random inputs equal w4a16_gemv of
+the concatenated rows bit for bit."""
 import numpy as np
 import pytest
 import torch
