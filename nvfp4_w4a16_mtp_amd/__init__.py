@@ -9,6 +9,7 @@ Operations (same names as the C ABI):
   nvfp4_quantize               bf16 W[n, k] -> NVFP4Weight (codes, scales, global)
   w4a16_gemv                   x[m<=8, k] @ W^T
   w4a16_gemv_grouped           the GEMV for several weights sharing x (q|k|v, gate|up)
+  w4a16_gemv_embed             the GEMV over [embedding rows of device ids | x_rest]
   w4a16_gemm_m128              x[m, k] @ W^T for prompt-sized m (bf16 MFMA)
   lmhead_gemv_argmax           argmax over the first V rows of h @ W^T
   lmhead_gemv_argmax_logprob   ... plus the top-1 log-probability
