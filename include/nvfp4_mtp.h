@@ -356,14 +356,14 @@ int w4a16_gemv_embed(const int32_t *idx, const uint16_t *table_bf16, int32_t tab
  *                  sticky status word: see moe_workspace_status).  One
  *                  call at a time per workspace.
  * Per selected expert: g = gate x, u = up x (fp32),
- * a = bf16_rne(silu(g) * u), d = down a (fp32).  Each expert's weights are
- * read once per call however many rows select it.  Requires H, I % 32 == 0
+ * a = bf16_rne(silu(g) * u), d = down a (fp32).  The gate/up weights are
+ * read once per (row, slot) pair, the down weights once per distinct expert.
+ * Requires H, I % 32 == 0
  * and round_up(m, 1|2|4|8) * max(H, I) * 2 <= 159744 bytes of LDS (H up to
  * 9984 at m = 8); NVFP4_ERR_UNSUPPORTED otherwise.  One launch at one
  * token when the down pass's activation rows fit in LDS and the whole grid
- * is resident at once (decode at the usual shapes); else routing with
- * gate/up (from three tokens on the routing is a launch of its own), then
- * the down pass with the combine.
+ * is resident at once (decode at the usual shapes); else gate/up (with the
+ * routing), then the down pass with the combine.
  */
 size_t moe_w4a16_gemv_workspace_bytes(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
 int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits,

@@ -5,23 +5,25 @@
 // The routing is decided on the device (no host round trip): top-k by
 // logit with the lower id first on ties, softmax over the selected logits,
 // the distinct experts in ascending id with their tokens and (token, slot)
-// pairs.  Each selected expert's weights are streamed once per call however
-// many tokens chose it.
+// pairs.  The gate/up pass takes one column of workgroups per (token, slot)
+// pair -- a workgroup needs only its own token's selections up to its slot,
+// and an expert two tokens chose is streamed once per pair -- and the down
+// pass streams each distinct expert's weights once.
 //
 // Launch structure:
 //  * one token, when the whole grid is resident: one launch (k_moe_fused).
-//    The gate/up workgroups route for themselves, run 16 rows of gate and up
-//    for the tokens that chose their expert and store a = bf16(silu(g) * u);
-//    the down workgroups, after them in dispatch order, route for
-//    themselves, prefetch their weights and wait for a per-call tagged go
-//    word before reading the activations;
-//  * otherwise: routing (in every gate/up workgroup, or from three tokens on
-//    once, in its own one-workgroup launch), gate/up, then the down pass:
-//    the row-owner pass (k_moe_down_rows: a workgroup owns 8 output rows of
-//    every routed expert, all pairs' activations in LDS, y summed per token
-//    in ascending expert order) when the activations fit in LDS, else the
-//    ticket pass (k_moe_down: 64-row tiles per expert, d per pair to the
-//    workspace, the last expert of a tile sums y in slot order).
+//    The gate/up workgroups of column j select the token's j-th expert, run
+//    16 rows of its gate and up and store a = bf16(silu(g) * u); the down
+//    workgroups, after them in dispatch order, route for themselves,
+//    prefetch their weights and wait for a release per column before
+//    reading the activations;
+//  * otherwise: gate/up (workgroup (0, 0) also routes every token and
+//    publishes the ids, the weights and the down pass's plan), then the down
+//    pass: the row-owner pass (k_moe_down_rows: a workgroup owns 8 output
+//    rows of every routed expert, all pairs' activations in LDS, y summed
+//    per token in ascending expert order) when the activations fit in LDS,
+//    else the ticket pass (k_moe_down: 64-row tiles per expert, d per pair
+//    to the workspace, the last expert of a tile sums y in slot order).
 // No floating-point atomics: y is deterministic for given inputs.
 #include <algorithm>
 
@@ -459,10 +461,7 @@ __device__ __forceinline__ void write_route(RouteLds &L, const nvfp4_moe_weights
     }
 }
 
-// PLANNED: the plan comes from k_moe_route instead of every workgroup's own
-// routing (which, at several tokens, costs a gate/up workgroup about as much
-// as its weights).
-template <int CPL, bool FUSED, bool PLANNED = false>
+template <int CPL, bool FUSED>
 __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx, const uint16_t *__restrict__ x,
                                              const float *__restrict__ logits, int m, int E, int topk,
                                              const nvfp4_moe_weights &e, int32_t *__restrict__ ids,
@@ -494,47 +493,35 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
             if (lane == 0) st_dev(&sh.sgate[t], sh.gate_w != nullptr ? 1.0f / (1.0f + expf(-z)) : 1.0f);
         }
     }
-    if constexpr (PLANNED) {
-        // the routing kernel wrote the plan (and the ids and weights)
-        if (threadIdx.x == 0) {
-            s_nd = route->n_distinct;
-            if (u < s_nd) {
-                s_ex = route->ex[u].expert;
-                s_cnt = route->ex[u].cnt;
-            }
-        }
-        if (threadIdx.x < 8 && u < route->n_distinct) {
-            tok[threadIdx.x] = route->ex[u].tok[threadIdx.x];
-            prs[threadIdx.x] = route->ex[u].pair[threadIdx.x];
-        }
-    } else if (FUSED && m == 1) {
-        // one token, one launch: column u takes the u-th selected expert
-        // (pair u), known after u + 1 selections, so that the early columns'
-        // weights start streaming while the later ones still select; a down
-        // workgroup publishes the ids and weights
+    if (FUSED || bx != 0 || u != 0) {
+        // column u is pair u = t top_k + j: token t's j-th selected expert,
+        // known after j + 1 selections of that token alone, so the early
+        // columns' weights stream while the later ones still select (an
+        // expert two tokens chose is streamed once per pair).  Workgroup
+        // (0, 0) publishes the whole routing; in the one-token launch a down
+        // workgroup does
         if (threadIdx.x < 64) {
-            const int id = u < topk ? moe_route_nth(logits, E, topk, u) : 0;
+            const int t = u / topk, j = u - t * topk;
+            const int id = u < m * topk ? moe_route_nth(logits + (size_t)t * E, E, topk, j) : 0;
             if (threadIdx.x == 0) {
-                s_nd = topk;
+                s_nd = m * topk;
                 s_ex = id;
                 s_cnt = 1;
-                tok[0] = 0;
+                tok[0] = t;
                 prs[0] = u;
             }
         }
     } else {
+        // workgroup (0, 0) of the two-launch form: the whole routing, the ids
+        // and weights and the down pass's plan, then its own pair 0
         moe_route_lds(logits, m, E, topk, L);
-        if (bx == 0 && u == 0) write_route(L, e, m, topk, ids, wts, FUSED ? nullptr : route);
+        write_route(L, e, m, topk, ids, wts, route);
         if (threadIdx.x == 0) {
-            s_nd = L.n_distinct;
-            if (u < L.n_distinct) {
-                s_ex = L.ex[u].expert;
-                s_cnt = L.ex[u].cnt;
-            }
-        }
-        if (threadIdx.x < 8 && u < L.n_distinct) {
-            tok[threadIdx.x] = L.ex[u].tok[threadIdx.x];
-            prs[threadIdx.x] = L.ex[u].pair[threadIdx.x];
+            s_nd = m * topk;
+            s_ex = L.sel_i[0][0];
+            s_cnt = 1;
+            tok[0] = 0;
+            prs[0] = 0;
         }
     }
     if (s_act) st_dev(&sh.sact[(size_t)st * I + si], (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv));
@@ -546,11 +533,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     const uint8_t *uc = e.up_codes + (size_t)ex * (wsz / 2), *us = e.up_scales + (size_t)ex * (wsz / 16);
     const float gdec = e.gate_global[ex].dec, udec = e.up_global[ex].dec;
     const int row0 = bx * kMoeRows;
-    const int mt = round_up_mt(cnt);
-    if (mt == 1) gate_up_body<1, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else if (mt == 2) gate_up_body<2, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else if (mt == 4) gate_up_body<4, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
-    else gate_up_body<8, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
+    gate_up_body<1, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     if constexpr (FUSED) {
         // count this workgroup in its column; the one that completes the
         // column releases it to every down workgroup through its go word
@@ -573,44 +556,17 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     }
 }
 
-// Without a plan (one or two tokens) every workgroup routes for itself and
-// its latency chain is long: 128 registers, four workgroups a CU, took two
-// tokens from 26.3 to 22.5 us (a few bytes spill); the planned kernel keeps
-// its 152 registers (capped, it was slower).
-template <int CPL, bool PLANNED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PLANNED ? 1 : 4))) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
+// The two-launch form's gate/up pass (one workgroup per 16-row tile and
+// (token, slot) pair), held to four workgroups a CU.
+template <int CPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                     int m, int E, int topk, nvfp4_moe_weights e,
                                                     int32_t *__restrict__ ids, float *__restrict__ wts,
                                                     MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
                                                     MoeShared sh) {
     extern __shared__ uint4 smem[];
-    gate_up_role<CPL, false, PLANNED>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts,
-                                      route, act, sh, nullptr, 0);
-}
-
-// The routing alone (one workgroup), for the planned gate/up launch.
-__global__ __launch_bounds__(512) void k_moe_route(const float *__restrict__ logits, int m, int E, int topk,
-                                                  nvfp4_moe_weights e, int32_t *__restrict__ ids,
-                                                  float *__restrict__ wts, MoeRoute *__restrict__ route) {
-    __shared__ RouteLds L;
-    __shared__ float s_dec[kMoeMaxExperts];
-    // every expert's down scale, loaded by the first 256 threads (the
-    // launch has 256 or 512) before the routing and kept in registers until
-    // it is done (the plan needs those of the routed experts)
-    float dec[kMoeMaxExperts / 256];
-#pragma unroll
-    for (int j = 0; j < kMoeMaxExperts / 256; ++j) {
-        const int i = threadIdx.x + 256 * j;
-        dec[j] = threadIdx.x < 256 && i < E ? e.down_global[i].dec : 0.0f;
-    }
-    moe_route_lds(logits, m, E, topk, L);
-#pragma unroll
-    for (int j = 0; j < kMoeMaxExperts / 256; ++j) {
-        const int i = threadIdx.x + 256 * j;
-        if (i < E && threadIdx.x < 256) s_dec[i] = dec[j];
-    }
-    __syncthreads();
-    write_route(L, e, m, topk, ids, wts, route, s_dec);
+    gate_up_role<CPL, false>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts, route, act,
+                             sh, nullptr, 0);
 }
 
 // Rows per slot of the ticket down pass: 4 (a 64-row tile, about 37 KB of
@@ -1069,29 +1025,14 @@ static MoeLayout moe_layout(int m, int topk, int H, int I) {
     return L;
 }
 
-// Fewest tokens for which the two-launch path routes once, in its own
-// kernel, instead of in every gate/up workgroup.
-constexpr int kMoePlanMinTokens = 3;
 
 template <int CPL>
 static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
                           uint16_t *act, const MoeShared &sh) {
-    if (m >= kMoePlanMinTokens) {
-        // one wavefront a token
-        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(64 * round_up_mt(m)), 0, s, logits, m, E, topk, e, ids, wts, route);
-        const int rc0 = check_launch("moe_w4a16_gemv(route)");
-        if (rc0) return rc0;
-        const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, true>), lds, "moe_w4a16_gemv");
-        if (rc) return rc;
-        hipLaunchKernelGGL((k_moe_gate_up<CPL, true>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route,
-                           act, sh);
-        return check_launch("moe_w4a16_gemv(gate_up)");
-    }
-    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, false>), lds, "moe_w4a16_gemv");
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL>), lds, "moe_w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL((k_moe_gate_up<CPL, false>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route,
-                       act, sh);
+    hipLaunchKernelGGL((k_moe_gate_up<CPL>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act, sh);
     return check_launch("moe_w4a16_gemv(gate_up)");
 }
 template <int CPL>
@@ -1196,8 +1137,11 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const int E = e->num_experts, H = e->hidden, I = e->inter, mt = round_up_mt(m);
     const int maxd = min(E, m * top_k);
     const nvfp4_moe_weights ev = *e;
-    const dim3 g1((I + kMoeRows - 1) / kMoeRows, maxd), g2((H + kDownTile - 1) / kDownTile, maxd);
-    const size_t lds1 = std::max((size_t)mt * H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
+    // gate/up: one column per (token, slot) pair; down (ticket pass): one per distinct expert
+    const dim3 g1((I + kMoeRows - 1) / kMoeRows, m * top_k), g2((H + kDownTile - 1) / kDownTile, maxd);
+    // gate/up: one token's activation row (or the routing scratch of
+    // workgroup (0, 0)); the ticket down pass: an expert's rows of up to m tokens
+    const size_t lds1 = std::max((size_t)H * 2, sizeof(RouteLds)), lds2 = (size_t)mt * I * 2;
     const size_t pos = (size_t)m * top_k + (sh.on ? m : 0);
     // the row-owner pass keeps about 8 KiB of static LDS next to the
     // activation rows of every pair; with 16 wavefronts a workgroup it beats
@@ -1206,7 +1150,7 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
     const bool row_owner = pos <= (size_t)kDownMaxPos && pos * I * 2 <= lds_limit && cpl_for(I) != 0;
     if (row_owner && m == 1) {
         // one launch: gate/up workgroups, then the row-owner down workgroups
-        const int gx = (int)g1.x, ng1 = gx * maxd, ng3 = (H + kDownRows - 1) / kDownRows;
+        const int gx = (int)g1.x, ng1 = gx * (int)g1.y, ng3 = (H + kDownRows - 1) / kDownRows;
         const size_t lds = std::max(lds1, pos * I * 2);
         const int frc = launch_fused(cpl_for(H), cpl_for(I), ng1 + ng3, lds, s, x_bf16, router_logits, m, E, top_k,
                                      ev, topk_ids, topk_w, act, y, sh, reinterpret_cast<unsigned int *>(ws + L.sync),

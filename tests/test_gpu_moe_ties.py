@@ -6,8 +6,10 @@ IEEE comparison).  The selection rule is the oracle's: top-k by fp32 logit,
 descending, the lower expert id first among equal logits (the scan order of
 `moe_topk_softmax` named in new.rs, `MtpHead::new`).  topk_ids are compared
 bit for bit; weights and outputs within |d| <= 1e-3 + 2e-3 |ref|.  One token
-takes the one-token routing path, two the per-workgroup routing, three or
-more the routing launch."""
+takes the one-launch path, where the ids come from the down workgroups'
+routing; more tokens the two-launch path, where workgroup (0, 0) of the
+gate/up pass publishes them (and every gate/up workgroup selects its own
+token's experts up to its slot)."""
 import math
 
 import numpy as np
