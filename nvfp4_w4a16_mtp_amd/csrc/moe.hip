@@ -497,9 +497,9 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
         // column u is pair u = t top_k + j: token t's j-th selected expert,
         // known after j + 1 selections of that token alone, so the early
         // columns' weights stream while the later ones still select (an
-        // expert two tokens chose is streamed once per pair).  Workgroup
-        // (0, 0) publishes the whole routing; in the one-token launch a down
-        // workgroup does
+        // expert two tokens chose is streamed once per pair).  The whole
+        // routing is published by workgroup (0, 0), or in the one-token
+        // launch by a down workgroup.
         if (threadIdx.x < 64) {
             const int t = u / topk, j = u - t * topk;
             const int id = u < m * topk ? moe_route_nth(logits + (size_t)t * E, E, topk, j) : 0;
