@@ -791,6 +791,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     __shared__ float contrib[kDownMaxPos][kDownRows];
     __shared__ int s_nr, s_p0, s_late;
     const int H = e.hidden, I = e.inter, C = I >> 5;
+    float s_decv = 0.0f;   // one-launch form: the down scale of distinct expert threadIdx.x
     // the plan in LDS; with a shared expert it follows the routed ones as
     // expert nd (id -1), its m positions after the pairs, weighted by the
     // shared gate, activation rows from sh.sact
@@ -799,11 +800,25 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         moe_route_lds(logits, m, E, topk, L);
         if (bx == 0 && ids != nullptr) write_route(L, e, m, topk, ids, wts, nullptr);
         const int nr = L.n_distinct;
-        for (int q = threadIdx.x; q < nr; q += blockDim.x) {
-            s_ex[q] = L.ex[q].expert;
-            s_dec[q] = e.down_global[L.ex[q].expert].dec;
-        }
-        if (threadIdx.x == 0) {
+        // the experts' down scales go to LDS after the weight loads are
+        // issued (a dependent load: waiting for it here delayed them)
+        for (int q = threadIdx.x; q < nr; q += blockDim.x) s_ex[q] = L.ex[q].expert;
+        if (threadIdx.x < nr) s_decv = e.down_global[L.ex[threadIdx.x].expert].dec;
+        if (m == 1) {
+            // one token: expert q is position q, its pair the slot that chose it
+            if (threadIdx.x < nr) {
+                const int pr = L.ex[threadIdx.x].pair[0];
+                s_pb[threadIdx.x] = threadIdx.x;
+                s_tok[threadIdx.x] = 0;
+                s_pair[threadIdx.x] = pr;
+                s_w[threadIdx.x] = L.sel_w[0][pr];
+            }
+            if (threadIdx.x == 0) {
+                s_pb[nr] = nr;
+                s_nr = nr;
+                s_p0 = nr;
+            }
+        } else if (threadIdx.x == 0) {
             int pb = 0;
             for (int q = 0; q < nr; ++q) {
                 const MoeExpert &me = L.ex[q];
@@ -870,6 +885,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         down_rows_load<CPL>(it, 0, kSlots, ca, sa);
         down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
         __builtin_amdgcn_sched_barrier(0);
+        if (threadIdx.x < nr) s_dec[threadIdx.x] = s_decv;   // read at the sums, after the staging barrier
         if (threadIdx.x == 0) {
             // one release per routed expert column; the count is advanced
             // whether or not the wait succeeds, so a late release of this
