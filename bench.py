@@ -24,7 +24,8 @@ one thread and at every host core.
 Other modes: --gemm-only (every prefill GEMM shape), --counters (the decode
 rows once each, separated by marker kernels, for rocprofv3 counter passes),
 --summarize-counters (turns those passes into the committed summary),
---calibrate-copy (a plain 1 GiB copy for the byte-counter calibration).
+--calibrate-copy (a plain 1 GiB copy for the byte-counter calibration),
+--moe-timeline (the one-token MoE's phase timestamps, moe_w4a16_gemv_trace).
 """
 from __future__ import annotations
 
@@ -74,6 +75,8 @@ def parse():
                    help="rocprofv3 output dirs of the --counters passes -> markdown summary on stdout")
     p.add_argument("--copy-dirs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="with --summarize-counters: the FETCH_SIZE and WRITE_SIZE passes of --calibrate-copy")
+    p.add_argument("--moe-timeline", action="store_true",
+                   help="phase timestamps of the one-token MoE launch (medians over launches) and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (PMC byte-counter calibration)")
     return p.parse_args()
@@ -672,6 +675,43 @@ def cpu_baseline(step_bytes_m1):
 
 
 # ------------------------------------------------------------------- main
+def moe_timeline(env, launches=40, skip=5):
+    """Phase timestamps of the one-token MoE (bench shapes: 256 experts,
+    top-8, 2048 x 1024): each launch starts on an idle GPU, after a spin
+    kernel that covers the host's queueing; per launch, each event's
+    [min, median, max] over the workgroups in microseconds from the first
+    workgroup's start; then the median of each over the launches after
+    `skip` warm-up ones."""
+    nv, torch = env.nv, env.torch
+    experts = [expert_stack(env) for _ in range(3)]
+    x = env.randn((1, H))
+    routers = [env.randn((1, E), dtype=torch.float32) for _ in range(launches)]
+    ws = nv.moe_workspace(1, TOPK, experts[0], env.dev)
+    y = torch.empty((1, H), dtype=torch.float32, device=env.dev)
+    ev, groups = nv.moe_trace_events(TOPK, experts[0])
+    gate_up = (I + 15) // 16 * TOPK
+    trace = torch.zeros((ev, groups), dtype=torch.int64, device=env.dev)
+    names = {"gate_up": ("start", "routed", "stored", "counted"),
+             "down": ("start", "weights_issued", "go_seen", "staged", "sums_done", "written")}
+    per = []
+    for i in range(launches):
+        torch.cuda._sleep(100000)
+        nv.moe_w4a16_gemv(x, routers[i], TOPK, experts[i % 3], workspace=ws, out=y, trace=trace)
+        torch.cuda.synchronize()
+        if i < skip:
+            continue
+        t = trace.cpu().numpy().astype(np.int64)
+        t0 = t[0].min()
+        row = {}
+        for role, cols in (("gate_up", t[:, :gate_up]), ("down", t[:, gate_up:])):
+            for e, name in enumerate(names[role]):
+                v = (cols[e] - t0) / 100.0   # 100 MHz ticks -> us
+                row[f"{role}.{name}"] = [float(v.min()), float(np.median(v)), float(v.max())]
+        per.append(row)
+    nv.moe_workspace_status(ws)
+    return {k: [round(float(np.median([r[k][j] for r in per])), 2) for j in range(3)] for k in per[0]}
+
+
 def main():
     a = parse()
     if a.summarize_counters:
@@ -696,6 +736,9 @@ def main():
     env = Env(nv, torch)
     if a.gemm_only:
         print(json.dumps({"prefill_gemm": gemm_rows(env, GEMM_SHAPES)}), flush=True)
+        return
+    if a.moe_timeline:
+        print(json.dumps({"moe_timeline_us": moe_timeline(env)}), flush=True)
         return
 
     # ---------------- weights: NCOPIES copies of the step, quantized on the GPU

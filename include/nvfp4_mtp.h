@@ -371,6 +371,33 @@ int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *router_logits
                    float *topk_w, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * moe_w4a16_gemv_trace -- moe_w4a16_gemv in its one-launch form with phase
+ * timestamps, for profiling the one-token latency chain; the outputs are
+ * those of moe_w4a16_gemv bit for bit.  Not a second computation: the same
+ * kernel, given a trace buffer.
+ *   m              1 (NVFP4_ERR_UNSUPPORTED otherwise, and when the call
+ *                  would not take the one-launch form).
+ *   trace          device uint64[trace_words], 8-byte aligned, at least
+ *                  moe_w4a16_gemv_trace_words(m, top_k, e) words (0 when m
+ *                  != 1); out: event ev of workgroup b at trace[ev * G + b],
+ *                  G = ceil(I / 16) * top_k gate/up workgroups followed by
+ *                  ceil(H / 8) down workgroups, each the GPU's 100 MHz
+ *                  constant clock (s_memrealtime) read by the workgroup's
+ *                  first thread.  Gate/up events: 0 start, 1 routing done,
+ *                  2 activations stored, 3 counted in its column (the last
+ *                  of a column: after issuing the release).  Down events:
+ *                  0 start, 1 weight loads issued, 2 go word seen,
+ *                  3 activations staged, 4 sums done, 5 output written.
+ *                  Unused slots are left as they were.
+ *   the other arguments and errors as moe_w4a16_gemv.
+ */
+size_t moe_w4a16_gemv_trace_words(int32_t m, int32_t top_k, const nvfp4_moe_weights *e);
+int moe_w4a16_gemv_trace(const uint16_t *x_bf16, int32_t m, const float *router_logits,
+                         int32_t top_k, const nvfp4_moe_weights *e, float *y, int32_t *topk_ids,
+                         float *topk_w, void *workspace, size_t ws_bytes, uint64_t *trace,
+                         size_t trace_words, void *stream);
+
+/*
  * moe_layer_w4a16 -- the complete MoE layer of the draft head: the NVFP4
  * router (`moe_gate`, quantized next to the experts in [new.rs]
  * `MtpHead::new`), the routed experts of moe_w4a16_gemv and the shared

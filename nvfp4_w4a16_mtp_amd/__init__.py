@@ -18,6 +18,7 @@ Operations (same names as the C ABI):
   lmhead_gemv_argmax_noalloc   lmhead_gemv_argmax on the library's own static scratch
   embed_from_argmax            embedding rows of device-resident token ids
   moe_w4a16_gemv               top-k routed NVFP4 expert FFN
+  moe_w4a16_gemv_trace         ... one token, with per-workgroup phase timestamps
   moe_layer_w4a16              router + routed experts + gated shared expert
   moe_workspace_status         sticky status of a MoE workspace (host query)
 """
@@ -84,6 +85,9 @@ def lib():
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
+        L.moe_w4a16_gemv_trace_words.argtypes = [i32, i32, EP]
+        L.moe_w4a16_gemv_trace_words.restype = sz
+        L.moe_w4a16_gemv_trace.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P, sz, P]
         L.moe_layer_w4a16_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_layer_w4a16_workspace_bytes.restype = sz
         L.moe_layer_w4a16.argtypes = [P, i32, WP, i32, EP, WP, WP, WP, P, P, P, P, P, P, sz, P]
@@ -93,7 +97,7 @@ def lib():
                   "lmhead_gemv_argmax_noalloc",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
                   "w4a16_gemv_embed",
-                  "moe_w4a16_gemv", "moe_layer_w4a16", "moe_workspace_status"):
+                  "moe_w4a16_gemv", "moe_w4a16_gemv_trace", "moe_layer_w4a16", "moe_workspace_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -465,9 +469,21 @@ def moe_workspace(m: int, top_k: int, experts: NVFP4Experts, device) -> torch.Te
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
+def moe_trace_events(top_k: int, experts: NVFP4Experts) -> tuple[int, int]:
+    """(events, workgroups) of a one-token moe_w4a16_gemv_trace: the trace
+    holds events x workgroups timestamps, gate/up workgroups first."""
+    d = experts.desc()
+    words = lib().moe_w4a16_gemv_trace_words(1, top_k, ctypes.byref(d))
+    return 6, words // 6
+
+
 def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, experts: NVFP4Experts,
                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                   topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+                   topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                   trace: torch.Tensor | None = None):
+    """Routed MoE over m rows.  With `trace` (int64 [6, workgroups] from
+    moe_trace_events, one token only) the one-launch form also records its
+    phase timestamps (moe_w4a16_gemv_trace)."""
     x = _as_bf16(x)
     _dev(x, "x")
     _dev(router_logits, "router_logits")
@@ -483,6 +499,15 @@ def moe_w4a16_gemv(x: torch.Tensor, router_logits: torch.Tensor, top_k: int, exp
     if topk_w is None:
         topk_w = torch.empty((m, top_k), dtype=torch.float32, device=x.device)
     d = experts.desc()
+    if trace is not None:
+        _dev(trace, "trace")
+        if trace.dtype != torch.int64 or not trace.is_contiguous():
+            raise TypeError("trace must be a contiguous int64 tensor")
+        _check(lib().moe_w4a16_gemv_trace(_ptr(x), m, _ptr(router_logits), top_k, ctypes.byref(d), _ptr(out),
+                                          _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), workspace.numel(),
+                                          _ptr(trace), trace.numel(), _stream(x)),
+               "moe_w4a16_gemv_trace")
+        return out, topk_ids, topk_w
     _check(lib().moe_w4a16_gemv(_ptr(x), m, _ptr(router_logits), top_k, ctypes.byref(d), _ptr(out), _ptr(topk_ids),
                                 _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x)),
            "moe_w4a16_gemv")

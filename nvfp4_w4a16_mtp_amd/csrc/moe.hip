@@ -98,7 +98,23 @@ struct MoeShared {
     const uint8_t *dcodes, *dscales;
     const nvfp4_global *dglob;      // its down projection [H][I]
     int on;
+    // phase timestamps of the one-launch form, or nullptr: event ev of
+    // workgroup b at trace[ev * grid + b] (moe_w4a16_gemv_trace)
+    unsigned long long *trace;
 };
+
+// Events of trace_mark.  Gate/up workgroups: start, routing done,
+// activations stored, counted in the column (and, for the last one of a
+// column, its release issued).  Down workgroups: start, weight loads issued,
+// go word seen, activations staged, sums done, output written.
+// Only the traced instantiation records them: a run-time test of the
+// pointer alone, in the plain kernel, slowed the one-token launch by 1.6 us.
+constexpr int kTraceEvents = 6;
+template <bool TRACE>
+__device__ __forceinline__ void trace_mark(unsigned long long *trace, int ev) {
+    if constexpr (TRACE)
+        if (threadIdx.x == 0) trace[(size_t)ev * gridDim.x + blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+}
 
 // Sum over the wavefront in a fixed order; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -461,7 +477,7 @@ __device__ __forceinline__ void write_route(RouteLds &L, const nvfp4_moe_weights
     }
 }
 
-template <int CPL, bool FUSED>
+template <int CPL, bool FUSED, bool TRACE = false>
 __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx, const uint16_t *__restrict__ x,
                                              const float *__restrict__ logits, int m, int E, int topk,
                                              const nvfp4_moe_weights &e, int32_t *__restrict__ ids,
@@ -471,6 +487,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // reused for the activations afterwards
     __shared__ int tok[8], prs[8];
     __shared__ int s_ex, s_cnt, s_nd;
+    if (FUSED) trace_mark<TRACE>(sh.trace, 0);
     // shared expert: the workgroups of the first expert column form 16 of its
     // activations per token each (loads issued before the routing, stored after)
     const int I = e.inter, H = e.hidden;
@@ -526,6 +543,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     }
     if (s_act) st_dev(&sh.sact[(size_t)st * I + si], (uint16_t)f32_to_bf16_bits(sgv / (1.0f + expf(-sgv)) * suv));
     __syncthreads();   // the routing scratch is free from here on
+    if (FUSED) trace_mark<TRACE>(sh.trace, 1);
     if (u >= s_nd) return;
     const int ex = s_ex, cnt = s_cnt;
     const size_t wsz = (size_t)I * H;
@@ -539,6 +557,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
         // column releases it to every down workgroup through its go word
         __shared__ int s_release;
         wait_mem();   // this workgroup's activations have reached device scope
+        trace_mark<TRACE>(sh.trace, 2);
         __syncthreads();
         if (threadIdx.x == 0) {
             int rel = 0;
@@ -553,6 +572,7 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
             for (int i = threadIdx.x; i < n_down; i += blockDim.x)
                 __hip_atomic_fetch_add(&done[kSyncWords + kGoStride * i], kGoTag, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
+        trace_mark<TRACE>(sh.trace, 3);
     }
 }
 
@@ -779,7 +799,7 @@ __device__ __forceinline__ void stage_rows_rest(uint4 *xs, const uint4 (&v)[kSta
             [&](int q, uint4 val) { put(q + done, val); });
 }
 
-template <int CPL, bool FUSED, int NW = 4>
+template <int CPL, bool FUSED, int NW = 4, bool TRACE = false>
 __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_moe_weights &e, int m, int topk,
                                                const MoeRoute *__restrict__ route, const float *__restrict__ logits,
                                                int E, int gx, const uint16_t *__restrict__ act, float *__restrict__ y,
@@ -790,6 +810,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
     __shared__ float contrib[kDownMaxPos][kDownRows];
     __shared__ int s_nr, s_p0, s_late;
+    if (FUSED) trace_mark<TRACE>(sh.trace, 0);
     const int H = e.hidden, I = e.inter, C = I >> 5;
     float s_decv = 0.0f;   // one-launch form: the down scale of distinct expert threadIdx.x
     // the plan in LDS; with a shared expert it follows the routed ones as
@@ -886,6 +907,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
         __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x < nr) s_dec[threadIdx.x] = s_decv;   // read at the sums, after the staging barrier
+        trace_mark<TRACE>(sh.trace, 1);
         if (threadIdx.x == 0) {
             // one release per routed expert column; the count is advanced
             // whether or not the wait succeeds, so a late release of this
@@ -912,6 +934,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
             s_late = bad;
         }
         __syncthreads();
+        trace_mark<TRACE>(sh.trace, 2);
         if (s_late) {
             for (int i = threadIdx.x; i < m * kDownRows; i += blockDim.x) {
                 const int row = r0 + i % kDownRows;
@@ -934,6 +957,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
     }
     __syncthreads();
+    if (FUSED) trace_mark<TRACE>(sh.trace, 3);
     if (FUSED && CPL <= 2 && P == nd && nitems <= 2 * kStep) {
         // one position per expert (position u is expert u's); the separate
         // pass has four times the wavefronts to overlap its items instead,
@@ -951,6 +975,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (FUSED) trace_mark<TRACE>(sh.trace, 4);
     __syncthreads();
     // y[t][row] = sum over token t's pairs, in ascending expert order, of
     // w * d: one thread per (token, row); the positions are read four at a
@@ -977,6 +1002,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
             if (s_tok[pos] == t) acc = __builtin_fmaf(s_w[pos], contrib[pos][r], acc);
         if (row < H) y[(size_t)t * H + row] = acc;
     }
+    if (FUSED) trace_mark<TRACE>(sh.trace, 5);
 }
 
 // The separate row-owner down pass: 16 wavefronts (64 slots) per
@@ -999,7 +1025,7 @@ __global__ __launch_bounds__(64 * down_rows_waves<CPL>()) void k_moe_down_rows(n
 // the gate/up tiles (gx per expert column), the rest own kDownRows output
 // rows each.  The down workgroups come after every gate/up workgroup in
 // dispatch order, so the ones they wait for are already running.
-template <int CPLG, int CPLD>
+template <int CPLG, int CPLD, bool TRACE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CPLD <= 2 ? 3 : 1))) void k_moe_fused(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                   int m, int E, int topk, nvfp4_moe_weights e,
                                                   int32_t *__restrict__ ids, float *__restrict__ wts,
@@ -1009,11 +1035,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CPLD <= 2 ?
     extern __shared__ uint4 smem[];
     const int b = blockIdx.x;
     if (b < g1)
-        gate_up_role<CPLG, true>(smem, b % gx, b / gx, gx, x, logits, m, E, topk, e, ids, wts, nullptr, act, sh,
-                                 counters, (int)gridDim.x - g1);
+        gate_up_role<CPLG, true, TRACE>(smem, b % gx, b / gx, gx, x, logits, m, E, topk, e, ids, wts, nullptr, act,
+                                        sh, counters, (int)gridDim.x - g1);
     else
-        down_rows_role<CPLD, true>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters, status, ids,
-                                   wts);
+        down_rows_role<CPLD, true, 4, TRACE>(smem, b - g1, e, m, topk, nullptr, logits, E, gx, act, y, sh, counters,
+                                             status, ids, wts);
 }
 
 template <int CPL>
@@ -1062,41 +1088,53 @@ static int launch_down(dim3 g, size_t lds, hipStream_t s, const nvfp4_moe_weight
 
 constexpr int kNotResident = 1;   // launch_fused: the grid does not fit at once (nothing launched)
 
-template <int CPLG, int CPLD>
+template <int CPLG, int CPLD, bool TRACE>
 static int launch_fused_t(int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act, float *y,
                           const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx, int g1) {
-    const void *kern = reinterpret_cast<const void *>(k_moe_fused<CPLG, CPLD>);
+    const void *kern = reinterpret_cast<const void *>(k_moe_fused<CPLG, CPLD, TRACE>);
     const int rc = allow_lds(kern, lds, "moe_w4a16_gemv");
     if (rc) return rc;
     // the down workgroups only overlap the gate/up pass when every workgroup
     // of the launch is resident at once
     if (grid > num_cus() * blocks_per_cu(kern, 256, lds)) return kNotResident;
-    hipLaunchKernelGGL((k_moe_fused<CPLG, CPLD>), dim3(grid), dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, act,
+    hipLaunchKernelGGL((k_moe_fused<CPLG, CPLD, TRACE>), dim3(grid), dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, act,
                        y, sh, counters, status, gx, g1);
     return check_launch("moe_w4a16_gemv");
 }
-template <int CPLG>
+template <int CPLG, bool TRACE>
 static int launch_fused_g(int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m,
                           int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
                           float *y, const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx,
                           int g1) {
     switch (cpld) {
-        case 1: return launch_fused_t<CPLG, 1>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-        case 2: return launch_fused_t<CPLG, 2>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-        default: return launch_fused_t<CPLG, 4>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 1: return launch_fused_t<CPLG, 1, TRACE>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 2: return launch_fused_t<CPLG, 2, TRACE>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        default: return launch_fused_t<CPLG, 4, TRACE>(grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
     }
 }
+template <bool TRACE>
+static int launch_fused_c(int cplg, int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x,
+                          const float *logits, int m, int E, int topk, const nvfp4_moe_weights &e, int32_t *ids,
+                          float *wts, uint16_t *act, float *y, const MoeShared &sh, unsigned int *counters,
+                          unsigned int *status, int gx, int g1) {
+    switch (cplg) {
+        case 1: return launch_fused_g<1, TRACE>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 2: return launch_fused_g<2, TRACE>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        case 4: return launch_fused_g<4, TRACE>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+        default: return launch_fused_g<0, TRACE>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
+    }
+}
+// The traced instantiation when sh.trace is set (moe_w4a16_gemv_trace).
 static int launch_fused(int cplg, int cpld, int grid, size_t lds, hipStream_t s, const uint16_t *x, const float *logits,
                         int m, int E, int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, uint16_t *act,
                         float *y, const MoeShared &sh, unsigned int *counters, unsigned int *status, int gx,
                         int g1) {
-    switch (cplg) {
-        case 1: return launch_fused_g<1>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-        case 2: return launch_fused_g<2>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-        case 4: return launch_fused_g<4>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-        default: return launch_fused_g<0>(cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters, status, gx, g1);
-    }
+    if (sh.trace != nullptr)
+        return launch_fused_c<true>(cplg, cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters,
+                                    status, gx, g1);
+    return launch_fused_c<false>(cplg, cpld, grid, lds, s, x, logits, m, E, topk, e, ids, wts, act, y, sh, counters,
+                                 status, gx, g1);
 }
 
 static int cpl_for(int k) {
@@ -1173,6 +1211,9 @@ static int moe_launch(const uint16_t *x_bf16, int32_t m, const float *router_log
                                      reinterpret_cast<unsigned int *>(ws + kMoeStatusOffset), gx, ng1);
         if (frc != kNotResident) return frc;
     }
+    if (sh.trace != nullptr)
+        return fail(NVFP4_ERR_UNSUPPORTED, "moe_w4a16_gemv_trace: the call does not take the one-launch form (one "
+                    "token, every activation row in LDS, the whole grid resident)");
     int rc;
     switch (cpl_for(H)) {
         case 1: rc = launch_gate_up<1>(g1, lds1, s, x_bf16, router_logits, m, E, top_k, ev, topk_ids, topk_w, route, act, sh); break;
@@ -1212,6 +1253,38 @@ extern "C" int moe_w4a16_gemv(const uint16_t *x_bf16, int32_t m, const float *ro
     if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "moe_w4a16_gemv: workspace not 256-byte aligned");
     return moe_launch(x_bf16, m, router_logits, top_k, e, y, topk_ids, topk_w, reinterpret_cast<char *>(workspace), L,
                       MoeShared{}, reinterpret_cast<hipStream_t>(stream));
+}
+
+// The one-launch form's grid: gate/up tiles per pair, then the down workgroups.
+static size_t moe_trace_grid(int m, int top_k, const nvfp4_moe_weights *e) {
+    return (size_t)(e->inter + kMoeRows - 1) / kMoeRows * m * top_k + (e->hidden + kDownRows - 1) / kDownRows;
+}
+
+extern "C" size_t moe_w4a16_gemv_trace_words(int32_t m, int32_t top_k, const nvfp4_moe_weights *e) {
+    if (!e || m != 1 || top_k < 1 || e->hidden < 1 || e->inter < 1) return 0;
+    return (size_t)kTraceEvents * moe_trace_grid(m, top_k, e);
+}
+
+extern "C" int moe_w4a16_gemv_trace(const uint16_t *x_bf16, int32_t m, const float *router_logits, int32_t top_k,
+                                    const nvfp4_moe_weights *e, float *y, int32_t *topk_ids, float *topk_w,
+                                    void *workspace, size_t ws_bytes, uint64_t *trace, size_t trace_words,
+                                    void *stream) {
+    const char *who = "moe_w4a16_gemv_trace";
+    int rc = moe_validate(x_bf16, m, top_k, e, y, topk_ids, topk_w, who);
+    if (rc) return rc;
+    if (m != 1) return fail(NVFP4_ERR_UNSUPPORTED, "%s: m=%d; the one-launch form serves one token", who, m);
+    if (!router_logits || !aligned(router_logits, 4))
+        return fail(NVFP4_ERR_ARG, "%s: router_logits must be a 4-byte aligned device buffer", who);
+    if (!trace || !aligned(trace, 8)) return fail(NVFP4_ERR_ARG, "%s: trace must be an 8-byte aligned device buffer", who);
+    if (trace_words < moe_w4a16_gemv_trace_words(m, top_k, e))
+        return fail(NVFP4_ERR_WORKSPACE, "%s: trace needs %zu words", who, moe_w4a16_gemv_trace_words(m, top_k, e));
+    const MoeLayout L = moe_layout(m, top_k, e->hidden, e->inter);
+    if (!workspace || ws_bytes < L.total) return fail(NVFP4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, L.total);
+    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGN, "%s: workspace not 256-byte aligned", who);
+    MoeShared sh{};
+    sh.trace = reinterpret_cast<unsigned long long *>(trace);
+    return moe_launch(x_bf16, m, router_logits, top_k, e, y, topk_ids, topk_w, reinterpret_cast<char *>(workspace), L,
+                      sh, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int moe_workspace_status(void *workspace, size_t ws_bytes, uint32_t *status, void *stream) {
