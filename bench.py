@@ -3,8 +3,11 @@
 A step is one draft step of a Qwen-shaped MTP head at M decode rows: the
 fc / q|k|v (grouped) / o W4A16 GEMVs, the routed MoE FFN (256 NVFP4
 experts, top-8) and the full-vocabulary (151936 x 2048) NVFP4 LM head fused
-with argmax, whose draft ids stay on the device: the next step's fc reads
-the embedding row of each id itself (device-resident chaining).  The step is captured
+with argmax, whose draft ids stay on the device: the same call runs the next
+step's fc over the embedding row of each id (lmhead_gemv_argmax_fc: one
+launch at M = 1, the LM head's workgroups finishing the fc once the last of
+them has published the id), so each step runs its fc with the previous
+step's head (device-resident chaining).  The step is captured
 in a HIP graph and replayed in rotation over NCOPIES independent copies of
 every weight (5.5 GB, 21x the 256 MB Infinity Cache), each step with its own
 router logits, so the weights stream from HBM as in serving.  The headline
@@ -217,16 +220,16 @@ def draft_step(env, copies, lm_pool, embed_table, M, steps, warmup):
 
     def step(c):
         ws = copies[c]
-        # fc over [embedding of the previous step's draft token | hidden state]:
-        # the GEMV reads the embedding row by the id the LM head wrote
-        prev = draft_log[((c - 1) % NCOPIES) * M:((c - 1) % NCOPIES + 1) * M]
-        nv.w4a16_gemv_embed(prev, embed_table, hfc, ws["fc"], out=ys["fc"])
+        # (this step's fc over [embedding of the previous draft | hidden
+        # state] ran with the previous step's LM head, below)
         nv.w4a16_gemv_grouped(xs["q"], [ws["q"], ws["k"], ws["v"]], outs=[ys["q"], ys["k"], ys["v"]])
         nv.w4a16_gemv(xs["o"], ws["o"], out=ys["o"])
         nv.moe_w4a16_gemv(xm, routers[c], TOPK, ws["moe"], workspace=moe_ws, out=ymoe, topk_ids=ids, topk_w=wts)
-        # the draft ids stay on the device: the next step's fc reads them
-        nv.lmhead_gemv_argmax(hl, lm_pool[c], vocab_rows=VOCAB, workspace=lm_ws,
-                              out_idx=draft_log[c * M:(c + 1) * M], out_max=out_max)
+        # the draft ids stay on the device; the same call runs the next
+        # step's fc over the embedding row of each id (one launch at M = 1)
+        nv.lmhead_gemv_argmax_fc(hl, lm_pool[c], embed_table, hfc, copies[(c + 1) % NCOPIES]["fc"], vocab_rows=VOCAB,
+                                 workspace=lm_ws, out_idx=draft_log[c * M:(c + 1) * M], out_max=out_max,
+                                 out=ys["fc"])
 
     nd = distinct_experts(nv, torch, xm, routers, copies[0]["moe"], moe_ws, M)
     gemv_b = sum(nvfp4_bytes(n, k) + M * n * 4 for name, n, k in PROJ) + M * 2 * (4096 + 2048 + 4096)
@@ -797,7 +800,7 @@ def main():
                    "proj": {n: [r_, c_] for n, r_, c_ in PROJ}, "moe": {"experts": E, "top_k": TOPK, "inter": I},
                    "lm_head": [VOCAB, H], "weight_copies_rotated": NCOPIES, "weight_bytes_allocated": int(rot_b),
                    "graph": f"{NCOPIES} steps per graph, each its own weight copy and router logits",
-                   "chained": "the next step's fc reads the embedding row of the draft id the LM head wrote"},
+                   "chained": "the LM head call runs the next step's fc over the embedding row of its draft id"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": round(r1["step_bytes"]),
         "drafts_per_s": round(1 / (lm_ms * 1e-3), 1),

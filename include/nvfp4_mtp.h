@@ -204,7 +204,8 @@ int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, vo
  *            of rows scored), 256-byte aligned.  It holds a ticket counter
  *            and per-row packed maxima that must be zero before the first
  *            call (zero-fill the buffer once); each call returns them to
- *            zero.  A workspace serves one call at a time: calls that
+ *            zero (and lmhead_gemv_argmax_fc's call count, which only
+ *            advances).  A workspace serves one call at a time: calls that
  *            overlap on one workspace race.
  * Rows with equal codes and scales produce bit-identical logits.  One launch.
  */
@@ -224,8 +225,8 @@ int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,
  * device share the array: calls that overlap on a device race (one at a
  * time per device, as with one workspace).  The grid is the device's
  * resident LM-head workgroups, each with m partials of 32 bytes; a grid
- * whose 256 + 32 * round_up(m) * workgroups bytes exceed the array is
- * refused with NVFP4_ERR_WORKSPACE (256 CUs need at most 131,328 bytes).
+ * whose 512 + 32 * round_up(m) * workgroups bytes exceed the array is
+ * refused with NVFP4_ERR_WORKSPACE (256 CUs need at most 131,584 bytes).
  * Allocates nothing (no hipMalloc, no allocating library routine).
  * Arguments, outputs and the other errors as lmhead_gemv_argmax.
  */
@@ -274,6 +275,32 @@ int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, const nvfp4_wei
                               int32_t vocab_rows, const uint32_t *allow_mask, int32_t mask_words,
                               int32_t *out_idx, float *out_max, float *out_logprob,
                               void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * lmhead_gemv_argmax_fc -- the end of one draft step and the start of the
+ * next: lmhead_gemv_argmax, then the next step's fc over the chosen
+ * tokens' embedding rows, y = w4a16_gemv_embed(out_idx, table, x_rest, fc)
+ * ([v4_mtp.rs] `propose` feeds each draft into the next step's input;
+ * [mtp_head.rs] `MtpHead` fields: `embed_from_argmax`, the fc).
+ *   h_bf16 ... flags          as lmhead_gemv_argmax (out_idx, out_max are
+ *                             its outputs, bit for bit).
+ *   table_bf16, table_vocab, hidden, x_rest_bf16, fc, y, y_dtype
+ *                             as w4a16_gemv_embed with idx = out_idx.
+ * At one row with K = 2048 and an fc of k = 2048 or 4096, one launch: the
+ * LM head's workgroups load their fc rows while its end chain runs, wait
+ * (bounded, about a second) for the last workgroup to publish the id in the
+ * workspace, gather its embedding row and finish the fc.  y then sums each
+ * row in another order than w4a16_gemv_embed (equal up to fp32 rounding;
+ * bit for bit on exactly representable sums), and is NaN if that wait gave
+ * up.  The whole grid must be resident at once (the persistent LM-head grid
+ * is sized so).  Otherwise the two calls, in order.  The workspace is
+ * lmhead_gemv_argmax's; every call advances a count in it.
+ */
+int lmhead_gemv_argmax_fc(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
+                          int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes, uint32_t flags,
+                          const uint16_t *table_bf16, int32_t table_vocab, int32_t hidden,
+                          const uint16_t *x_rest_bf16, const nvfp4_weight *fc, void *y, int32_t y_dtype,
+                          void *stream);
 
 /*
  * embed_from_argmax -- the draft tokens' embedding rows, gathered on the

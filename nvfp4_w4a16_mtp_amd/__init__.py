@@ -16,6 +16,7 @@ Operations (same names as the C ABI):
   lmhead_gemv_argmax_masked    ... restricted to a grammar's allowed tokens
   lmhead_gemv_argmax_embed     ... with the draft tokens' embedding rows gathered
   lmhead_gemv_argmax_noalloc   lmhead_gemv_argmax on the library's own static scratch
+  lmhead_gemv_argmax_fc        ... then the next draft step's fc over the chosen token's embedding row
   embed_from_argmax            embedding rows of device-resident token ids
   moe_w4a16_gemv               top-k routed NVFP4 expert FFN
   moe_w4a16_gemv_trace         ... one token, with per-workgroup phase timestamps
@@ -82,6 +83,7 @@ def lib():
         L.w4a16_gemv_embed.argtypes = [P, P, i32, i32, P, i32, WP, P, i32, P]
         L.lmhead_gemv_argmax_embed.argtypes = [P, i32, WP, i32, P, i32, P, P, P, P, i32, i32, P, ctypes.c_int64, P,
                                                P, sz, u32, P]
+        L.lmhead_gemv_argmax_fc.argtypes = [P, i32, WP, i32, P, P, P, sz, u32, P, i32, i32, P, WP, P, i32, P]
         L.moe_w4a16_gemv_workspace_bytes.argtypes = [i32, i32, EP]
         L.moe_w4a16_gemv_workspace_bytes.restype = sz
         L.moe_w4a16_gemv.argtypes = [P, i32, P, i32, EP, P, P, P, P, sz, P]
@@ -96,6 +98,7 @@ def lib():
         for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax",
                   "lmhead_gemv_argmax_noalloc",
                   "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed",
+                  "lmhead_gemv_argmax_fc",
                   "w4a16_gemv_embed",
                   "moe_w4a16_gemv", "moe_w4a16_gemv_trace", "moe_layer_w4a16", "moe_workspace_status"):
             getattr(L, f).restype = ctypes.c_int
@@ -326,6 +329,44 @@ def lmhead_gemv_argmax(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf1
                                     NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0, _stream(h)),
            "lmhead_gemv_argmax")
     return out_idx, out_max
+
+
+def lmhead_gemv_argmax_fc(h: torch.Tensor, w: NVFP4Weight, table: torch.Tensor, x_rest: torch.Tensor | None,
+                          fc: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,
+                          workspace: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                          out_max: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                          out_dtype=torch.float32):
+    """lmhead_gemv_argmax of h, then the next draft step's fc over the rows
+    [table[out_idx[i]] | x_rest[i]] (w4a16_gemv_embed): one launch at one
+    row, the two calls otherwise.  Returns (out_idx, out_max, out)."""
+    h = _as_bf16(h)
+    _dev(h, "h")
+    _dev(table, "table")
+    if table.dtype != torch.bfloat16 or table.dim() != 2 or not table.is_contiguous():
+        raise ValueError("table must be a contiguous bf16 [vocab][hidden] tensor")
+    m = h.shape[0]
+    vocab, hidden = table.shape
+    if x_rest is not None:
+        x_rest = _as_bf16(x_rest)
+        _dev(x_rest, "x_rest")
+        if x_rest.shape != (m, fc.k - hidden):
+            raise ValueError(f"x_rest must be [{m}][{fc.k - hidden}]")
+    if workspace is None:
+        v = w.n if vocab_rows <= 0 else min(vocab_rows, w.n)
+        workspace = lmhead_workspace(m, v, h.device)
+    if out_idx is None:
+        out_idx = torch.empty(m, dtype=torch.int32, device=h.device)
+    if out_max is None:
+        out_max = torch.empty(m, dtype=torch.float32, device=h.device)
+    if out is None:
+        out = torch.empty((m, fc.n), dtype=out_dtype, device=h.device)
+    d, dfc = w.desc(), fc.desc()
+    _check(lib().lmhead_gemv_argmax_fc(_ptr(h), m, ctypes.byref(d), vocab_rows, _ptr(out_idx), _ptr(out_max),
+                                       _ptr(workspace), workspace.numel(), NVFP4_ARGMAX_BF16_KEYS if bf16_keys else 0,
+                                       _ptr(table), vocab, hidden, _ptr(x_rest), ctypes.byref(dfc), _ptr(out),
+                                       _out_code(out.dtype), _stream(h)),
+           "lmhead_gemv_argmax_fc")
+    return out_idx, out_max, out
 
 
 def lmhead_gemv_argmax_noalloc(h: torch.Tensor, w: NVFP4Weight, vocab_rows: int = 0, bf16_keys: bool = False,

@@ -183,11 +183,33 @@ __device__ __forceinline__ int unpack_best_idx(unsigned long long p) { return (i
 constexpr int kLmTicket = 0;      // uint32 ticket counter (zero between calls)
 constexpr int kLmRow0 = 64;       // fp32[8]: logits of row 0
 constexpr int kLmBest = 128;      // uint64[8]: packed best (key, index) per row (zero between calls)
-constexpr int kLmParts = 256;     // ArgPart[grid][MT]
+constexpr int kLmFcSpinLimit = 1 << 22;   // polls of the fused fc's wait for the draft id (seconds)
+constexpr int kLmFcRows = 2;              // fc rows per wavefront: (NW - 1) G kLmFcRows >= n
+constexpr int kLmFcNoFit = 1;             // launch_lm_fc: too many fc rows for the grid (nothing launched)
+// uint64: call count (high) and draft id (low) of the fused next fc, on a
+// 128-byte line of its own: every waiting workgroup polls it, and on the
+// line of the maxima its polls slowed the end chain
+constexpr int kLmFcWord = 384;
+constexpr int kLmParts = 512;     // ArgPart[grid][MT]
 
 // Optional gather of the selected tokens' embedding rows by the last
 // workgroup (the next draft step's input, device-resident): table [vocab][units
 // x 16 B], row i written at out + i * stride_units, id_log[i] = index.
+// The next draft step's fc, run by the LM head's workgroups once the draft
+// id is known (lmhead_gemv_argmax_fc): y[r] = sum_k W[r][k] a[k] with a =
+// [table row of the id (kt elements) | rest (k - kt elements)], one
+// activation row.  codes == nullptr: none.
+struct FcNext {
+    const uint8_t *codes, *scales;
+    const nvfp4_global *g;
+    int n, k;
+    const uint16_t *table;   // [vocab][kt] bf16
+    int vocab, kt;
+    const uint16_t *rest;    // [k - kt] bf16
+    void *y;                 // [n] fp32, or bf16 when y_bf16
+    int y_bf16;
+};
+
 struct EmbedOut {
     const uint4 *table;   // nullptr: no gather
     uint4 *out;
@@ -280,13 +302,26 @@ __device__ __forceinline__ ArgPart combine_waves(const ArgPart (&wb)[NW][MT], in
 // the global scale, go to gy[m][row] (fp32, or bf16 with gy_bf16) and there
 // is no argmax, mask or workspace.  Large decode GEMVs use it for the
 // persistent grid, the LDS unit queue and the next unit's loads in flight.
-template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW, bool MF = false, bool MASKED = true, bool GOUT = false>
+//
+// FCPL > 0 (one activation row, argmax only; lmhead_gemv_argmax_fc): the
+// workgroups then run the next step's fc, a wavefront per row and FCPL
+// 32-element chunks a lane (k = 2048 FCPL).  Wavefronts 1.. load their fc
+// rows and the rest part of the activations as soon as their LM-head loop
+// ends, so the loads stream during the end chain (wavefront 0 carries the
+// chain's stores, and its completion wait would wait for them too); the last
+// workgroup publishes the draft id with this call's count in the fc word,
+// the others compute the rest part's products while they wait for the count
+// to change (bounded); then each lane loads its chunks of the id's
+// embedding row and the rows are finished.
+template <int MT, int R, int CPL, bool BF16KEY, bool LP, int NW, bool MF = false, bool MASKED = true, bool GOUT = false,
+          int FCPL = 0>
 __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__ x, int m_rt, const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, const nvfp4_global *__restrict__ g,
                                                    int v, int k, char *__restrict__ ws, int32_t *__restrict__ out_idx,
                                                    float *__restrict__ out_max, float *__restrict__ out_lp,
                                                    const uint32_t *__restrict__ mask, int mask_words, EmbedOut emb,
-                                                   void *__restrict__ gy, int gy_bf16) {
+                                                   void *__restrict__ gy, int gy_bf16, FcNext fc) {
+    static_assert(FCPL == 0 || (MT == 1 && !LP && !MASKED && !MF && !GOUT), "the fused fc follows a plain one-row argmax");
     extern __shared__ uint4 smem[];
     uint4 *xs = smem;
     __shared__ ArgPart wbest[NW][MT];
@@ -295,6 +330,12 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
     float *row0 = reinterpret_cast<float *>(ws + kLmRow0);
     ArgPart *parts = reinterpret_cast<ArgPart *>(ws + kLmParts);
     unsigned long long *best = reinterpret_cast<unsigned long long *>(ws + kLmBest);
+    unsigned long long *fcword = reinterpret_cast<unsigned long long *>(ws + kLmFcWord);
+    __shared__ unsigned int s_fce;   // FCPL: the fc word's count when the call started
+    __shared__ int32_t s_fcidx;      // FCPL: the draft id the fc gathers (-1: the wait gave up)
+    unsigned int fce = 0;            // thread 0; the last workgroup advances the word only after every ticket
+    if constexpr (FCPL > 0)
+        if (threadIdx.x == 0) fce = (unsigned int)(ld_dev(fcword) >> 32);
 
     constexpr int rows = MF ? 16 : 4 * R;
     static_assert(32 % rows == 0, "a unit lies inside one 32-row mask word");
@@ -543,6 +584,46 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
 
     if constexpr (GOUT) return;   // plain GEMV: every output is written
 
+    // FCPL: the fc rows of this wavefront (wavefronts 1..NW-1; row b + G ((w - 1)
+    // + (NW - 1) j)), lane l taking 32-element chunks l + 64 i, i < FCPL; the
+    // weights and the rest part of the activations now, so that the rest
+    // part's products are done while the draft id is awaited
+    constexpr int FCP = FCPL > 0 ? FCPL : 1;
+    uint4 fcw[kLmFcRows][FCP];
+    uint32_t fcs[kLmFcRows][FCP];
+    uint32_t fxr[FCP][16];   // the lane's rest-part activations (its emb-part chunks: loaded after the id)
+    if constexpr (FCPL > 0) {
+        if (wave >= 1) {
+#pragma unroll
+            for (int j = 0; j < kLmFcRows; ++j) {
+                const int row = min((int)blockIdx.x + (int)gridDim.x * (wave - 1 + (NW - 1) * j), fc.n - 1);
+                const uint8_t *cp = fc.codes + (size_t)row * (size_t)(fc.k >> 1);
+                const uint8_t *sp = fc.scales + (size_t)row * (size_t)(fc.k >> 4);
+#pragma unroll
+                for (int i = 0; i < FCP; ++i) {
+                    fcw[j][i] = ld_stream16(cp + 16 * (size_t)(lane + 64 * i));
+                    fcs[j][i] = ld_stream2(sp + 2 * (size_t)(lane + 64 * i));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FCP; ++i) {
+                const int kk = 32 * (lane + 64 * i);
+                if (kk >= fc.kt) {
+                    const uint4 *p = reinterpret_cast<const uint4 *>(fc.rest + (kk - fc.kt));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 u = p[q];
+                        fxr[i][4 * q] = u.x;
+                        fxr[i][4 * q + 1] = u.y;
+                        fxr[i][4 * q + 2] = u.z;
+                        fxr[i][4 * q + 3] = u.w;
+                    }
+                }
+            }
+        }
+        if (threadIdx.x == 0) s_fce = fce;
+    }
+
     // workgroup combine: the four slots of a wavefront by shuffles, then the
     // NW wavefronts in LDS -> MT candidates
     if constexpr (MF) {
@@ -580,10 +661,101 @@ __global__ __launch_bounds__(64 * NW) void k_lmhead(const uint16_t *__restrict__
             __hip_atomic_fetch_max(&best[lane], pack_best(b.key, b.idx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    wait_mem();   // partials, maxima and row-0 logits have reached device scope
+    // partials, maxima and row-0 logits (wavefront 0's stores) have reached
+    // device scope
+    if (FCPL == 0 || wave == 0) wait_mem();
     __syncthreads();
     if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
     __syncthreads();
+    if constexpr (FCPL > 0) {
+        float fpart[kLmFcRows];   // the rest part's sum of each fc row (lanes' shares)
+        if (s_last) {
+            if (wave == 0) {
+                // the argmax of the one row (as below), its outputs, and the
+                // id published with this call's count
+                const unsigned long long pk = ld_dev(&best[0]);
+                float key = unpack_best_key(pk), val = key;
+                int idx = unpack_best_idx(pk);
+                if (key > -INFINITY && (BF16KEY || key == 0.0f))
+                    val = ld_dev(&parts[(size_t)((idx / rows) % (int)gridDim.x) * MT].val);
+                if (!(key > -INFINITY)) {   // nothing above -inf: index 0
+                    idx = 0;
+                    val = ld_dev(&row0[0]);
+                }
+                if (lane == 0) {
+                    st_dev(&best[0], 0ull);   // ready for the next call
+                    st_dev(ticket, 0u);
+                    out_idx[0] = idx;
+                    out_max[0] = val;
+                    s_fcidx = idx;
+                    st_dev(fcword, ((unsigned long long)(s_fce + 1u) << 32) | (unsigned int)idx);
+                }
+            }
+        } else if (threadIdx.x == 0) {
+            unsigned long long w = ld_dev(fcword);
+            int n = 0;
+            while ((unsigned int)(w >> 32) == s_fce && n < kLmFcSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                w = ld_dev(fcword);
+                ++n;
+            }
+            s_fcidx = (unsigned int)(w >> 32) == s_fce ? -1 : (int32_t)(unsigned int)w;
+        }
+        if (wave >= 1) {
+            // the rest part's products (their loads were issued after the loop)
+#pragma unroll
+            for (int j = 0; j < kLmFcRows; ++j) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < FCP; ++i)
+                    if (32 * (lane + 64 * i) >= fc.kt) acc = chunk_dot_xreg(fcw[j][i], fcs[j][i], fxr[i], acc);
+                fpart[j] = acc;
+            }
+        }
+        __syncthreads();
+        const int32_t fid = s_fcidx;
+        if (wave >= 1) {
+            // the emb part: each lane's chunks of the id's table row (a zero
+            // row for an id outside the table, or when the wait gave up)
+            const bool in = fid >= 0 && fid < fc.vocab;
+            const uint16_t *trow = fc.table + (size_t)(in ? fid : 0) * (size_t)fc.kt;
+#pragma unroll
+            for (int i = 0; i < FCP; ++i) {
+                const int kk = 32 * (lane + 64 * i);
+                if (kk < fc.kt) {
+                    const uint4 *p = reinterpret_cast<const uint4 *>(trow + kk);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 u = in ? p[q] : make_uint4(0, 0, 0, 0);
+                        fxr[i][4 * q] = u.x;
+                        fxr[i][4 * q + 1] = u.y;
+                        fxr[i][4 * q + 2] = u.z;
+                        fxr[i][4 * q + 3] = u.w;
+                    }
+                }
+            }
+            const float fdec = fc.g->dec;
+#pragma unroll
+            for (int j = 0; j < kLmFcRows; ++j) {
+                float acc = fpart[j];
+#pragma unroll
+                for (int i = 0; i < FCP; ++i)
+                    if (32 * (lane + 64 * i) < fc.kt) acc = chunk_dot_xreg(fcw[j][i], fcs[j][i], fxr[i], acc);
+                // the row's sum over the 64 lanes, in a fixed order
+                const float r16 = row16_sum(acc);
+                const float sum = (__shfl(r16, 0, 64) + __shfl(r16, 16, 64)) + (__shfl(r16, 32, 64) + __shfl(r16, 48, 64));
+                const int row = (int)blockIdx.x + (int)gridDim.x * (wave - 1 + (NW - 1) * j);
+                if (lane == 0 && row < fc.n) {
+                    const float o = fid < 0 ? __builtin_nanf("") : sum * fdec;   // a wait that gave up: NaN rows
+                    if (fc.y_bf16)
+                        reinterpret_cast<uint16_t *>(fc.y)[row] = (uint16_t)f32_to_bf16_bits(o);
+                    else
+                        reinterpret_cast<float *>(fc.y)[row] = o;
+                }
+            }
+        }
+        return;
+    }
     if (!s_last) return;
 
     // last workgroup: its first wavefront reads the maxima and merges the
@@ -1009,7 +1181,7 @@ static int launch_lm_kernel(size_t lds, hipStream_t s, const uint16_t *h, int m,
         return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax: %d workgroups need %zu bytes of workspace, %zu available",
                     grid, need, wsb);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, s, h, m, w->codes, w->scales, w->global, v, w->k, ws, oi,
-                       om, olp, mask, mask_words, emb, nullptr, 0);
+                       om, olp, mask, mask_words, emb, nullptr, 0, FcNext{});
     return check_launch("lmhead_gemv_argmax");
 }
 
@@ -1045,7 +1217,7 @@ static bool launch_gemv_persist_k(size_t lds, hipStream_t s, const XRows &x, int
     if (per_cu < 1 || (MF ? 4 * units < waves : units < kPersistUnits * waves)) return false;
     if (allow_lds(reinterpret_cast<const void *>(kern), lds, "w4a16_gemv")) return false;
     hipLaunchKernelGGL(kern, dim3(num_cus() * per_cu), dim3(64 * NW), lds, s, x.x, m, w->codes, w->scales, w->global,
-                       w->n, w->k, nullptr, nullptr, nullptr, nullptr, nullptr, 0, EmbedOut{}, y, bf16);
+                       w->n, w->k, nullptr, nullptr, nullptr, nullptr, nullptr, 0, EmbedOut{}, y, bf16, FcNext{});
     return true;
 }
 
@@ -1070,15 +1242,57 @@ static bool launch_gemv_persist(hipStream_t s, const XRows &x, int m, const nvfp
     }
 }
 
+// The one-row LM head (4 chunks a lane) with the next step's fc fused
+// (FCPL chunks a lane), on the same persistent grid as launch_lm_kernel.
+template <bool BK, int FCPL>
+static int launch_lm_fc_k(size_t lds, hipStream_t s, const uint16_t *h, const nvfp4_weight *w, int v, char *ws,
+                          size_t wsb, int32_t *oi, float *om, const FcNext &fc) {
+    constexpr int NW = lm_waves<1, 4>();
+    auto kern = k_lmhead<1, lm_rows_per_slot<1>(), 4, BK, false, NW, false, false, false, FCPL>;
+    const size_t l = lds;
+    const int rc = allow_lds(reinterpret_cast<const void *>(kern), l, "lmhead_gemv_argmax_fc");
+    if (rc) return rc;
+    const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kern), 64 * NW, l);
+    if (per_cu < 1)
+        return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax_fc: a %d-thread workgroup does not fit on a CU", 64 * NW);
+    // every workgroup resident at once: all but the last wait for its draft id
+    const int cap = num_cus() * per_cu, nparts = (v + 15) / 16, grid = cap < nparts ? cap : nparts;
+    if ((long)(NW - 1) * grid * kLmFcRows < fc.n) return kLmFcNoFit;   // rows past the wavefronts' share
+    const size_t need = (size_t)kLmParts + sizeof(ArgPart) * (size_t)grid;
+    if (need > wsb)
+        return fail(NVFP4_ERR_WORKSPACE, "lmhead_gemv_argmax_fc: %d workgroups need %zu bytes of workspace, %zu available",
+                    grid, need, wsb);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), l, s, h, 1, w->codes, w->scales, w->global, v, w->k, ws, oi, om,
+                       nullptr, nullptr, 0, EmbedOut{}, nullptr, 0, fc);
+    return check_launch("lmhead_gemv_argmax_fc");
+}
+template <bool BK>
+static int launch_lm_fc(size_t lds, hipStream_t s, const uint16_t *h, const nvfp4_weight *w, int v, char *ws,
+                        size_t wsb, int32_t *oi, float *om, const FcNext &fc) {
+    if (fc.k == 2048) return launch_lm_fc_k<BK, 1>(lds, s, h, w, v, ws, wsb, oi, om, fc);
+    if (fc.k == 4096) return launch_lm_fc_k<BK, 2>(lds, s, h, w, v, ws, wsb, oi, om, fc);
+    return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax_fc: fused fc needs k = 2048 or 4096, got %d", fc.k);
+}
+
 // The LM head keeps KS = 1 and R = 2 (8-row wavefront units); there are at
-// most ceil(V / 16) partials.  A fixed chunk count when K = 2048.
+// most ceil(V / 16) partials.  A fixed chunk count when K = 2048.  fcn: the
+// next step's fc fused into the one-row argmax (lmhead_gemv_argmax_fc).
 template <int MT>
 static int launch_lmhead_m(const uint16_t *h, int m, const nvfp4_weight *w, int v, char *ws, size_t wsb, int32_t *oi,
                            float *om, float *olp, const uint32_t *mask, int mask_words, const EmbedOut &emb, bool bk,
-                           hipStream_t s) {
+                           hipStream_t s, const FcNext *fcn = nullptr) {
     const TileChoice tc{2, 1, w->k == 2048 ? 4 : 0};
     const size_t lds = gemv_lds_bytes(MT, w->k, tc);
     const bool lp = olp != nullptr;
+    if constexpr (MT == 1) {
+        if (fcn != nullptr) {
+            if (tc.CPL != 4 || lp || mask != nullptr || emb.table != nullptr)
+                return fail(NVFP4_ERR_UNSUPPORTED, "lmhead_gemv_argmax_fc: the fused fc follows a plain one-row argmax "
+                            "at k = 2048");
+            return bk ? launch_lm_fc<true>(lds, s, h, w, v, ws, wsb, oi, om, *fcn)
+                      : launch_lm_fc<false>(lds, s, h, w, v, ws, wsb, oi, om, *fcn);
+        }
+    }
     if (lm_mf_fits(MT, w->k)) {
         if constexpr (MT >= kLmMfMinRows) {
             const size_t lmf = (size_t)MT * w->k * 2 + (size_t)kLmMfWaves * kMfStageBytes;
@@ -1181,7 +1395,7 @@ extern "C" size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_ro
 static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
                          int32_t *out_idx, float *out_max, float *out_lp, const uint32_t *mask, int32_t mask_words,
                          const EmbedOut &emb, void *workspace, size_t ws_bytes, uint32_t flags, void *stream,
-                         const char *who, bool sized_by_grid = false) {
+                         const char *who, bool sized_by_grid = false, const FcNext *fcn = nullptr) {
     int rc = validate_weight(w, who);
     if (rc) return rc;
     if (!h_bf16 || !out_idx || !out_max) return fail(NVFP4_ERR_ARG, "%s: NULL h/out_idx/out_max", who);
@@ -1205,7 +1419,7 @@ static int lmhead_common(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *
     char *ws = reinterpret_cast<char *>(workspace);
     const bool bk = (flags & NVFP4_ARGMAX_BF16_KEYS) != 0;
     switch (mt) {
-        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
+        case 1: return launch_lmhead_m<1>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s, fcn);
         case 2: return launch_lmhead_m<2>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
         case 4: return launch_lmhead_m<4>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
         default: return launch_lmhead_m<8>(h_bf16, m, w, v, ws, ws_bytes, out_idx, out_max, out_lp, mask, mask_words, emb, bk, s);
@@ -1217,6 +1431,43 @@ extern "C" int lmhead_gemv_argmax(const uint16_t *h_bf16, int32_t m, const nvfp4
                                   uint32_t flags, void *stream) {
     return lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, workspace, ws_bytes,
                          flags, stream, "lmhead_gemv_argmax");
+}
+
+extern "C" int lmhead_gemv_argmax_fc(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w, int32_t vocab_rows,
+                                     int32_t *out_idx, float *out_max, void *workspace, size_t ws_bytes,
+                                     uint32_t flags, const uint16_t *table_bf16, int32_t table_vocab, int32_t hidden,
+                                     const uint16_t *x_rest_bf16, const nvfp4_weight *fc, void *y, int32_t y_dtype,
+                                     void *stream) {
+    const char *who = "lmhead_gemv_argmax_fc";
+    int rc = validate_weight(fc, who);
+    if (rc) return rc;
+    const bool fuse = m == 1 && w != nullptr && w->k == 2048 && (fc->k == 2048 || fc->k == 4096) && fc->n > 0;
+    if (!fuse) {
+        // the two calls it stands for
+        rc = lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, workspace,
+                           ws_bytes, flags, stream, who);
+        if (rc) return rc;
+        return w4a16_gemv_embed(out_idx, table_bf16, table_vocab, hidden, x_rest_bf16, m, fc, y, y_dtype, stream);
+    }
+    // the fc's checks of w4a16_gemv_embed
+    if (!table_bf16 || !y) return fail(NVFP4_ERR_ARG, "%s: NULL table or y", who);
+    if (table_vocab < 1 || hidden < 32 || hidden % 32 || hidden > fc->k)
+        return fail(NVFP4_ERR_SHAPE, "%s: need table_vocab >= 1 and hidden a positive multiple of 32 up to the fc's k "
+                    "(vocab=%d hidden=%d k=%d)", who, table_vocab, hidden, fc->k);
+    if (hidden < fc->k && !x_rest_bf16) return fail(NVFP4_ERR_ARG, "%s: NULL x_rest", who);
+    if (y_dtype != NVFP4_OUT_F32 && y_dtype != NVFP4_OUT_BF16) return fail(NVFP4_ERR_ARG, "%s: unknown y_dtype %d", who, y_dtype);
+    if (!aligned(table_bf16, 16) || !aligned(x_rest_bf16, 16) || !aligned(y, 4))
+        return fail(NVFP4_ERR_ALIGN, "%s: table and x_rest need 16-byte, y 4-byte alignment", who);
+    const FcNext f{fc->codes, fc->scales, fc->global, fc->n, fc->k, table_bf16, table_vocab, hidden, x_rest_bf16, y,
+                   y_dtype == NVFP4_OUT_BF16 ? 1 : 0};
+    rc = lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, workspace, ws_bytes,
+                       flags, stream, who, false, &f);
+    if (rc != kLmFcNoFit) return rc;
+    // more fc rows than the LM head's grid serves: the two calls
+    rc = lmhead_common(h_bf16, m, w, vocab_rows, out_idx, out_max, nullptr, nullptr, 0, EmbedOut{}, workspace, ws_bytes,
+                       flags, stream, who);
+    if (rc) return rc;
+    return w4a16_gemv_embed(out_idx, table_bf16, table_vocab, hidden, x_rest_bf16, m, fc, y, y_dtype, stream);
 }
 
 extern "C" int lmhead_gemv_argmax_logprob(const uint16_t *h_bf16, int32_t m, const nvfp4_weight *w,

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax", "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed", "w4a16_gemv_embed", "moe_w4a16_gemv", "moe_layer_w4a16",
+    for f in ("nvfp4_quantize", "w4a16_gemv", "w4a16_gemv_grouped", "w4a16_gemm_m128", "lmhead_gemv_argmax", "lmhead_gemv_argmax_logprob", "lmhead_gemv_argmax_masked", "embed_from_argmax", "lmhead_gemv_argmax_embed", "lmhead_gemv_argmax_fc", "w4a16_gemv_embed", "moe_w4a16_gemv", "moe_layer_w4a16",
               "moe_workspace_status", "moe_w4a16_gemv_trace", "moe_w4a16_gemv_trace_words", "lmhead_gemv_argmax_noalloc", "lmhead_gemv_argmax_workspace_bytes", "moe_w4a16_gemv_workspace_bytes", "w4a16_gemm_m128_workspace_bytes",
               "nvfp4_mtp_last_error"):
         assert f in names, f
