@@ -673,10 +673,11 @@ constexpr int kDownMaxPos = 136;       // pairs (<= 128) + one per token for the
 // from the route the gate/up launch published.  FUSED (one launch with the
 // gate/up workgroups, which come first in dispatch order): the workgroup
 // computes the routing itself, builds the plan in LDS, issues its weight
-// loads, then waits for its go flag (set once every gate/up workgroup of
-// the routed experts has finished) and reads the activations with
-// device-coherent loads.  The wait is bounded: past kSpinLimit polls the
-// workgroup writes NaN rows instead of waiting for ever.
+// loads, then waits until its go word holds one release of this call per
+// expert column (every gate/up workgroup of the column has stored its
+// activations) and reads the activations with device-coherent loads.  The
+// wait is bounded: past kSpinLimit polls the workgroup writes NaN rows and
+// sets the workspace's status instead of waiting for ever.
 // The items of the row-owner down pass: item it is row r0 + it % kDownRows
 // of distinct expert it / kDownRows (the shared expert where s_ex is -1).
 // Slot sl takes items b0 + sl + kSlots n of a batch; items past the end load

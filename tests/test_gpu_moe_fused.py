@@ -1,5 +1,6 @@
 """GPU parity of the one-launch MoE (gate/up and the row-owner down pass in
-one grid, handing off through counters and go flags in the workspace): a
+one grid, handing off through column counters and tagged go words in the
+workspace): a
 run of calls on one workspace with a different routing each time, and a
 captured graph replayed several times with eager work in between, every
 result against the oracle.  A wrong reset of the hand-off words would let a
