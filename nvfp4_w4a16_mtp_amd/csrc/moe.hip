@@ -431,6 +431,38 @@ __device__ __forceinline__ void gate_up_body(uint4 *xs, const uint16_t *x, const
 // activations and gate, are stored device-scope: in the fused launch the
 // down workgroups read them in the same launch, once the workgroup has
 // counted itself in the hand-off words `done` (FUSED).
+// gate/up of one token's pair over the row tiles bx0, bx0 + bs, ... (< gx):
+// the workgroup routes once and stages the activation row once for all of
+// them; each tile's weights are loaded and computed in turn (the other
+// workgroups of the CU cover the loads' latency).
+template <int CPL>
+__device__ __forceinline__ void gate_up_tiles(uint4 *xs, const uint16_t *x, const int *tok, const int *prs,
+                                              const uint8_t *gc, const uint8_t *gs, float gdec, const uint8_t *uc,
+                                              const uint8_t *us, float udec, int I, int H, int bx0, int bs, int gx,
+                                              uint16_t *__restrict__ act) {
+    static_assert(CPL > 0, "preloaded tiles need a fixed chunk count");
+    TileRegs<1, 1, 1, CPL> tg, tu;
+    gemv_tile_load(tg, gc, gs, I, H, bx0 * kMoeRows);
+    gemv_tile_load(tu, uc, us, I, H, bx0 * kMoeRows);
+    stage_rows(xs, x, tok, 1, 1, H);
+    __syncthreads();
+    const size_t arow = (size_t)prs[0] * I;
+    for (int bx = bx0; bx < gx; bx += bs) {
+        if (bx != bx0) {
+            gemv_tile_load(tg, gc, gs, I, H, bx * kMoeRows);
+            gemv_tile_load(tu, uc, us, I, H, bx * kMoeRows);
+        }
+        float gl = 0.0f;   // gate value of this lane's row
+        auto epi_g = [&](int row, int mm, float v) { gl = v * gdec; };
+        auto epi_u = [&](int row, int mm, float v) {
+            const float up = v * udec;
+            act[arow + row] = (uint16_t)f32_to_bf16_bits(gl / (1.0f + expf(-gl)) * up);
+        };
+        gemv_tile_compute(tg, xs, I, H, bx * kMoeRows, nullptr, epi_g);
+        gemv_tile_compute(tu, xs, I, H, bx * kMoeRows, nullptr, epi_u);
+    }
+}
+
 // The routing's outputs: ids and weights, and (route != nullptr) the plan of
 // the two-launch path -- distinct experts, and per pair position (in
 // (expert, token) order) its token, pair and weight.  One workgroup.
@@ -477,13 +509,13 @@ __device__ __forceinline__ void write_route(RouteLds &L, const nvfp4_moe_weights
     }
 }
 
-template <int CPL, bool FUSED, bool TRACE = false>
+template <int CPL, bool FUSED, bool TRACE = false, bool MULTI = false>
 __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx, const uint16_t *__restrict__ x,
                                              const float *__restrict__ logits, int m, int E, int topk,
                                              const nvfp4_moe_weights &e, int32_t *__restrict__ ids,
                                              float *__restrict__ wts, MoeRoute *__restrict__ route,
                                              uint16_t *__restrict__ act, const MoeShared &sh, unsigned int *done,
-                                             int n_down) {
+                                             int n_down, int gx_tiles = 0) {
     RouteLds &L = *reinterpret_cast<RouteLds *>(smem);   // reused for the activations afterwards
     __shared__ int tok[8], prs[8];
     __shared__ int s_ex, s_cnt, s_nd;
@@ -551,6 +583,11 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
     const uint8_t *uc = e.up_codes + (size_t)ex * (wsz / 2), *us = e.up_scales + (size_t)ex * (wsz / 16);
     const float gdec = e.gate_global[ex].dec, udec = e.up_global[ex].dec;
     const int row0 = bx * kMoeRows;
+    if constexpr (MULTI) {
+        // tiles bx, bx + gx, ... of gx_tiles (gx: workgroups per pair); no shared expert
+        gate_up_tiles<CPL>(smem, x, tok, prs, gc, gs, gdec, uc, us, udec, I, H, bx, gx, gx_tiles, act);
+        return;
+    }
     gate_up_body<1, CPL>(smem, x, tok, prs, cnt, gc, gs, gdec, uc, us, udec, I, H, row0, act);
     if constexpr (FUSED) {
         // count this workgroup in its column; the one that completes the
@@ -577,16 +614,17 @@ __device__ __forceinline__ void gate_up_role(uint4 *smem, int bx, int u, int gx,
 }
 
 // The two-launch form's gate/up pass (one workgroup per 16-row tile and
-// (token, slot) pair), held to four workgroups a CU.
-template <int CPL>
+// (token, slot) pair), held to four workgroups a CU.  MULTI: a workgroup
+// over several tiles of its pair (gate_up_tiles).
+template <int CPL, bool MULTI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_moe_gate_up(const uint16_t *__restrict__ x, const float *__restrict__ logits,
                                                     int m, int E, int topk, nvfp4_moe_weights e,
                                                     int32_t *__restrict__ ids, float *__restrict__ wts,
                                                     MoeRoute *__restrict__ route, uint16_t *__restrict__ act,
-                                                    MoeShared sh) {
+                                                    MoeShared sh, int gx_tiles) {
     extern __shared__ uint4 smem[];
-    gate_up_role<CPL, false>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids, wts, route, act,
-                             sh, nullptr, 0);
+    gate_up_role<CPL, false, false, MULTI>(smem, blockIdx.x, blockIdx.y, gridDim.x, x, logits, m, E, topk, e, ids,
+                                           wts, route, act, sh, nullptr, 0, gx_tiles);
 }
 
 // Rows per slot of the ticket down pass: 4 (a 64-row tile, about 37 KB of
@@ -1073,9 +1111,29 @@ template <int CPL>
 static int launch_gate_up(dim3 g, size_t lds, hipStream_t s, const uint16_t *x, const float *logits, int m, int E,
                           int topk, const nvfp4_moe_weights &e, int32_t *ids, float *wts, MoeRoute *route,
                           uint16_t *act, const MoeShared &sh) {
-    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL>), lds, "moe_w4a16_gemv");
+    const int gx = (int)g.x;   // row tiles of a pair
+    if constexpr (CPL > 0) {
+        // more workgroups than one round holds: fewer, each over several
+        // tiles of its pair, as evenly as the round allows (one routing and
+        // one activation staging for all of them).  256 experts of 2048 x
+        // 1024, top-8: 4 and 8 tokens 33.1 / 55.6 -> 29.2 / 46.3 us; an even
+        // share of tiles at 3 tokens 26.2 -> 24.6 us.
+        const void *km = reinterpret_cast<const void *>(k_moe_gate_up<CPL, true>);
+        const long most = (long)num_cus() * blocks_per_cu(km, 256, lds) / (long)g.y;   // one round
+        const long t = most >= 1 ? (gx + most - 1) / most : 0;                        // tiles a workgroup
+        const long per_pair = t >= 1 ? (gx + t - 1) / t : 0;   // so that each takes t or t - 1 tiles
+        if (!sh.on && t > 1) {
+            const int rc = allow_lds(km, lds, "moe_w4a16_gemv");
+            if (rc) return rc;
+            hipLaunchKernelGGL((k_moe_gate_up<CPL, true>), dim3((unsigned)per_pair, g.y), dim3(256), lds, s, x, logits,
+                               m, E, topk, e, ids, wts, route, act, sh, gx);
+            return check_launch("moe_w4a16_gemv(gate_up)");
+        }
+    }
+    const int rc = allow_lds(reinterpret_cast<const void *>(k_moe_gate_up<CPL, false>), lds, "moe_w4a16_gemv");
     if (rc) return rc;
-    hipLaunchKernelGGL((k_moe_gate_up<CPL>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act, sh);
+    hipLaunchKernelGGL((k_moe_gate_up<CPL, false>), g, dim3(256), lds, s, x, logits, m, E, topk, e, ids, wts, route, act,
+                       sh, gx);
     return check_launch("moe_w4a16_gemv(gate_up)");
 }
 template <int CPL>
