@@ -755,7 +755,7 @@ __device__ __forceinline__ void down_rows_fma(const DownItems &d, int b0, int kS
                                               const uint4 (&cw)[kDownBatch][CPL],
                                               const uint32_t (&sw)[kDownBatch][CPL], const int *s_pb,
                                               const float *s_dec, const uint4 *smem, int C,
-                                              float (*contrib)[kDownRows]) {
+                                              float (*contrib)[kDownRows], const int *img = nullptr) {
 #pragma unroll
     for (int n = 0; n < kDownBatch; ++n) {
         const int it = b0 + d.sl + kSlots * n;
@@ -763,8 +763,9 @@ __device__ __forceinline__ void down_rows_fma(const DownItems &d, int b0, int kS
         const int u = it / kDownRows, r = it % kDownRows;
         for (int pos = s_pb[u]; pos < s_pb[u + 1]; ++pos) {
             float acc[1] = {0.0f};
+            const int ir = img ? img[pos] : pos;   // the position's row of the activation image
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)pos * 4 * C, C, d.tl + 16 * j, acc);
+            for (int j = 0; j < CPL; ++j) chunk_fma<1>(cw[n][j], sw[n][j], smem + (size_t)ir * 4 * C, C, d.tl + 16 * j, acc);
             const float v = row16_sum(acc[0]);
             if (d.tl == 0) contrib[pos][r] = v * s_dec[u];
         }
@@ -805,14 +806,14 @@ __device__ __forceinline__ void down_rows_fma_one(const DownItems &d, int b0, in
 
 // stage_rows in two steps, so that loads issued in between do not delay the
 // image: the first kStageBatch units of each thread into registers, then
-// their stores and the rest of the image.
+// their stores and the rest of the image.  rows == nullptr: rows 0, 1, ...
 __device__ __forceinline__ void stage_rows_first(uint4 (&v)[kStageBatch], const uint16_t *__restrict__ src,
                                                  const int *rows, int cnt, int k) {
     const int upr = k >> 3, units = cnt * upr;
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j) {
         const int p = threadIdx.x + j * blockDim.x, mm = p / upr;
-        v[j] = p < units ? reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[p - mm * upr]
+        v[j] = p < units ? reinterpret_cast<const uint4 *>(src + (size_t)(rows ? rows[mm] : mm) * k)[p - mm * upr]
                          : make_uint4(0, 0, 0, 0);
     }
 }
@@ -833,7 +834,7 @@ __device__ __forceinline__ void stage_rows_rest(uint4 *xs, const uint4 (&v)[kSta
             units - done, threadIdx.x, blockDim.x,
             [&](int q) {
                 const int p = q + done, mm = p / upr;
-                return reinterpret_cast<const uint4 *>(src + (size_t)rows[mm] * k)[p - mm * upr];
+                return reinterpret_cast<const uint4 *>(src + (size_t)(rows ? rows[mm] : mm) * k)[p - mm * upr];
             },
             [&](int q, uint4 val) { put(q + done, val); });
 }
@@ -847,6 +848,8 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
     __shared__ int s_ex[kDownMaxExperts], s_pb[kDownMaxExperts + 1];
     __shared__ float s_dec[kDownMaxExperts], s_w[kDownMaxPos];
     __shared__ int s_tok[kDownMaxPos], s_pair[kDownMaxPos];
+    __shared__ int s_img[kDownMaxPos];   // separate launch: the activation image's row of each position
+    uint4 av[kStageBatch];               // separate launch: the first activation loads, issued with the plan's
     __shared__ float contrib[kDownMaxPos][kDownRows];
     __shared__ int s_nr, s_p0, s_late;
     if (FUSED) trace_mark<TRACE>(sh.trace, 0);
@@ -895,20 +898,35 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         }
         __syncthreads();
     } else {
-        const int nr = route->n_distinct, P0 = route->n_pairs;
-        for (int i = threadIdx.x; i <= nr; i += blockDim.x) {
-            s_pb[i] = route->pb[i];
-            if (i < nr) {
-                s_ex[i] = route->ex_id[i];
-                s_dec[i] = route->ddec[i];
-            }
+        // the plan in one round of loads: every entry up to the m top_k pairs
+        // (the distinct count only bounds which are used), then the
+        // activation rows, which need no plan (image row u is pair u; the
+        // sums look up each position's row): both round trips overlap
+        const int P0 = m * topk;   // every (token, slot) pair is a position
+        const int i = threadIdx.x;
+        int pb = 0, ex = 0, tk = 0, pr = 0, nr = 0;
+        float dec = 0.0f, w = 0.0f;
+        if (i <= P0) pb = route->pb[i];
+        if (i < P0) {
+            ex = route->ex_id[i];
+            dec = route->ddec[i];
+            tk = route->pos_tok[i];
+            pr = route->pos_pair[i];
+            w = route->pos_w[i];
         }
-        for (int i = threadIdx.x; i < P0; i += blockDim.x) {
-            s_tok[i] = route->pos_tok[i];
-            s_pair[i] = route->pos_pair[i];
-            s_w[i] = route->pos_w[i];
+        if (i == 0) nr = route->n_distinct;
+        stage_rows_first(av, act, nullptr, P0, I);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i <= P0) s_pb[i] = pb;
+        if (i < P0) {
+            s_ex[i] = ex;
+            s_dec[i] = dec;
+            s_tok[i] = tk;
+            s_pair[i] = pr;
+            s_w[i] = w;
+            s_img[i] = pr;
         }
-        if (threadIdx.x == 0) {
+        if (i == 0) {
             s_nr = nr;
             s_p0 = P0;
         }
@@ -923,6 +941,7 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
             s_pb[nr + 1] = P;
         }
         if (threadIdx.x < m) {
+            if (!FUSED) s_img[P0 + threadIdx.x] = P0 + threadIdx.x;   // the shared expert's rows follow the pairs'
             s_tok[P0 + threadIdx.x] = threadIdx.x;
             s_pair[P0 + threadIdx.x] = threadIdx.x;   // row of sh.sact
             if (!FUSED) s_w[P0 + threadIdx.x] = sh.sgate[threadIdx.x];   // FUSED: read after the wait
@@ -985,14 +1004,12 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         stage_rows_dev(smem, act, (size_t)m * topk, s_pair, P0, P0, I);
         if (sh.on) stage_rows_dev(smem + (size_t)P0 * 4 * C, sh.sact, (size_t)m, s_pair + P0, m, m, I);
     } else {
-        // the activation loads first, so that waiting for them does not wait
-        // for the weights issued after them
-        uint4 av[kStageBatch];
-        stage_rows_first(av, act, s_pair, P0, I);   // row pos of the image = pair position pos
+        // the activation loads went out with the plan's, before the weights,
+        // so that waiting for them does not wait for the weights
         down_rows_load<CPL>(it, 0, kSlots, ca, sa);
         down_rows_load<CPL>(it, kStep, kSlots, cb, sb);   // always (past the end: valid rows, unused)
         __builtin_amdgcn_sched_barrier(0);
-        stage_rows_rest(smem, av, act, s_pair, P0, I);
+        stage_rows_rest(smem, av, act, nullptr, P0, I);   // image row u = pair u
         if (sh.on) stage_rows(smem + (size_t)P0 * 4 * C, sh.sact, s_pair + P0, m, m, I);
     }
     __syncthreads();
@@ -1005,11 +1022,11 @@ __device__ __forceinline__ void down_rows_role(uint4 *smem, int bx, const nvfp4_
         if (kStep < nitems) down_rows_fma_one<CPL>(it, kStep, kSlots, cb, sb, s_dec, smem, C, contrib);
     } else {
         for (int b0 = 0; b0 < nitems; b0 += 2 * kStep) {
-            down_rows_fma<CPL>(it, b0, kSlots, ca, sa, s_pb, s_dec, smem, C, contrib);
+            down_rows_fma<CPL>(it, b0, kSlots, ca, sa, s_pb, s_dec, smem, C, contrib, FUSED ? nullptr : s_img);
             if (b0 + 2 * kStep < nitems) down_rows_load<CPL>(it, b0 + 2 * kStep, kSlots, ca, sa);
             __builtin_amdgcn_sched_barrier(0);
             if (b0 + kStep >= nitems) break;
-            down_rows_fma<CPL>(it, b0 + kStep, kSlots, cb, sb, s_pb, s_dec, smem, C, contrib);
+            down_rows_fma<CPL>(it, b0 + kStep, kSlots, cb, sb, s_pb, s_dec, smem, C, contrib, FUSED ? nullptr : s_img);
             if (b0 + 3 * kStep < nitems) down_rows_load<CPL>(it, b0 + 3 * kStep, kSlots, cb, sb);
             __builtin_amdgcn_sched_barrier(0);
         }
