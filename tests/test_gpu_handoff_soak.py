@@ -1,8 +1,9 @@
 """Repeated calls through the cross-workgroup hand-offs inside one launch: the
 one-launch MoE (activations stored device-scope, column counters, per-column
-releases into the down workgroups' go words) and the LM head (per-workgroup
-partials, the packed per-row maxima and the ticket of the last workgroup).
-Both rely on the ordering of device-scope relaxed atomics and coherent
+releases into the down workgroups' go words), the LM head (per-workgroup
+partials, the packed per-row maxima and the ticket of the last workgroup) and
+the LM head with the next step's fc (the draft id published with the call's
+count to every workgroup).  All three rely on the ordering of device-scope relaxed atomics and coherent
 loads and stores on gfx950 rather than on release/acquire fences, so this
 replays thousands of calls from HIP graphs -- the bench's Qwen shapes,
 inputs rotating between calls -- and requires every one of them to be bit
@@ -112,3 +113,44 @@ def test_lmhead_replays_match_eager():
     want_i = torch.cat([ref_i[i % ROT] for i in range(CALLS)]).reshape(CALLS, 1)
     want_m = torch.cat([ref_m[i % ROT] for i in range(CALLS)]).reshape(CALLS, 1)
     assert _soak(g, [oi.reshape(CALLS, 1), om.reshape(CALLS, 1)], [want_i, want_m]) == 0
+
+
+def test_lmhead_fc_replays_match_eager():
+    """The LM head with the next step's fc in one launch: the last workgroup
+    publishes the draft id with the call's count, the others wait for the
+    count to change and finish the fc over that id's embedding row."""
+    import nvfp4_w4a16_mtp_amd as nv
+    V, H = 151936, 2048
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(902)
+    w = nv.nvfp4_quantize(_randn(gen, (V, H), 0.02))
+    fc = nv.nvfp4_quantize(_randn(gen, (H, 2 * H), 0.02))
+    table = _randn(gen, (V, H))
+    hs = _randn(gen, (ROT, H))
+    rest = _randn(gen, (ROT, H))
+    ws = nv.lmhead_workspace(1, V, "cuda")
+    ref_i, ref_y = [], []
+    for r in range(ROT):
+        i, _, y = nv.lmhead_gemv_argmax_fc(hs[r:r + 1], w, table, rest[r:r + 1], fc, workspace=ws)
+        ref_i.append(i.clone())
+        ref_y.append(y.clone())
+    oi = torch.empty(CALLS, dtype=torch.int32, device="cuda")
+    om = torch.empty(CALLS, dtype=torch.float32, device="cuda")
+    ys = torch.empty((CALLS, H), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def calls():
+        for i in range(CALLS):
+            r = i % ROT
+            nv.lmhead_gemv_argmax_fc(hs[r:r + 1], w, table, rest[r:r + 1], fc, workspace=ws, out_idx=oi[i:i + 1],
+                                     out_max=om[i:i + 1], out=ys[i:i + 1])
+    with torch.cuda.stream(s):
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    want_i = torch.cat([ref_i[i % ROT] for i in range(CALLS)]).reshape(CALLS, 1)
+    want_y = torch.cat([ref_y[i % ROT] for i in range(CALLS)])
+    assert _soak(g, [oi.reshape(CALLS, 1), ys], [want_i, want_y]) == 0
