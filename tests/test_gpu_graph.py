@@ -59,6 +59,7 @@ def test_graph_replays_match_eager():
         nv.moe_w4a16_gemv(x, r, 8, ex, workspace=mws, out=ym, topk_ids=ids, topk_w=wts)
         nv.lmhead_gemv_argmax(x, wl, workspace=lws, out_idx=oi, out_max=om)
 
+    torch.cuda.synchronize()   # the workspaces are zero-filled before the stream's calls start
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         step()

@@ -62,6 +62,7 @@ def test_moe_one_launch_replays_match_eager():
     ys = torch.empty((CALLS, H), dtype=torch.float32, device="cuda")
     ids = torch.empty((CALLS, K), dtype=torch.int32, device="cuda")
     wts = torch.empty((CALLS, K), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()   # the reference calls have finished before the stream's calls start
     s = torch.cuda.Stream()
 
     def calls():
@@ -97,6 +98,7 @@ def test_lmhead_replays_match_eager():
         ref_m.append(m.clone())
     oi = torch.empty(CALLS, dtype=torch.int32, device="cuda")
     om = torch.empty(CALLS, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()   # the reference calls have finished before the stream's calls start
     s = torch.cuda.Stream()
 
     def calls():
@@ -137,6 +139,7 @@ def test_lmhead_fc_replays_match_eager():
     oi = torch.empty(CALLS, dtype=torch.int32, device="cuda")
     om = torch.empty(CALLS, dtype=torch.float32, device="cuda")
     ys = torch.empty((CALLS, H), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()   # the reference calls have finished before the stream's calls start
     s = torch.cuda.Stream()
 
     def calls():

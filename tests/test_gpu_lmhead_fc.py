@@ -89,6 +89,7 @@ def test_graph_replays_follow_each_draft():
         for i in range(5):
             nv.lmhead_gemv_argmax_fc(hs[i], w, table, rest[:1], fc, workspace=ws, out_idx=ids[i:i + 1],
                                      out_max=mx[i:i + 1], out=ys[i:i + 1])
+    torch.cuda.synchronize()   # the workspace is zero-filled before the stream's calls start
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         calls()

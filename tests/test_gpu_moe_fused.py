@@ -51,6 +51,7 @@ def test_graph_replays(orc, experts):
     y = torch.empty((m, H), dtype=torch.float32, device="cuda")
     ids = torch.empty((m, TOPK), dtype=torch.int32, device="cuda")
     w = torch.empty((m, TOPK), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()   # the workspace is zero-filled before the stream's calls start
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         nv.moe_w4a16_gemv(xin, rin, TOPK, dex, workspace=ws, out=y, topk_ids=ids, topk_w=w)
