@@ -206,7 +206,9 @@ int w4a16_gemm_m128(const uint16_t *x_bf16, int32_t m, const nvfp4_weight *w, vo
  *            call (zero-fill the buffer once); each call returns them to
  *            zero (and lmhead_gemv_argmax_fc's call count, which only
  *            advances).  A workspace serves one call at a time: calls that
- *            overlap on one workspace race.
+ *            overlap on one workspace race, and can leave the ticket off
+ *            zero, which makes later calls wrong; zero-fill it again after
+ *            such an overlap.
  * Rows with equal codes and scales produce bit-identical logits.  One launch.
  */
 size_t lmhead_gemv_argmax_workspace_bytes(int32_t m, int32_t vocab_rows);
