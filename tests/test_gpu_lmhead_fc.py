@@ -122,3 +122,32 @@ def test_two_rows_take_the_two_calls():
     i1, m1, y1 = nv.lmhead_gemv_argmax_fc(h, w, table, rest[:2], fc)
     assert torch.equal(i0, i1) and torch.equal(m0.view(torch.int32), m1.view(torch.int32))
     assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+
+
+@pytest.mark.parametrize("V,fc_n,fc_k", [
+    (8192, 4000, 2048),    # more fc rows than the head's wavefronts take (7 x 256 CUs x 2): the two calls
+    (300, 2048, 4096),     # a 19-workgroup head: too few wavefronts for the fc rows
+    (8192, 1024, 3072),    # an fc width other than 2048 or 4096
+    (8192, 2048, 2048)])   # fused, no rest part
+def test_each_path_equals_the_two_calls(V, fc_n, fc_k):
+    """Shapes on either side of the one-launch form's limits: the outputs are
+    the two separate calls' (the id bit for bit, the fc row bit for bit when
+    the call falls back to them, up to summation order when it fuses)."""
+    import nvfp4_w4a16_mtp_amd as nv
+    H = 2048
+    w = nv.nvfp4_quantize(dev_bf16(synth.weight_bf16(780, V, H)))
+    fc = nv.nvfp4_quantize(dev_bf16(synth.weight_bf16(781, fc_n, fc_k)))
+    table = dev_bf16(synth.acts_bf16(782, V, H))
+    rest = dev_bf16(synth.acts_bf16(783, 1, fc_k - H)) if fc_k > H else None
+    h = dev_bf16(synth.acts_bf16(784, 1, H))
+    i0, m0 = nv.lmhead_gemv_argmax(h, w)
+    y0 = nv.w4a16_gemv_embed(i0, table, rest, fc)
+    i1, m1, y1 = nv.lmhead_gemv_argmax_fc(h, w, table, rest, fc)
+    assert torch.equal(i0, i1) and torch.equal(m0.view(torch.int32), m1.view(torch.int32))
+    # one workgroup of 8 wavefronts per CU; wavefronts 1..7 take two fc rows each
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = fc_k in (2048, 4096) and fc_n <= 7 * min(cus, (V + 15) // 16) * 2
+    if fused:
+        assert_close(y1.cpu().numpy(), y0.cpu().numpy(), f"V={V} fc {fc_n}x{fc_k}")
+    else:
+        assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
