@@ -60,3 +60,14 @@ def test_config_256_experts(orc, m):
     x = synth.acts_bf16(3 + m, m, 2048)
     r = synth.router_logits(3 + m, m, 256)
     _run(orc, ex, dex, x, r, 8)
+
+
+@pytest.mark.parametrize("m", [3, 4, 8])
+def test_several_tiles_per_workgroup_uneven(orc, m):
+    """inter 1056: 66 row tiles per (token, slot) pair, more than one round of
+    gate/up workgroups holds at these token counts, so a workgroup takes
+    several tiles of its pair and the tiles do not divide evenly among them."""
+    ex = synth.moe_quantized_experts(5, 64, 512, 1056)
+    x = synth.acts_bf16(50 + m, m, 512)
+    r = synth.router_logits(50 + m, m, 64)
+    _run(orc, ex, _dev_experts(*ex), x, r, 8)
