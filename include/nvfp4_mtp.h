@@ -288,7 +288,9 @@ int lmhead_gemv_argmax_masked(const uint16_t *h_bf16, int32_t m, const nvfp4_wei
  *                             its outputs, bit for bit).
  *   table_bf16, table_vocab, hidden, x_rest_bf16, fc, y, y_dtype
  *                             as w4a16_gemv_embed with idx = out_idx.
- * At one row with K = 2048 and an fc of k = 2048 or 4096, one launch: the
+ * At one row with K = 2048 and an fc of k = 2048 or 4096, and when the LM
+ * head's grid can take every fc row (wavefronts 1..7 of each workgroup, two
+ * rows each: 14 rows a workgroup, 3584 on 256 CUs), one launch: the
  * LM head's workgroups load their fc rows while its end chain runs, wait
  * (bounded, about a second) for the last workgroup to publish the id in the
  * workspace, gather its embedding row and finish the fc.  y then sums each
